@@ -1,0 +1,436 @@
+"""CPU oracle of the routed Mixture-of-Experts expert layer.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+directory.  The product path (the HIP library and its Python binding) never
+calls it, shares no code with it and must fail loudly without its own native
+library.
+
+What it computes is the plain, dense definition of a dropless top-k routed
+MoE layer, one expert at a time, in float64 numpy with explicit bit-level
+bf16 / E4M3 / E8M0 conversions.  It does no tiling, fusion or scheduling.
+
+Sources (titles of the web pages the method comes from):
+
+* "LigerCute - native CUTLASS + NVSHMEM kernels" (Liger-Kernel
+  liger_cute_kernels README), sections "Overview" (symmetric buffers sized
+  from the total routed-token capacity: nothing is dropped), "Forward pass"
+  (routed tokens are sorted, the expert MLP runs, a final local combine
+  applies the router weights) and "Backward pass" (activation recomputation,
+  input and expert-weight gradients, routed dX reduced back to tokens).
+* "LightMoE" README (lightmoe 0.1.0 metadata), sections "Standalone GEMM /
+  Grouped GEMM" (contiguous expert-major rows, int32 ``m_indptr`` of length
+  E+1, experts with zero rows are valid), "MoE inference" (stage order:
+  dispatch, input quantisation, gate/up projection, gated activation,
+  requantisation, down projection, routing-weight application, deterministic
+  combine; ``top_k_ids`` int32 with distinct experts per token,
+  ``top_k_weights`` fp32) and "MoE training" (dispatch returns gather
+  indices, ``m_indptr``, routing weights and inverse slots; deterministic
+  dispatch, combine, input-, weight- and router-gradient kernels).
+* "cutedsl-megamoe" skill page (FlashInfer), section on the reference
+  helpers: MXFP8 data is quantised per block of 32 with E8M0 scales.
+* The OCP Microscaling Formats (MX) v1.0 specification, section 6.3
+  (conversion of a block of 32 values: shared exponent = floor(log2(amax))
+  minus the element format's largest exponent, elements quantised with
+  saturation) and section 5.3 / 5.4 (E8M0 scale, FP8 E4M3 element with bias 7,
+  no infinities, a single NaN mantissa pattern, largest normal 448).
+
+Readings where the pages leave a step open (each is also listed with the
+design notes of the repository):
+
+* Top-k is taken on the fp32 logits (softmax is monotone), descending, ties to
+  the lowest expert index; weights are the softmax restricted to the k chosen
+  logits, which equals softmax over all E renormalised over the k.
+* SwiGLU: h = silu(G) * U with silu(x) = x * sigmoid(x); W_gate feeds silu.
+* Rounding points: h, the expert outputs O and the layer output Y are rounded
+  to bf16 (round-to-nearest-even); accumulation is exact (float64 here).
+* Combine adds the k weighted expert rows of a token in slot order
+  (descending logit), in high precision, then rounds once.
+* Backward: bf16 roundings are straight-through (identity) in the
+  derivative.  The materialised gradients dg, du (of the gate and up
+  pre-activations) and dO = w * dY (of the expert output rows) are rounded to
+  bf16, like h in the forward; dX and dW_* are rounded once after exact
+  accumulation; the router-weight gradient is <h_r, dY_t W_down^T> in fp32
+  range (no rounding).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# bf16 (1 sign, 8 exponent, 7 mantissa bits)
+# ----------------------------------------------------------------------------
+
+BF16_MAX = float.fromhex("0x1.fep127")
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact widening)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), as float64.
+
+    bf16 keeps 8 significant bits: a normal value m*2**e (0.5 <= |m| < 1) is
+    rounded to a multiple of 2**(e-8); below 2**-126 the spacing is fixed at
+    2**-133 (subnormals).  Values past the largest finite bf16 plus half an
+    ulp become infinite.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, -133)
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    y = np.where(np.abs(y) > BF16_MAX, np.copysign(np.inf, x), y)
+    return np.where(np.isnan(x), np.nan, y)
+
+
+def bf16_encode(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns (round to nearest even)."""
+    y = bf16_round(x).astype(np.float32)          # exact: y is a bf16 value
+    return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 ("FN": bias 7, no infinities, NaN = S.1111.111) and E8M0 scales
+# OCP MX v1.0, sections 5.3-5.4
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest normal (448 = 1.75 * 2**8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3FN byte codes -> float64 (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = c & 0x7
+    val = np.where(ex == 0, np.ldexp(man.astype(np.float64), -9),
+                   np.ldexp(1.0 + man / 8.0, ex - 7))
+    val = np.where((ex == 15) & (man == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round float64 to the nearest E4M3FN value, ties to even, saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 4, -9)                   # 4 significant bits; subnormal spacing 2**-9
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    return np.clip(y, -E4M3_MAX, E4M3_MAX)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float64 (finite) -> E4M3FN byte codes, saturating round to nearest even."""
+    y = e4m3_round(x)
+    a = np.abs(y)
+    sign = np.where(np.signbit(y), 0x80, 0)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    unb = e - 1                                      # floor(log2 a) for a > 0
+    normal = a >= 2.0 ** -6
+    ex_field = np.where(normal, unb + 7, 0)
+    man = np.where(normal, np.rint(np.ldexp(a, -unb) * 8.0 - 8.0), np.rint(np.ldexp(a, 9)))
+    code = sign | (ex_field.astype(np.int64) << 3) | man.astype(np.int64)
+    return np.where(a == 0, sign, code).astype(np.uint8)
+
+
+def e8m0_decode(s) -> np.ndarray:
+    """E8M0 scale bytes -> float64 powers of two (255 is NaN)."""
+    s = np.asarray(s, dtype=np.uint8).astype(np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def mx_quantize(v, block: int = 32):
+    """MXFP8 (E4M3 elements, E8M0 scale) quantisation along the last axis.
+
+    OCP MX v1.0 section 6.3: for each block of 32 consecutive values, the
+    shared exponent is floor(log2(max |v|)) - 8 (8 = largest E4M3 exponent),
+    clamped to the E8M0 range [-127, 127]; each element is v / 2**shared
+    rounded to E4M3 with saturation.  A block whose values are all zero gets
+    scale byte 0 and zero elements.
+    Returns (codes uint8 [..., K], scale bytes uint8 [..., K/32]).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % block:
+        raise ValueError("last axis must be a multiple of the block size")
+    vb = v.reshape(v.shape[:-1] + (K // block, block))
+    amax = np.max(np.abs(vb), axis=-1)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.clip((e - 1) - E4M3_EMAX, -127, 127)
+    scale_bytes = np.where(amax > 0, shared + 127, 0).astype(np.uint8)
+    codes = e4m3_encode(np.ldexp(vb, -shared[..., None]))
+    codes = np.where((amax > 0)[..., None], codes, 0).astype(np.uint8)
+    return codes.reshape(v.shape), scale_bytes
+
+
+def mx_dequantize(codes, scales, block: int = 32) -> np.ndarray:
+    codes = np.asarray(codes)
+    K = codes.shape[-1]
+    vals = e4m3_decode(codes).reshape(codes.shape[:-1] + (K // block, block))
+    return (vals * e8m0_decode(scales)[..., None]).reshape(codes.shape)
+
+
+def mx_fake_quant(v) -> np.ndarray:
+    """The value an MXFP8 tensor represents after quantising ``v``."""
+    return mx_dequantize(*mx_quantize(v))
+
+
+# ----------------------------------------------------------------------------
+# Routing: softmax -> top-k -> renormalise
+# ----------------------------------------------------------------------------
+
+
+def route(logits, k: int):
+    """Top-k routing of fp32 logits [T, E].
+
+    Experts are ranked by logit, descending, ties to the lowest expert index
+    (comparison of the fp32 logits themselves; -0.0 equals +0.0).  The k
+    weights are the softmax over all E logits renormalised over the k chosen
+    ones, i.e. exp(l_j - l_max) / sum over the chosen of exp(l - l_max).
+    Returns (topk_idx int32 [T, k], topk_w float64 [T, k]).
+    """
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    key = lg.astype(np.float64) + 0.0               # -0.0 -> +0.0
+    order = np.argsort(-key, axis=1, kind="stable")  # stable: equal logits keep index order
+    idx = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(key, order[:, :k], axis=1)
+    ex = np.exp(sel - sel[:, :1])
+    w = ex / ex.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+# ----------------------------------------------------------------------------
+# Dispatch: expert-major order of the T*k assignments
+# ----------------------------------------------------------------------------
+
+
+def dispatch(topk_idx, E: int):
+    """Expert-major dispatch of the T*k assignments.
+
+    Assignment (t, j) has flat slot s = t*k + j.  Rows are ordered by expert,
+    and inside an expert by slot (so by token).  Returns int32 arrays
+    expert_offsets [E+1] (exclusive prefix sum of per-expert counts),
+    row_token [T*k], row_slot [T*k] and slot_row [T*k] (inverse of row_slot).
+    """
+    sel = np.asarray(topk_idx, dtype=np.int64)
+    T, k = sel.shape
+    flat = sel.reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_slot = np.argsort(flat, kind="stable").astype(np.int32)
+    row_token = (row_slot // k).astype(np.int32)
+    slot_row = np.empty(T * k, dtype=np.int32)
+    slot_row[row_slot] = np.arange(T * k, dtype=np.int32)
+    return offsets, row_token, row_slot, slot_row
+
+
+# ----------------------------------------------------------------------------
+# Expert MLP (gate/up projection, SwiGLU, down projection) and combine
+# ----------------------------------------------------------------------------
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def _as_f64(w) -> np.ndarray:
+    """Weights may be given as bf16 bits (uint16) or as real values."""
+    w = np.asarray(w)
+    return bf16_decode(w) if w.dtype == np.uint16 else w.astype(np.float64)
+
+
+def _expert_getter(W):
+    """W: array [E, K, N] (bits or values) or a callable e -> [K, N]."""
+    if callable(W):
+        return lambda e: _as_f64(W(e))
+    return lambda e: _as_f64(W[e])
+
+
+def expert_forward_rows(x_rows, wg, wu, wd, mxfp8: bool = False, exact: bool = False):
+    """One expert's MLP on rows x_rows [n, H] (float64 values).
+
+    G = x Wg, U = x Wu, h = bf16(silu(G) * U), O = bf16(h Wd).  With
+    ``mxfp8`` the GEMM operands x, W and h are the values their MXFP8 (32-long
+    blocks along the contraction axis) representation holds.  ``exact``
+    skips every rounding (used to check derivatives).
+    Returns (G, U, h, O) as float64.
+    """
+    if mxfp8:
+        x_rows = mx_fake_quant(x_rows)
+        wg = mx_fake_quant(wg.T).T
+        wu = mx_fake_quant(wu.T).T
+        wd = mx_fake_quant(wd.T).T
+    G = x_rows @ wg
+    U = x_rows @ wu
+    h = silu(G) * U
+    if not exact:
+        h = bf16_round(h)
+    hq = mx_fake_quant(h) if mxfp8 else h
+    O = hq @ wd
+    if not exact:
+        O = bf16_round(O)
+    return G, U, h, O
+
+
+def expert_mlp(X, row_token, offsets, W_gate, W_up, W_down, mxfp8: bool = False,
+               experts=None, exact: bool = False):
+    """Expert-major expert MLP over all routed rows.
+
+    X: [T, H] (bf16 bits or values); row_token / offsets from ``dispatch``;
+    W_gate, W_up: [E, H, I]; W_down: [E, I, H] (or callables e -> matrix).
+    Returns (h [A, I], O [A, H]) as float64 (bf16 values).  Rows of experts
+    not in ``experts`` (when given) are left NaN.
+    """
+    Xv = _as_f64(X)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = offsets.shape[0] - 1
+    A = int(offsets[-1])
+    gg, gu, gd = _expert_getter(W_gate), _expert_getter(W_up), _expert_getter(W_down)
+    I = gg(0).shape[1] if E else 0
+    H = Xv.shape[1]
+    h = np.full((A, I), np.nan)
+    O = np.full((A, H), np.nan)
+    todo = range(E) if experts is None else experts
+    for e in todo:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = Xv[np.asarray(row_token[lo:hi], dtype=np.int64)]
+        _, _, he, Oe = expert_forward_rows(rows, gg(e), gu(e), gd(e), mxfp8=mxfp8, exact=exact)
+        h[lo:hi] = he
+        O[lo:hi] = Oe
+    return h, O
+
+
+def combine(O, slot_row, topk_w, exact: bool = False):
+    """Y[t] = bf16( sum over j ascending of w[t, j] * O[slot_row[t*k + j]] )."""
+    w = np.asarray(topk_w, dtype=np.float64)
+    T, k = w.shape
+    rows = np.asarray(slot_row, dtype=np.int64).reshape(T, k)
+    acc = np.zeros((T, O.shape[1]))
+    for j in range(k):
+        acc = acc + w[:, j:j + 1] * O[rows[:, j]]
+    return acc if exact else bf16_round(acc)
+
+
+def layer_forward_tokens(X, topk_idx, topk_w, W_gate, W_up, W_down, tokens,
+                         mxfp8: bool = False, exact: bool = False):
+    """The layer output Y for the listed tokens only, straight from the
+    per-token definition (no dispatch): Y[t] = bf16(sum_j w[t,j] * MLP_e(x_t))."""
+    Xv = _as_f64(X)
+    gg, gu, gd = _expert_getter(W_gate), _expert_getter(W_up), _expert_getter(W_down)
+    idx = np.asarray(topk_idx)
+    w = np.asarray(topk_w, dtype=np.float64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((len(tokens), Xv.shape[1]))
+    by_expert = {}
+    for n, t in enumerate(tokens):
+        for j in range(idx.shape[1]):
+            by_expert.setdefault(int(idx[t, j]), []).append((n, int(t), j))
+    contrib = {}
+    for e, items in by_expert.items():
+        rows = Xv[[t for _, t, _ in items]]
+        _, _, _, Oe = expert_forward_rows(rows, gg(e), gu(e), gd(e), mxfp8=mxfp8, exact=exact)
+        for (n, t, j), o in zip(items, Oe):
+            contrib[(n, j)] = w[t, j] * o
+    for n in range(len(tokens)):
+        acc = np.zeros(Xv.shape[1])
+        for j in range(idx.shape[1]):
+            acc = acc + contrib[(n, j)]
+        out[n] = acc
+    return out if exact else bf16_round(out)
+
+
+# ----------------------------------------------------------------------------
+# Backward
+# ----------------------------------------------------------------------------
+
+
+def dsilu(x):
+    """d/dx of x*sigmoid(x) = sigmoid(x) * (1 + x * (1 - sigmoid(x)))."""
+    x = np.asarray(x, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-x))
+    return s * (1.0 + x * (1.0 - s))
+
+
+def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = False):
+    """Backward of one expert for its rows.
+
+    x_rows, dy_rows: [n, H] token inputs and output gradients of the rows;
+    w_rows: [n] routing weights.  G, U, h are recomputed as in the forward.
+    P = dY W_down^T; dwt = <h, P>; dh = w P; du = bf16(dh * silu(G));
+    dg = bf16(dh * U * silu'(G)); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
+    dWg = x^T dg, dWu = x^T du, dWd = h^T dO (not yet rounded).
+    Returns dict of float64 arrays.
+    """
+    rnd = (lambda a: a) if exact else bf16_round
+    G = x_rows @ wg
+    U = x_rows @ wu
+    h = silu(G) * U
+    if not exact:
+        h = bf16_round(h)
+    P = dy_rows @ wd.T
+    dwt = np.sum(h * P, axis=1)
+    dh = w_rows[:, None] * P
+    du = rnd(dh * silu(G))
+    dg = rnd(dh * U * dsilu(G))
+    dO = rnd(w_rows[:, None] * dy_rows)
+    dXr = dg @ wg.T + du @ wu.T
+    return {"dwt": dwt, "dXr": dXr, "dWg": x_rows.T @ dg, "dWu": x_rows.T @ du,
+            "dWd": h.T @ dO, "dg": dg, "du": du, "h": h}
+
+
+def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact: bool = False,
+             want_dx: bool = True, E: int | None = None):
+    """Gradients of the layer.
+
+    Returns dict with dX [T, H], dW_gate / dW_up [E, H, I], dW_down [E, I, H]
+    (bf16 values after exact accumulation; only for ``experts`` when given, the
+    rest NaN; experts with no rows get exact zeros) and d_topk_w [T, k]
+    (float64).  dX sums a token's k row contributions in slot order and is
+    only complete when every expert is processed.  ``E`` is needed when the
+    weights are given as callables.
+    """
+    rnd = (lambda a: a) if exact else bf16_round
+    Xv, dYv = _as_f64(X), _as_f64(dY)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    T, k = idx.shape
+    H = Xv.shape[1]
+    gg, gu, gd = _expert_getter(W_gate), _expert_getter(W_up), _expert_getter(W_down)
+    if E is None:
+        E = W_gate.shape[0]
+    I = gg(int(idx[0, 0])).shape[1]
+    todo = range(E) if experts is None else sorted(set(experts))
+    dW = {n: {} for n in ("dWg", "dWu", "dWd")}
+    dxr = np.zeros((T, k, H)) if want_dx else None
+    dwt = np.full((T, k), np.nan)
+    for e in todo:
+        tt, jj = np.nonzero(idx == e)            # (t, j) in slot order
+        if len(tt) == 0:
+            dW["dWg"][e] = np.zeros((H, I))
+            dW["dWu"][e] = np.zeros((H, I))
+            dW["dWd"][e] = np.zeros((I, H))
+            continue
+        r = expert_backward_rows(Xv[tt], dYv[tt], w[tt, jj], gg(e), gu(e), gd(e), exact=exact)
+        dW["dWg"][e] = rnd(r["dWg"])
+        dW["dWu"][e] = rnd(r["dWu"])
+        dW["dWd"][e] = rnd(r["dWd"])
+        dwt[tt, jj] = r["dwt"]
+        if want_dx:
+            dxr[tt, jj] = r["dXr"]
+    out = {"d_topk_w": dwt, "dW": dW}
+    if want_dx:
+        acc = np.zeros((T, H))
+        for j in range(k):
+            acc = acc + dxr[:, j]
+        out["dX"] = rnd(acc)
+    return out
