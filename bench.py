@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE expert layer on one MI355X.
+
+One step is one pass of the layer's hot path over one batch of synthetic
+input: routing, dispatch, the grouped-GEMM expert MLP (gate/up + SwiGLU,
+down) and the weighted combine; for the training workload also the backward.
+Inputs are resident in HBM before the timed region; weight packing happens at
+load time, outside it.  Caches are not flushed between steps.
+
+Prints one JSON line.  Default workload: prefill (T=4096 tokens, hidden 2048,
+intermediate 512, 256 experts, top-8, bf16).  Other workloads (--workload
+decode | train | large_mxfp8 | tiny | prefill_rankzipf) are for diagnostics.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MoE layer fwd/bwd TFLOP/s + tokens/s, % of MFMA (prefill) / HBM (decode) peak"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 / MXFP8 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    return ap.parse_args()
+
+
+def device_weights(cfg, name, experts=None):
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    from grouped_gemm_router_amd import workloads as wl
+    K, N = wl.weight_shape(cfg, name)
+    out = torch.full((cfg.E, K, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    todo = range(cfg.E) if experts is None else sorted(set(int(e) for e in experts))
+    with ThreadPoolExecutor(16) as ex:
+        for e, bits in ex.map(lambda e: (e, wl.make_expert_weight(cfg, name, e)), todo):
+            out[e].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    return out
+
+
+def step_flops(cfg, active_rows):
+    A, H, I = active_rows, cfg.H, cfg.I
+    fwd = 6.0 * A * H * I
+    bwd = 12.0 * A * H * I if cfg.backward else 0.0
+    return fwd, bwd
+
+
+def cpu_baseline(cfg, logits, X, dY, time_budget_s=30.0):
+    """The oracle, as it stands, on the host cores: the full routing and
+    dispatch plus the expert MLP and combine of a bounded sample of tokens."""
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as orc
+    from grouped_gemm_router_amd import workloads as wl
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    idx, w = orc.route(logits, cfg.k)
+    orc.dispatch(idx, cfg.E)
+    t_route = time.perf_counter() - t0
+    fn = lambda n: (lambda e: wl.make_expert_weight(cfg, n, e))
+    # sample of tokens sized to the time budget: start small, grow while cheap
+    ntok = min(cfg.T, 64)
+    rng = np.random.default_rng(0)
+    while True:
+        toks = np.sort(rng.choice(cfg.T, ntok, replace=False))
+        t0 = time.perf_counter()
+        orc.layer_forward_tokens(X, idx, w, fn("gate"), fn("up"), fn("down"), toks, mxfp8=cfg.dtype == "mxfp8")
+        if cfg.backward:
+            orc.backward_tokens(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), toks)
+        dt = time.perf_counter() - t0
+        if dt > time_budget_s / 4 or ntok >= cfg.T:
+            break
+        ntok = min(cfg.T, ntok * 4)
+    f_fwd, f_bwd = step_flops(cfg, ntok * cfg.k)
+    tflops = (f_fwd + f_bwd) / dt / 1e12
+    tok_s = ntok / (dt + t_route * ntok / cfg.T)
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "tokens_per_s": round(tok_s, 2),
+            "sample": f"routing+dispatch of all {cfg.T} tokens ({t_route:.2f} s) and the expert MLP + combine"
+                      f"{' + backward' if cfg.backward else ''} of {ntok} sampled tokens ({dt:.2f} s), "
+                      f"float64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer runs every "
+              "expert on one MI355X; see the design notes for how it would shard).", file=sys.stderr)
+        return 2
+    import torch
+    from grouped_gemm_router_amd import workloads as wl
+    from grouped_gemm_router_amd.layer import MoELayer
+
+    cfg = wl.config(args.workload)
+    logits_np, X_np = wl.make_logits(cfg), wl.make_x(cfg)
+    dY_np = wl.make_dy(cfg) if cfg.backward else None
+    full_weights = cfg.E * cfg.H * cfg.I <= 128 * 4096 * 1024
+    experts = None
+    if not full_weights:
+        # too large to draw every expert quickly: only the experts the router picks get weights, the
+        # others hold NaN (never read by the layer)
+        from grouped_gemm_router_amd import binding as B
+        idx, _ = B.route(torch.from_numpy(logits_np).cuda(), cfg.k)
+        experts = torch.unique(idx).cpu().numpy()
+    W = {n: device_weights(cfg, n, experts) for n in ("gate", "up", "down")}
+    logits = torch.from_numpy(logits_np).cuda()
+    X = torch.from_numpy(X_np.view(np.int16)).cuda().view(torch.bfloat16)
+    dY = torch.from_numpy(dY_np.view(np.int16)).cuda().view(torch.bfloat16) if cfg.backward else None
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(W["gate"], W["up"], W["down"],
+                                                                         keep_math=cfg.backward)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        layer.forward(logits, X, backward_plan=cfg.backward, mlp_events=ev)
+        if cfg.backward:
+            layer.backward(X, dY)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    pl = layer.plan(cfg.T, cfg.backward)
+    offsets = pl["offsets"].cpu().numpy()
+    n_active = int(np.count_nonzero(np.diff(offsets)))
+    f_fwd, f_bwd = step_flops(cfg, cfg.A)
+    tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if cfg.dtype == "mxfp8" else PEAK_BF16_TFLOPS
+    wbytes = 1 if cfg.dtype == "mxfp8" else 2
+    weight_bytes = n_active * 3 * cfg.H * cfg.I * wbytes
+    act_bytes = cfg.T * cfg.E * 4 + cfg.T * cfg.H * 2 * 2
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8" if cfg.dtype == "mxfp8" else "bf16",
+        "data": "synthetic (seeded numpy draws; shapes and routing skew of the workload)",
+        "config": {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
+                   "top_k": cfg.k, "active_experts": n_active, "backward": cfg.backward,
+                   "graph": bool(args.graph)},
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "frac_of_mfma_peak": round(tflops / peak, 4),
+        "hbm_GBps_algorithmic": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1),
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if graph is None:
+        mlp_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        mlp_flops = 6.0 * cfg.A * cfg.H * cfg.I
+        if cfg.T <= 64:   # small-token path: weight streaming, HBM bound
+            achieved = (weight_bytes + cfg.A * (cfg.H + cfg.I) * 2 * 2) / (mlp_ms * 1e-3) / 1e9
+            out["roofline"] = {"kernel": "moe_expert_mlp (gate/up+SwiGLU and down)", "bound": "hbm",
+                               "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                               "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                               "avg_launch_ms": round(mlp_ms, 5)}
+        else:
+            achieved = mlp_flops / (mlp_ms * 1e-3) / 1e12
+            out["roofline"] = {"kernel": "moe_expert_mlp (gate/up+SwiGLU and down grouped GEMMs)",
+                               "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                               "frac": round(achieved / peak, 4), "traffic": None,
+                               "avg_launch_ms": round(mlp_ms, 5)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, logits_np, X_np, dY_np)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,288 @@
+// C ABI of the MoE layer (include/moe.h): argument checks on the host before
+// any launch, workspace sizing, the gfx950 device check, and the launches.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int MAX_E = 1024;
+constexpr int MAX_K = 32;
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_route_args(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (k > E) return MOE_ERR_INVALID_ARG;
+  if (E > MAX_E || k > MAX_K) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+moe_status check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_route_args(p->T, p->E, p->k);
+  if (s != MOE_OK) return s;
+  if (p->H < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_MXFP8) return MOE_ERR_INVALID_ARG;
+  const int align = p->dtype == MOE_DTYPE_MXFP8 ? 128 : 64;
+  if (p->H % align || p->I % align) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // element offsets of the largest tensors must fit the kernels' index math
+  if ((int64_t)p->T * p->k * (int64_t)p->H >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+size_t mlp_ws(const moe_problem* p) {
+  if (p->dtype != MOE_DTYPE_MXFP8) return 0;
+  const size_t T = p->T, H = p->H, I = p->I, A = (size_t)p->T * p->k;
+  return align_up(T * H) + align_up(T * H / 32) + align_up(A * I) + align_up(A * I / 32);
+}
+
+size_t bwd_ws(const moe_problem* p) {
+  const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
+  const size_t nparts = moe::bwd_nparts(p->I);
+  return align_up(A * I * 4) + align_up(A * 2 * I * 2) + align_up(A * I * 2) + align_up(A * H * 4) +
+         align_up(A * nparts * 4);
+}
+
+// Device check, cached per device id.
+std::mutex g_mu;
+int g_dev_state[64];   // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[64];
+
+moe_status device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    g_dev_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[dev] = prop.multiProcessorCount;
+  }
+  return g_dev_state[dev] == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+}  // namespace
+
+namespace moe {
+int num_cus() {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int n = (dev >= 0 && dev < 64) ? g_dev_cus[dev] : 0;
+  return n > 0 ? n : 256;
+}
+}  // namespace moe
+
+extern "C" {
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+MOE_API moe_status moe_validate_problem(const moe_problem* p) { return check_problem(p); }
+
+MOE_API moe_status moe_workspace_size(const moe_problem* p, int call, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_problem(p);
+  if (s != MOE_OK) return s;
+  switch (call) {
+    case MOE_CALL_DISPATCH: *bytes = align_up(moe::dispatch_ws_bytes((long)p->T * p->k, p->E)); break;
+    case MOE_CALL_EXPERT_MLP: *bytes = mlp_ws(p); break;
+    case MOE_CALL_BACKWARD:
+      if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
+      *bytes = bwd_ws(p);
+      break;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_check_device(void) { return device_ok(); }
+
+MOE_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                             float* topk_w, void* stream) {
+  moe_status s = check_route_args(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if ((s = device_ok()) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  return from_hip(moe::launch_route(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                int32_t* expert_offsets, int32_t* row_token, int32_t* row_slot,
+                                int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_route_args(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!expert_offsets || (T > 0 && (!topk_idx || !row_token || !row_slot || !slot_row)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::dispatch_ws_bytes((long)T * k, E);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if ((s = device_ok()) != MOE_OK) return s;
+  return from_hip(moe::launch_dispatch(topk_idx, T, E, k, expert_offsets, row_token, row_slot, slot_row,
+                                       (int32_t*)ws, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_pack_weights(const void* W, int32_t E, int32_t K, int32_t N, void* Wt, void* stream) {
+  if (!W || !Wt || E < 1 || K < 1 || N < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 64 || N % 64 || E > 65535) return MOE_ERR_UNSUPPORTED_SHAPE;
+  moe_status s = device_ok();
+  if (s != MOE_OK) return s;
+  return from_hip(moe::launch_pack((const uint16_t*)W, E, K, N, (uint16_t*)Wt, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* q, uint8_t* scales,
+                                   void* stream) {
+  if (rows < 0 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 32) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_INVALID_ARG;
+  moe_status s = device_ok();
+  if (s != MOE_OK) return s;
+  return from_hip(moe::launch_mx_quantize((const uint16_t*)x, rows, K, q, scales, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token,
+                                  const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                  const void* Wd_t, const uint8_t* Sg, const uint8_t* Su, const uint8_t* Sd,
+                                  void* H_rows, void* O_rows, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_problem(p);
+  if (s != MOE_OK) return s;
+  if (!X || !expert_offsets || !Wg_t || !Wu_t || !Wd_t || !H_rows || !O_rows) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && !row_token) return MOE_ERR_INVALID_ARG;
+  const bool mx = p->dtype == MOE_DTYPE_MXFP8;
+  if (mx != (Sg && Su && Sd)) return MOE_ERR_INVALID_ARG;
+  if (!mx && (Sg || Su || Sd)) return MOE_ERR_INVALID_ARG;
+  const size_t need = mlp_ws(p);
+  if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if ((s = device_ok()) != MOE_OK) return s;
+  if (p->T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (!mx) {
+    moe::GemmArgs a = {};
+    a.T = p->T; a.H = p->H; a.I = p->I; a.E = p->E; a.k = p->k;
+    a.offsets = expert_offsets;
+    a.row_token = row_token;
+    a.X = (const uint16_t*)X;
+    a.Wg_t = (const uint16_t*)Wg_t;
+    a.Wu_t = (const uint16_t*)Wu_t;
+    a.Wd_t = (const uint16_t*)Wd_t;
+    a.Hrows = (uint16_t*)H_rows;
+    a.Orows = (uint16_t*)O_rows;
+    if (p->T <= moe::DECODE_MAX_T) return from_hip(moe::launch_decode_mlp(a, st));
+    hipError_t e = moe::launch_fwd_gateup(a, st);
+    if (e == hipSuccess) e = moe::launch_fwd_down(a, st);
+    return from_hip(e);
+  }
+  const size_t T = p->T, H = p->H, I = p->I, A = (size_t)p->T * p->k;
+  uint8_t* w8 = (uint8_t*)ws;
+  uint8_t* Xq = w8;
+  uint8_t* Xs = Xq + align_up(T * H);
+  uint8_t* Hq = Xs + align_up(T * H / 32);
+  uint8_t* Hs = Hq + align_up(A * I);
+  moe::MxArgs m = {};
+  m.T = p->T; m.H = p->H; m.I = p->I; m.E = p->E; m.k = p->k;
+  m.offsets = expert_offsets;
+  m.row_token = row_token;
+  m.Xq = Xq; m.Xs = Xs;
+  m.Wg = (const uint8_t*)Wg_t; m.Sg = Sg;
+  m.Wu = (const uint8_t*)Wu_t; m.Su = Su;
+  m.Wd = (const uint8_t*)Wd_t; m.Sd = Sd;
+  m.Hrows = (uint16_t*)H_rows;
+  m.Hq = Hq; m.Hs = Hs;
+  m.Orows = (uint16_t*)O_rows;
+  hipError_t e = moe::launch_mx_quantize((const uint16_t*)X, p->T, p->H, Xq, Xs, st);
+  if (e == hipSuccess) e = moe::launch_mx_gateup(m, st);
+  if (e == hipSuccess) e = moe::launch_mx_quantize((const uint16_t*)H_rows, (long)A, p->I, Hq, Hs, st);
+  if (e == hipSuccess) e = moe::launch_mx_down(m, st);
+  return from_hip(e);
+}
+
+MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, const float* topk_w, int32_t T,
+                               int32_t k, int32_t H, void* Y, void* stream) {
+  if (T < 0 || k < 1 || k > MAX_K || H < 1) return MOE_ERR_INVALID_ARG;
+  if (H % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!O_rows || !slot_row || !topk_w || !Y) return MOE_ERR_INVALID_ARG;
+  moe_status s = device_ok();
+  if (s != MOE_OK) return s;
+  return from_hip(moe::launch_combine((const uint16_t*)O_rows, slot_row, topk_w, T, k, H, (uint16_t*)Y,
+                                      (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY, const float* topk_w,
+                                const int32_t* row_token, const int32_t* row_slot, const int32_t* slot_row,
+                                const int32_t* expert_offsets, const void* W_gate, const void* W_up,
+                                const void* W_down, const void* Wg_t, const void* Wu_t, void* dX,
+                                void* dW_gate, void* dW_up, void* dW_down, float* d_topk_w, void* ws,
+                                size_t ws_bytes, void* stream) {
+  moe_status s = check_problem(p);
+  if (s != MOE_OK) return s;
+  if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !expert_offsets || !W_gate || !W_up ||
+      !W_down || !Wg_t || !Wu_t || !dX || !dW_gate || !dW_up || !dW_down || !d_topk_w)
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = bwd_ws(p);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if ((s = device_ok()) != MOE_OK) return s;
+  const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
+  uint8_t* w8 = (uint8_t*)ws;
+  moe::GemmArgs a = {};
+  a.T = p->T; a.H = p->H; a.I = p->I; a.E = p->E; a.k = p->k;
+  a.offsets = expert_offsets;
+  a.row_token = row_token;
+  a.row_slot = row_slot;
+  a.topk_w = topk_w;
+  a.X = (const uint16_t*)X;
+  a.dY = (const uint16_t*)dY;
+  a.Wg_t = (const uint16_t*)Wg_t;
+  a.Wu_t = (const uint16_t*)Wu_t;
+  a.Wg = (const uint16_t*)W_gate;
+  a.Wu = (const uint16_t*)W_up;
+  a.Wd = (const uint16_t*)W_down;
+  a.nparts = moe::bwd_nparts(p->I);
+  a.P = (float*)w8;
+  w8 += align_up(A * I * 4);
+  a.dGU = (uint16_t*)w8;
+  w8 += align_up(A * 2 * I * 2);
+  a.Hrows = (uint16_t*)w8;
+  w8 += align_up(A * I * 2);
+  a.dXr = (float*)w8;
+  w8 += align_up(A * H * 4);
+  a.dwt_part = (float*)w8;
+  a.dWg = (uint16_t*)dW_gate;
+  a.dWu = (uint16_t*)dW_up;
+  a.dWd = (uint16_t*)dW_down;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (p->T > 0) {
+    e = moe::launch_bwd_p(a, st);
+    if (e == hipSuccess) e = moe::launch_bwd_recompute(a, st);
+    if (e == hipSuccess) e = moe::launch_bwd_dx_rows(a, st);
+    if (e == hipSuccess) e = moe::launch_bwd_token_reduce(a, slot_row, (uint16_t*)dX, d_topk_w, st);
+  }
+  if (e == hipSuccess) e = moe::launch_bwd_dw_down(a, st);
+  if (e == hipSuccess) e = moe::launch_bwd_dw_gateup(a, st);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 pair -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+
+// sigmoid / silu in fp32 with the hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
+
+// One 128-byte row of a 64-element bf16 k-tile is 8 chunks of 16 bytes.  The
+// chunk order is permuted per row so that the 32 rows one MFMA operand read
+// touches spread over all LDS banks, both for 8-lane and 16-lane phases of a
+// 128-bit read.
+__device__ __forceinline__ int lds_chunk(int row, int chunk) {
+  return row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7));
+}
+
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const T* p) { return __builtin_nontemporal_load(p); }
+
+}  // namespace moe

@@ -1,0 +1,155 @@
+// Memory-bound kernels of the MoE layer on gfx950: weighted combine, weight
+// packing (transpose to contraction-contiguous) and MXFP8 quantisation.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Combine: Y[t] = bf16(sum_j w[t,j] * O[slot_row[t*k+j]]), fp32, j ascending.
+// One thread per 8 consecutive outputs (16-byte loads and stores).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ O, const int32_t* __restrict__ slot_row,
+                                                 const float* __restrict__ w, int T, int k, int H,
+                                                 uint16_t* __restrict__ Y) {
+  const int chunks = H / 8;
+  const long total = (long)T * chunks;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int t = (int)(i / chunks), c = (int)(i - (long)t * chunks);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = slot_row[t * k + j];
+      const float wj = w[t * k + j];
+      const uint4 v = *reinterpret_cast<const uint4*>(O + (size_t)r * H + c * 8);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += wj * bf16_to_f32(d[q] & 0xffffu);
+        acc[2 * q + 1] += wj * bf16_to_f32(d[q] >> 16);
+      }
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(Y + (size_t)t * H + c * 8) = o;
+  }
+}
+
+static int grid_for(long work, int per_block, int cap) {
+  long b = (work + per_block - 1) / per_block;
+  if (b > cap) b = cap;
+  return (int)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_combine(const uint16_t* O, const int32_t* slot_row, const float* w, int T, int k, int H,
+                          uint16_t* Y, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3(grid_for((long)T * (H / 8), 256, 8192)), dim3(256), 0, s, O, slot_row,
+                     w, T, k, H, Y);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Packing: W [E, K, N] -> Wt [E, N, K] (bf16), 64x64 tiles through LDS.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_pack(const uint16_t* __restrict__ W, int K, int N,
+                                              uint16_t* __restrict__ Wt) {
+  __shared__ uint16_t tile[64][66];
+  const int e = blockIdx.z;
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const uint16_t* src = W + (size_t)e * K * N;
+  uint16_t* dst = Wt + (size_t)e * K * N;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    int kk = i / 64, nn = i % 64;
+    tile[kk][nn] = src[(size_t)(k0 + kk) * N + n0 + nn];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    int nn = i / 64, kk = i % 64;
+    dst[(size_t)(n0 + nn) * K + k0 + kk] = tile[kk][nn];
+  }
+}
+
+hipError_t launch_pack(const uint16_t* W, int E, int K, int N, uint16_t* Wt, hipStream_t s) {
+  hipLaunchKernelGGL(k_pack, dim3(N / 64, K / 64, E), dim3(256), 0, s, W, K, N, Wt);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantisation (OCP MX v1.0 section 6.3) of 32-element blocks along rows:
+// scale exponent = floor(log2(amax)) - 8 clamped to [-127, 127] (byte 0 for an
+// all-zero block), elements rounded to E4M3FN to nearest even, saturating.
+// One thread per block of 32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int floor_log2_f32(float a) {  // a > 0, finite
+  uint32_t u = __float_as_uint(a);
+  int ex = (int)(u >> 23);
+  if (ex == 0) return -118 - __builtin_clz(u & 0x7fffffu);  // subnormal: mantissa * 2^-149
+  return ex - 127;
+}
+
+// |x| already scaled into E4M3 range; returns the code (sign included).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (!(a < 448.f)) return sign | 0x7eu;                 // saturate (also catches 448 exactly)
+  if (a < 0.015625f) {                                    // subnormal range: multiples of 2^-9
+    uint32_t m = (uint32_t)__builtin_rintf(a * 512.f);   // 8 -> the smallest normal, code 0x08
+    return sign | m;
+  }
+  int e = floor_log2_f32(a);
+  uint32_t m = (uint32_t)__builtin_rintf(ldexpf(a, 3 - e));  // 8..16
+  if (m == 16) { m = 8; ++e; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | (m - 8);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+__global__ void __launch_bounds__(256) k_mx_quantize(const uint16_t* __restrict__ x, long nblocks,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  for (long b = blockIdx.x * 256L + threadIdx.x; b < nblocks; b += (long)gridDim.x * 256) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = src[i];
+      d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(d[i] & 0xffffu)), fabsf(bf16_to_f32(d[i] >> 16))));
+    uint32_t out[8];
+    uint8_t sbyte = 0;
+    if (amax > 0.f) {
+      int s = floor_log2_f32(amax) - 8;
+      s = s < -127 ? -127 : (s > 127 ? 127 : s);
+      sbyte = (uint8_t)(s + 127);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t c0 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i] & 0xffffu), -s));
+        uint32_t c1 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i] >> 16), -s));
+        uint32_t c2 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i + 1] & 0xffffu), -s));
+        uint32_t c3 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i + 1] >> 16), -s));
+        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = 0;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(q + b * 32);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    sc[b] = sbyte;
+  }
+}
+
+hipError_t launch_mx_quantize(const uint16_t* x, long rows, int K, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  long nb = rows * (K / 32);
+  hipLaunchKernelGGL(k_mx_quantize, dim3(grid_for(nb, 256, 16384)), dim3(256), 0, s, x, nb, q, sc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

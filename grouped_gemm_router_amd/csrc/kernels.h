@@ -1,0 +1,83 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Arguments of every grouped GEMM of the layer (unused fields stay null).
+struct GemmArgs {
+  int T, H, I, E, k;
+  const int32_t* offsets;
+  const int32_t* row_token;
+  const int32_t* row_slot;
+  const float* topk_w;
+  const uint16_t* X;
+  const uint16_t* dY;
+  const uint16_t* Wg_t;   // [E, I, H]
+  const uint16_t* Wu_t;   // [E, I, H]
+  const uint16_t* Wd_t;   // [E, H, I]
+  const uint16_t* Wg;     // [E, H, I]
+  const uint16_t* Wu;     // [E, H, I]
+  const uint16_t* Wd;     // [E, I, H]
+  uint16_t* Hrows;        // [A, I]
+  uint16_t* Orows;        // [A, H]
+  float* P;               // [A, I]
+  uint16_t* dGU;          // [A, 2I]
+  float* dXr;             // [A, H]
+  float* dwt_part;        // [A, nparts]
+  int nparts;
+  uint16_t* dWg;
+  uint16_t* dWu;
+  uint16_t* dWd;
+};
+
+int num_cus();
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                        hipStream_t s);
+size_t dispatch_ws_bytes(long A, int E);
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* offsets,
+                           int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
+                           int32_t* ws, hipStream_t s);
+hipError_t launch_pack(const uint16_t* W, int E, int K, int N, uint16_t* Wt, hipStream_t s);
+hipError_t launch_mx_quantize(const uint16_t* x, long rows, int K, uint8_t* q, uint8_t* sc,
+                              hipStream_t s);
+hipError_t launch_combine(const uint16_t* O, const int32_t* slot_row, const float* w, int T,
+                          int k, int H, uint16_t* Y, hipStream_t s);
+
+// bf16 expert GEMMs
+hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s);
+hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s);
+hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s);
+hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s);
+hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s);
+hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s);
+hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s);
+int bwd_nparts(int I);
+hipError_t launch_bwd_token_reduce(const GemmArgs& a, const int32_t* slot_row, uint16_t* dX,
+                                   float* d_topk_w, hipStream_t s);
+
+// small-token path: every expert has at most T <= DECODE_MAX_T rows
+constexpr int DECODE_MAX_T = 64;
+hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s);
+
+// MXFP8 expert GEMMs
+struct MxArgs {
+  int T, H, I, E, k;
+  const int32_t* offsets;
+  const int32_t* row_token;
+  const uint8_t* Xq;  const uint8_t* Xs;    // [T, H], [T, H/32]
+  const uint8_t* Wg;  const uint8_t* Sg;    // [E, I, H], [E, I, H/32]
+  const uint8_t* Wu;  const uint8_t* Su;
+  const uint8_t* Wd;  const uint8_t* Sd;    // [E, H, I], [E, H, I/32]
+  uint16_t* Hrows;                          // [A, I] bf16
+  const uint8_t* Hq;  const uint8_t* Hs;    // [A, I], [A, I/32]
+  uint16_t* Orows;                          // [A, H]
+};
+hipError_t launch_mx_gateup(const MxArgs& a, hipStream_t s);
+hipError_t launch_mx_down(const MxArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,233 @@
+// Router (softmax -> top-k -> renormalise) and expert-major dispatch
+// (histogram, prefix scan, stable scatter) on gfx950.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router: one wave per token.  Each lane keeps up to 16 logits (E <= 1024) in
+// registers; k rounds of a wave arg-max pick the experts in descending logit
+// order, ties to the lowest index.  The weights are exp(l_j - l_max) over the
+// chosen logits, normalised by their sum (softmax over E renormalised over k).
+// ---------------------------------------------------------------------------
+constexpr int ROUTE_MAX_PER_LANE = 16;
+
+__device__ __forceinline__ bool route_better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits, int T, int E, int k,
+                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[ROUTE_MAX_PER_LANE];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+    int e = lane + 64 * i;
+    v[i] = (e < E) ? row[e] : 0.f;
+    if (e >= E) taken |= 1u << i;
+  }
+  float sel_v = 0.f;   // lane j < k keeps the j-th chosen logit
+  int sel_i = 0;
+  float top = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+      int e = lane + 64 * i;
+      if (!(taken & (1u << i)) && route_better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ov = __shfl_xor(bv, o, 64);
+      int oi = __shfl_xor(bi, o, 64);
+      if (route_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) {
+      sel_v = bv;
+      sel_i = bi;
+    }
+    if (j == 0) top = bv;
+  }
+  float ex = (lane < k) ? expf(sel_v - top) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane < k) {
+    topk_idx[(size_t)t * k + lane] = sel_i;
+    topk_w[(size_t)t * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
+  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch.  The T*k slots are cut into chunks of 4096 (one block, four
+// waves of 1024 consecutive slots each).  Inside a wave, 64 slots are handled
+// at a time: ten ballots over the bits of the expert id give every lane the
+// mask of lanes holding the same expert, so its rank among equal experts in
+// slot order is a popcount, and one lane per expert updates the running count.
+// No atomics anywhere: the positions are the same on every run.
+//   k_dispatch_count:   per-wave histograms  -> ws[(chunk*4 + wave) * E + e]
+//   k_dispatch_scatter: offsets (scan of the totals), per-wave bases, then the
+//                       stable scatter of (row_token, row_slot, slot_row).
+// ---------------------------------------------------------------------------
+constexpr int DISPATCH_CHUNK = 4096;
+constexpr int DISPATCH_WAVE_SLOTS = 1024;
+constexpr int DISPATCH_MAX_E = 1024;
+
+size_t dispatch_ws_bytes(long A, int E) {
+  long nchunks = (A + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
+  if (nchunks < 1) nchunks = 1;
+  return (size_t)nchunks * 4 * E * sizeof(int32_t);
+}
+
+// Mask of the lanes whose 11-bit key equals this lane's key.
+__device__ __forceinline__ uint64_t match_key(int key) {
+  uint64_t m = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 11; ++b) {
+    uint64_t bal = __ballot((key >> b) & 1);
+    m &= ((key >> b) & 1) ? bal : ~bal;
+  }
+  return m;
+}
+
+__global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restrict__ idx, long A, int E,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int hist[4][DISPATCH_MAX_E];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < 4 * DISPATCH_MAX_E; e += 256) (&hist[0][0])[e] = 0;
+  __syncthreads();
+  const long base = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
+  for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
+    long s = base + g * 64 + lane;
+    int e = (s < A) ? idx[s] : -1;
+    if (e >= E) e = -1;                       // out-of-range ids are skipped
+    int key = (e >= 0) ? e : 0x400;
+    uint64_t m = match_key(key);
+    // the highest lane of each group of equal experts adds the group size
+    bool leader = (m >> lane) == 1ull;
+    if (e >= 0 && leader) hist[wave][key] += __popcll(m);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    for (int w = 0; w < 4; ++w) counts[((long)blockIdx.x * 4 + w) * E + e] = hist[w][e];
+}
+
+__global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restrict__ idx, long A, int E, int k,
+                                                          const int32_t* __restrict__ counts, int nsub,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ row_token,
+                                                          int32_t* __restrict__ row_slot,
+                                                          int32_t* __restrict__ slot_row) {
+  __shared__ int base[4][DISPATCH_MAX_E];
+  __shared__ int red[8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int my_sub0 = blockIdx.x * 4;
+  // per-expert totals and the prefix over earlier sub-chunks (4 experts per thread)
+  int tot[4], pre[4][4];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = threadIdx.x * 4 + i;
+    tot[i] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pre[i][w] = 0;
+    if (e < E) {
+      for (int sc = 0; sc < nsub; ++sc) {
+        int c = counts[(long)sc * E + e];
+        if (sc < my_sub0) {
+          pre[i][0] += c;
+        } else if (sc < my_sub0 + 4) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (sc - my_sub0 < w) pre[i][w] += c;
+        }
+        tot[i] += c;
+      }
+    }
+    sum += tot[i];
+  }
+  // pre[i][w] for w > 0 must also include the earlier sub-chunks
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 1; w < 4; ++w) pre[i][w] += pre[i][0];
+  // exclusive scan of the totals over experts
+  int x = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += red[w];
+  int ex = wave_base + x - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = threadIdx.x * 4 + i;
+    if (e < E) {
+      if (blockIdx.x == 0) offsets[e] = ex;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) base[w][e] = ex + pre[i][w];
+    }
+    ex += tot[i];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 255) offsets[E] = ex;
+  __syncthreads();
+  // stable scatter of this wave's 1024 slots
+  const long sbase = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
+    long s = sbase + g * 64 + lane;
+    int e = (s < A) ? idx[s] : -1;
+    if (e >= E) e = -1;                       // out-of-range ids are skipped
+    int key = (e >= 0) ? e : 0x400;
+    uint64_t m = match_key(key);
+    if (e >= 0) {
+      int pos = base[wave][key] + __popcll(m & below);
+      row_token[pos] = (int)(s / k);
+      row_slot[pos] = (int)s;
+      slot_row[s] = pos;
+    }
+    // wave-wide order: all lanes read base before the leaders update it
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && (m >> lane) == 1ull) base[wave][key] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* row_token,
+                           int32_t* row_slot, int32_t* slot_row, int32_t* ws, hipStream_t s) {
+  long A = (long)T * k;
+  int nchunks = (int)((A + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK);
+  if (nchunks < 1) nchunks = 1;  // block 0 still writes the offsets when there are no slots
+  hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, A, E, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), 0, s, idx, A, E, k, ws, nchunks * 4,
+                     offsets, row_token, row_slot, slot_row);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+"""Routed MoE expert layer on top of the C ABI.
+
+``MoELayer`` owns the packed (and, for MXFP8, quantised) expert weights and,
+per token count, every intermediate buffer and workspace, so that a warmed
+forward or backward enqueues kernels only (no allocation) and can be captured
+in a HIP graph.  The five calls run in the order the LightMoE README lists
+for one inference call (dispatch, gate/up projection, gated activation, down
+projection, routing-weight application and combine), preceded by routing.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class MoELayer:
+    def __init__(self, H: int, I: int, E: int, k: int, dtype: str = "bf16", device="cuda"):
+        self.H, self.I, self.E, self.k, self.dtype = H, I, E, k, dtype
+        self.device = torch.device(device)
+        self.W_gate = self.W_up = self.W_down = None
+        self._plans = {}
+
+    # -- weights (once, outside any timed region) ---------------------------------
+    def load_weights(self, W_gate: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor, keep_math=True):
+        """W_gate, W_up [E, H, I] and W_down [E, I, H] bf16 on the device."""
+        self.Wg_t = B.pack_weights(W_gate)
+        self.Wu_t = B.pack_weights(W_up)
+        self.Wd_t = B.pack_weights(W_down)
+        if keep_math:
+            self.W_gate, self.W_up, self.W_down = W_gate, W_up, W_down
+        self.scales = None
+        if self.dtype == "mxfp8":
+            qg, sg = B.mx_quantize(self.Wg_t)
+            qu, su = B.mx_quantize(self.Wu_t)
+            qd, sd = B.mx_quantize(self.Wd_t)
+            self.Wg_t, self.Wu_t, self.Wd_t = qg, qu, qd
+            self.scales = (sg, su, sd)
+        return self
+
+    # -- buffers per token count ------------------------------------------------------
+    def plan(self, T: int, backward: bool = False):
+        key = (T, backward)
+        if key in self._plans:
+            return self._plans[key]
+        H, I, E, k, dev = self.H, self.I, self.E, self.k, self.device
+        A = T * k
+        p = B.problem(T, H, I, E, k, self.dtype)
+        pl = {
+            "topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev),
+            "topk_w": torch.empty(T, k, dtype=torch.float32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "row_token": torch.empty(A, dtype=torch.int32, device=dev),
+            "row_slot": torch.empty(A, dtype=torch.int32, device=dev),
+            "slot_row": torch.empty(A, dtype=torch.int32, device=dev),
+            "H_rows": torch.empty(A, I, dtype=torch.bfloat16, device=dev),
+            "O_rows": torch.empty(A, H, dtype=torch.bfloat16, device=dev),
+            "Y": torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+            "ws_dispatch": torch.empty(max(1, B.workspace_size(p, B.CALL_DISPATCH)), dtype=torch.uint8, device=dev),
+            "ws_mlp": torch.empty(max(1, B.workspace_size(p, B.CALL_EXPERT_MLP)), dtype=torch.uint8, device=dev),
+        }
+        if backward:
+            pl["ws_bwd"] = torch.empty(B.workspace_size(p, B.CALL_BACKWARD), dtype=torch.uint8, device=dev)
+            pl["grads"] = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                           torch.empty(E, H, I, dtype=torch.bfloat16, device=dev),
+                           torch.empty(E, H, I, dtype=torch.bfloat16, device=dev),
+                           torch.empty(E, I, H, dtype=torch.bfloat16, device=dev),
+                           torch.empty(T, k, dtype=torch.float32, device=dev))
+        self._plans[key] = pl
+        return pl
+
+    # -- forward / backward -----------------------------------------------------------
+    def forward(self, logits: torch.Tensor, X: torch.Tensor, backward_plan: bool = False, mlp_events=None):
+        """Runs route, dispatch, expert MLP and combine on the current stream.
+        ``mlp_events`` = (start, end) torch.cuda.Events recorded around the expert
+        MLP call (same stream as its kernels)."""
+        T = X.shape[0]
+        pl = self.plan(T, backward_plan)
+        B.route(logits, self.k, pl["topk_idx"], pl["topk_w"])
+        B.dispatch(pl["topk_idx"], self.E, (pl["offsets"], pl["row_token"], pl["row_slot"], pl["slot_row"]),
+                   ws=pl["ws_dispatch"])
+        if mlp_events is not None:
+            mlp_events[0].record()
+        B.expert_mlp(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
+                     scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"])
+        if mlp_events is not None:
+            mlp_events[1].record()
+        B.combine(pl["O_rows"], pl["slot_row"], pl["topk_w"], pl["Y"])
+        return pl["Y"]
+
+    def backward(self, X: torch.Tensor, dY: torch.Tensor):
+        """Gradients of the last forward with the same X (needs backward_plan=True)."""
+        if self.dtype != "bf16" or self.W_gate is None:
+            raise ValueError("backward needs bf16 weights kept in the math layout")
+        T = X.shape[0]
+        pl = self.plan(T, True)
+        return B.backward(X, dY, pl["topk_w"], pl["row_token"], pl["row_slot"], pl["slot_row"], pl["offsets"],
+                          self.W_gate, self.W_up, self.W_down, self.Wg_t, self.Wu_t, out=pl["grads"],
+                          ws=pl["ws_bwd"])

@@ -67,8 +67,8 @@ CONFIGS = {
 }
 
 
-def config(name: str, **over) -> MoEConfig:
-    cfg = CONFIGS[name]
+def config(base: str, **over) -> MoEConfig:
+    cfg = CONFIGS[base]
     return replace(cfg, **over) if over else cfg
 
 

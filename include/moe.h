@@ -1,0 +1,216 @@
+/*
+ * moe.h - C ABI of a routed Mixture-of-Experts expert layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer is the dropless top-k routed MoE described by the LigerCute
+ * README ("LigerCute - native CUTLASS + NVSHMEM kernels": Overview, Forward
+ * pass, Backward pass) and the LightMoE README (lightmoe 0.1.0: Grouped GEMM,
+ * MoE inference, MoE training).  One GPU runs every expert:
+ *
+ *   moe_route       softmax over E logits -> top-k -> renormalise
+ *   moe_dispatch    expert-major order of the T*k token-expert assignments
+ *   moe_expert_mlp  grouped GEMM gate/up + SwiGLU, grouped GEMM down
+ *   moe_combine     weighted sum of each token's k expert rows
+ *   moe_backward    dX, dW_gate, dW_up, dW_down, d(top-k weights)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers to dense row-major arrays; the
+ *   shapes are given in elements next to each argument.  bf16 tensors are
+ *   passed as raw 16-bit patterns.
+ * - The caller owns every buffer: inputs, outputs and the workspace (sized by
+ *   moe_workspace_size).  No call allocates device memory or synchronises;
+ *   every call only enqueues work on `stream` (a hipStream_t, NULL for the
+ *   default stream) and returns.  Use one workspace per concurrent stream.
+ * - Arguments are checked on the host before anything is enqueued; on any
+ *   error nothing is launched and the status says why.  A device that is not
+ *   gfx950 gives MOE_ERR_UNSUPPORTED_DEVICE.  A launch failure gives
+ *   MOE_ERR_HIP.  No C++ exception crosses this interface.
+ * - Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31; H and I multiples
+ *   of 64 (MXFP8: multiples of 128).
+ * - Results are deterministic: the same inputs give bitwise-identical outputs
+ *   (no floating-point atomics, fixed reduction orders).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,       /* null pointer, non-positive size, k > E ... */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2, /* outside the limits listed above */
+  MOE_ERR_WORKSPACE = 3,         /* workspace missing or smaller than required */
+  MOE_ERR_UNSUPPORTED_DEVICE = 4,/* current device is not gfx950 */
+  MOE_ERR_HIP = 5                /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_DTYPE_BF16 = 0,   /* X, weights and h in bf16 */
+  MOE_DTYPE_MXFP8 = 1   /* X, weights and h as FP8 E4M3 with one E8M0 scale
+                           per 32 elements along the contraction axis */
+} moe_dtype;
+
+/* Problem shape.  T tokens, hidden size H, expert intermediate size I,
+ * E experts, k experts per token. */
+typedef struct {
+  int32_t T, H, I, E, k;
+  int32_t dtype; /* moe_dtype */
+} moe_problem;
+
+/* Which call a workspace is sized for (moe_workspace_size). */
+typedef enum {
+  MOE_CALL_DISPATCH = 0,
+  MOE_CALL_EXPERT_MLP = 1,
+  MOE_CALL_BACKWARD = 2
+} moe_call;
+
+/* Human-readable name of a status code (static storage; host only). */
+MOE_API const char* moe_status_string(int status);
+
+/* Checks a problem against the limits above (host only, no device access). */
+MOE_API moe_status moe_validate_problem(const moe_problem* p);
+
+/* Bytes of device workspace `call` needs for problem `p` (host only). */
+MOE_API moe_status moe_workspace_size(const moe_problem* p, int call, size_t* bytes);
+
+/* MOE_OK when the current HIP device is gfx950 (queries the device once). */
+MOE_API moe_status moe_check_device(void);
+
+/*
+ * Routing (LightMoE "MoE inference": top_k_ids int32 with distinct experts
+ * per token, top_k_weights fp32; softmax -> top-k -> renormalise).
+ *   logits   [T, E] fp32 in
+ *   topk_idx [T, k] int32 out: experts in descending logit order, ties to the
+ *            lowest expert index (-0.0 equals +0.0); NaN logits are invalid
+ *   topk_w   [T, k] fp32 out: exp(l_j - l_max) / sum over the k chosen,
+ *            equal to the softmax over all E renormalised over the k.
+ */
+MOE_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Expert-major dispatch (LigerCute "Forward pass": routed tokens are sorted;
+ * LightMoE "Grouped GEMM": contiguous expert-major rows with an int32
+ * m_indptr of length E+1, zero-row experts valid; "MoE training": gather
+ * indices and inverse slots).  Assignment (t, j) has slot s = t*k + j; rows
+ * are grouped by expert and, inside an expert, ordered by slot.
+ *   topk_idx       [T, k] int32 in, each value in [0, E), distinct per token
+ *   expert_offsets [E+1] int32 out: rows of expert e are
+ *                  [expert_offsets[e], expert_offsets[e+1])
+ *   row_token      [T*k] int32 out: token of each row
+ *   row_slot       [T*k] int32 out: slot of each row
+ *   slot_row       [T*k] int32 out: row of each slot (inverse of row_slot)
+ *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_DISPATCH)
+ * Out-of-range expert ids are not detected on the device; they give
+ * unspecified (but memory-safe) output.
+ */
+MOE_API moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                int32_t* expert_offsets, int32_t* row_token,
+                                int32_t* row_slot, int32_t* slot_row,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weight packing, done once when weights are loaded (LightMoE "Standalone
+ * GEMM": packing is a separate operation, outside latency measurements; its
+ * grouped GEMM takes b as [num_experts, N, K]).
+ *   W  [E, K, N] bf16 in  (the math layout: x @ W)
+ *   Wt [E, N, K] bf16 out (contraction axis contiguous)
+ */
+MOE_API moe_status moe_pack_weights(const void* W, int32_t E, int32_t K, int32_t N,
+                                    void* Wt, void* stream);
+
+/*
+ * MXFP8 quantisation along rows (OCP Microscaling v1.0, section 6.3; the
+ * per-32 E8M0 block scaling named by the cutedsl-megamoe page).  For every
+ * block of 32 consecutive values: shared exponent = floor(log2(max|v|)) - 8
+ * clamped to [-127, 127] (scale byte = exponent + 127; 0 for an all-zero
+ * block); elements = v * 2^-exponent rounded to FP8 E4M3FN, to nearest even,
+ * saturating at +-448.
+ *   x      [rows, K] bf16 in, K a multiple of 32
+ *   q      [rows, K] uint8 out (E4M3FN codes)
+ *   scales [rows, K/32] uint8 out (E8M0)
+ */
+MOE_API moe_status moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* q,
+                                   uint8_t* scales, void* stream);
+
+/*
+ * Expert MLP over the expert-major rows (LightMoE "MoE inference": gate/up
+ * projection, gated activation, requantisation, down projection):
+ *   G = X[row_token[r]] W_gate[e], U = X[row_token[r]] W_up[e]   (fp32 accumulation)
+ *   h[r] = bf16(silu(G) * U),  O[r] = bf16(h[r] W_down[e])
+ * for every row r of every expert e with rows.  Experts without rows are
+ * never read.
+ *   p              problem (dtype selects bf16 or MXFP8 operands)
+ *   X              [T, H] bf16
+ *   row_token, expert_offsets   from moe_dispatch
+ *   bf16:  Wg_t, Wu_t [E, I, H] bf16 and Wd_t [E, H, I] bf16 (moe_pack_weights);
+ *          Sg, Su, Sd must be NULL
+ *   MXFP8: Wg_t, Wu_t [E, I, H] and Wd_t [E, H, I] E4M3 codes with
+ *          Sg, Su [E, I, H/32] and Sd [E, H, I/32] E8M0 scales (moe_mx_quantize
+ *          of the packed bf16 weights); X is quantised here, and h is
+ *          requantised to MXFP8 along I before the down projection
+ *   H_rows         [T*k, I] bf16 out (h, bf16 in both modes)
+ *   O_rows         [T*k, H] bf16 out
+ *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_EXPERT_MLP)
+ */
+MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token,
+                                  const int32_t* expert_offsets, const void* Wg_t,
+                                  const void* Wu_t, const void* Wd_t, const uint8_t* Sg,
+                                  const uint8_t* Su, const uint8_t* Sd, void* H_rows,
+                                  void* O_rows, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine (LigerCute "Forward pass": a final local combine applies
+ * the router weights; LightMoE: routing-weight application and deterministic
+ * combine):  Y[t] = bf16( sum_{j=0..k-1} topk_w[t,j] * O_rows[slot_row[t*k+j]] ),
+ * accumulated in fp32 in ascending j.
+ *   O_rows [T*k, H] bf16, slot_row [T*k] int32, topk_w [T, k] fp32, Y [T, H] bf16 out
+ */
+MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, const float* topk_w,
+                               int32_t T, int32_t k, int32_t H, void* Y, void* stream);
+
+/*
+ * Backward (LigerCute "Backward pass": activation recomputation, input and
+ * expert-weight gradients, routed dX reduced back to the tokens; LightMoE:
+ * deterministic input-, weight- and router-gradient kernels).  bf16 only.
+ * Per row r (token t, slot s, expert e, weight w = topk_w[s]):
+ *   G, U, h recomputed as in moe_expert_mlp;  P = dY[t] W_down[e]^T (fp32)
+ *   d_topk_w[s] = <h, P>;  dh = w P
+ *   du = bf16(dh * silu(G)),  dg = bf16(dh * U * silu'(G)),  dO = bf16(w dY[t])
+ *   dX[t]      = bf16( sum_j (dg W_gate[e]^T + du W_up[e]^T) ), j ascending
+ *   dW_gate[e] = bf16( sum_r X[t]^T dg ),  dW_up[e] = bf16( sum_r X[t]^T du )
+ *   dW_down[e] = bf16( sum_r h^T dO )      (all sums in fp32, fixed order;
+ *                                           experts without rows get zeros)
+ *   X, dY [T, H] bf16;  topk_w [T, k] fp32;  dispatch arrays as above
+ *   W_gate, W_up [E, H, I], W_down [E, I, H] bf16 (math layout)
+ *   Wg_t, Wu_t [E, I, H] bf16 (moe_pack_weights of W_gate, W_up)
+ *   dX [T, H], dW_gate, dW_up [E, H, I], dW_down [E, I, H] bf16 out;
+ *   d_topk_w [T, k] fp32 out
+ *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_BACKWARD)
+ */
+MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY,
+                                const float* topk_w, const int32_t* row_token,
+                                const int32_t* row_slot, const int32_t* slot_row,
+                                const int32_t* expert_offsets, const void* W_gate,
+                                const void* W_up, const void* W_down, const void* Wg_t,
+                                const void* Wu_t, void* dX, void* dW_gate, void* dW_up,
+                                void* dW_down, float* d_topk_w, void* ws, size_t ws_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

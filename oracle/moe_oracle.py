@@ -434,3 +434,26 @@ def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact:
             acc = acc + dxr[:, j]
         out["dX"] = rnd(acc)
     return out
+
+
+def backward_tokens(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, tokens, exact: bool = False):
+    """dX and d_topk_w of the listed tokens only, straight from the per-row
+    definition (same formulas as ``backward``).  Returns (dX [n, H], dwt [n, k])."""
+    rnd = (lambda a: a) if exact else bf16_round
+    Xv, dYv = _as_f64(X), _as_f64(dY)
+    gg, gu, gd = _expert_getter(W_gate), _expert_getter(W_up), _expert_getter(W_down)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    k = idx.shape[1]
+    dX = np.zeros((len(tokens), Xv.shape[1]))
+    dwt = np.zeros((len(tokens), k))
+    for n, t in enumerate(tokens):
+        acc = np.zeros(Xv.shape[1])
+        for j in range(k):
+            e = int(idx[t, j])
+            r = expert_backward_rows(Xv[t:t + 1], dYv[t:t + 1], w[t, j:j + 1], gg(e), gu(e), gd(e), exact=exact)
+            acc = acc + r["dXr"][0]
+            dwt[n, j] = r["dwt"][0]
+        dX[n] = acc
+    return rnd(dX), dwt

@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU parity tests: moving bf16 bit patterns to and
+from the device, device-resident seeded weights, and the tolerance check
+|gpu - oracle| <= 1e-2 + 2e-2 * |oracle| (elementwise)."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as orc
+from grouped_gemm_router_amd import workloads as wl
+
+ATOL, RTOL = 1e-2, 2e-2
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return orc.bf16_decode(to_bits(t))
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check_close(gpu, ref, what: str, atol=ATOL, rtol=RTOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite GPU values"
+    err = np.abs(gpu - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    rel = err / np.maximum(np.abs(ref), 1e-6)
+    msg = (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; max abs err {err.max():.3g}; "
+           f"mean_rel {float(np.mean(rel[np.abs(ref) > 1e-3])) if (np.abs(ref) > 1e-3).any() else 0:.3g}")
+    assert not bad.any(), msg
+    return msg
+
+
+def device_weights(cfg, name, experts=None, fill=float("nan")):
+    """[E, K, N] bf16 device tensor with the seeded weights of ``experts`` (all
+    when None); the others hold ``fill`` (NaN: an unread expert stays unread)."""
+    K, N = wl.weight_shape(cfg, name)
+    out = torch.full((cfg.E, K, N), fill, dtype=torch.bfloat16, device="cuda")
+    todo = range(cfg.E) if experts is None else sorted(set(int(e) for e in experts))
+
+    def one(e):
+        return e, wl.make_expert_weight(cfg, name, e)
+
+    with ThreadPoolExecutor(8) as ex:
+        for e, bits in ex.map(one, todo):
+            out[e].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    return out
+
+
+def host_weight_fn(cfg, name):
+    """Per-expert weight getter for the oracle (regenerates the seeded draw)."""
+    return lambda e: wl.make_expert_weight(cfg, name, e)

@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports exactly the
+moe_* entry points include/moe.h declares, links no torch, and the host-side
+argument checks return the documented status codes before any launch."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "grouped_gemm_router_amd", "libmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    from grouped_gemm_router_amd import binding
+    declared = _declared()
+    assert len(declared) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("moe_"))
+    assert exported == declared
+    assert sorted(binding.EXPORTS) == declared
+    # nothing but the moe_ prefix (and toolchain-internal underscore symbols) is exported
+    others = [l.split()[-1] for l in out.splitlines() if " T " in l and not l.split()[-1].startswith(("moe_", "_"))]
+    assert others == []
+
+
+def test_no_torch_dependency():
+    out = subprocess.run(["readelf", "-d", LIB], capture_output=True, text=True).stdout
+    needed = re.findall(r"NEEDED.*\[(.*)\]", out)
+    assert not any("torch" in n or "c10" in n for n in needed)
+    assert any("amdhip64" in n for n in needed)
+
+
+def test_status_strings():
+    from grouped_gemm_router_amd import binding as B
+    for code, name in B.STATUS.items():
+        assert B.status_string(code) == name
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((64, 256, 128, 8, 2, "bf16"), 0),
+    ((4096, 2048, 512, 256, 8, "bf16"), 0),
+    ((8192, 4096, 1024, 512, 10, "mxfp8"), 0),
+    ((0, 256, 128, 8, 2, "bf16"), 0),          # empty batch is valid
+    ((64, 256, 128, 8, 9, "bf16"), 1),         # k > E
+    ((64, 256, 128, 8, 0, "bf16"), 1),         # k < 1
+    ((-1, 256, 128, 8, 2, "bf16"), 1),
+    ((64, 0, 128, 8, 2, "bf16"), 1),
+    ((64, 250, 128, 8, 2, "bf16"), 2),         # H not a multiple of 64
+    ((64, 256, 100, 8, 2, "bf16"), 2),
+    ((64, 192, 128, 8, 2, "mxfp8"), 2),        # MXFP8 needs multiples of 128
+    ((64, 256, 128, 2048, 2, "bf16"), 2),      # E > 1024
+    ((64, 256, 128, 64, 33, "bf16"), 2),       # k > 32
+    ((2**28, 256, 128, 64, 8, "bf16"), 2),     # T*k >= 2^31
+])
+def test_validate_problem(args, expect):
+    from grouped_gemm_router_amd import binding as B
+    assert B.validate_problem(B.problem(*args)) == expect
+
+
+def test_workspace_sizes():
+    from grouped_gemm_router_amd import binding as B
+    p = B.problem(4096, 2048, 512, 256, 8)
+    assert B.workspace_size(p, B.CALL_DISPATCH) >= 8 * 4 * 256 * 4
+    assert B.workspace_size(p, B.CALL_EXPERT_MLP) == 0
+    A, H, I = 4096 * 8, 2048, 512
+    assert B.workspace_size(p, B.CALL_BACKWARD) >= A * I * 4 + A * 2 * I * 2 + A * I * 2 + A * H * 4
+    pm = B.problem(8192, 4096, 1024, 512, 10, "mxfp8")
+    assert B.workspace_size(pm, B.CALL_EXPERT_MLP) >= 8192 * 4096 + 81920 * 1024
+    with pytest.raises(B.MoEError):
+        B.workspace_size(pm, B.CALL_BACKWARD)          # backward is bf16 only
+    with pytest.raises(B.MoEError):
+        B.workspace_size(B.problem(64, 256, 128, 8, 9), B.CALL_DISPATCH)
+
+
+def test_calls_reject_bad_arguments_before_touching_the_device():
+    """Argument errors come back before the device check, so they are seen
+    here even without a GPU (null pointers, k > E, small workspace)."""
+    import ctypes
+    from grouped_gemm_router_amd import binding as B
+    lib = B.lib
+    assert lib.moe_route(None, 4, 8, 2, None, None, None) == 1
+    assert lib.moe_route(ctypes.c_void_p(16), 4, 8, 9, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == 1
+    assert lib.moe_dispatch(ctypes.c_void_p(16), 4, 8, 2, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                            ctypes.c_void_p(16), ctypes.c_void_p(16), None, 0, None) == 3
+    p = B.problem(64, 256, 128, 8, 2)
+    assert lib.moe_expert_mlp(ctypes.byref(p), None, None, None, None, None, None, None, None, None, None,
+                              None, None, 0, None) == 1
+    # scales given for a bf16 problem
+    v = ctypes.c_void_p(16)
+    assert lib.moe_expert_mlp(ctypes.byref(p), v, v, v, v, v, v, v, v, v, v, v, None, 0, None) == 1
+    pm = B.problem(64, 256, 128, 8, 2, "mxfp8")
+    assert lib.moe_expert_mlp(ctypes.byref(pm), v, v, v, v, v, v, v, v, v, v, v, None, 0, None) == 3
+    assert lib.moe_combine(v, v, v, 4, 2, 60, v, None) == 2
+    assert lib.moe_mx_quantize(v, 4, 48, v, v, None) == 2
+    assert lib.moe_pack_weights(v, 2, 100, 64, v, None) == 2
+    assert lib.moe_backward(ctypes.byref(pm), *([v] * 17), None, 0, None) == 2

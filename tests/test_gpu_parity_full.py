@@ -1,0 +1,87 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (MoELayer.forward / backward).  Routing and dispatch are
+compared whole and bit for bit; the layer output, h and O rows and the
+gradients on samples the oracle computes one by one (tokens, rows, experts).
+Unused experts' weights are NaN, which also checks that they are never read."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+from grouped_gemm_router_amd import workloads as wl
+
+from gpu_helpers import check_close, device_weights, host_weight_fn, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _setup(name, backward=False):
+    from grouped_gemm_router_amd.layer import MoELayer
+    cfg = wl.config(name)
+    logits, X = wl.make_logits(cfg), wl.make_x(cfg)
+    idx, w = orc.route(logits, cfg.k)
+    active = np.unique(idx)
+    _say(name, "active experts", len(active))
+    W = {n: device_weights(cfg, n, experts=active) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(W["gate"], W["up"], W["down"],
+                                                                         keep_math=backward)
+    layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=backward)
+    torch.cuda.synchronize()
+    return cfg, layer, logits, X, idx, w
+
+
+@pytest.mark.parametrize("name", ["prefill", "decode", "large_mxfp8", "train"])
+def test_forward_full_size_sampled(name):
+    cfg, layer, logits, X, idx, w = _setup(name)
+    pl = layer.plan(cfg.T)
+    off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
+    assert np.array_equal(pl["topk_idx"].cpu().numpy(), idx)
+    for g, r in zip((pl["offsets"], pl["row_token"], pl["row_slot"], pl["slot_row"]),
+                    (off, row_token, row_slot, slot_row)):
+        assert np.array_equal(g.cpu().numpy(), r)
+    rng = np.random.default_rng(123)
+    ntok = min(cfg.T, 48)
+    tokens = np.sort(rng.choice(cfg.T, ntok, replace=False))
+    tokens[0], tokens[-1] = 0, cfg.T - 1
+    fn = lambda n: host_weight_fn(cfg, n)
+    mx = cfg.dtype == "mxfp8"
+    Yref = orc.layer_forward_tokens(X, idx, w, fn("gate"), fn("up"), fn("down"), tokens, mxfp8=mx)
+    Y = to_f64(pl["Y"])
+    check_close(Y[tokens], Yref, f"{name} Y[sampled tokens]")
+    assert np.isfinite(Y).all()
+    # h and O rows of sampled rows, including each expert segment's first and last row
+    seg_ends = np.concatenate([off[:-1][np.diff(off) > 0], off[1:][np.diff(off) > 0] - 1])
+    rows = np.unique(np.concatenate([rng.choice(cfg.A, min(cfg.A, 64), replace=False), seg_ends[:64]]))
+    Hg, Og = to_f64(pl["H_rows"][torch.from_numpy(rows).cuda()]), to_f64(pl["O_rows"][torch.from_numpy(rows).cuda()])
+    Xv = orc.bf16_decode(X)
+    for n, r in enumerate(rows):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        _, _, h, O = orc.expert_forward_rows(Xv[row_token[r]][None], orc.bf16_decode(fn("gate")(e)),
+                                             orc.bf16_decode(fn("up")(e)), orc.bf16_decode(fn("down")(e)), mxfp8=mx)
+        check_close(Hg[n], h[0], f"{name} h[{r}]")
+        check_close(Og[n], O[0], f"{name} O[{r}]")
+
+
+def test_backward_full_size_sampled():
+    cfg, layer, logits, X, idx, w = _setup("train", backward=True)
+    dY = wl.make_dy(cfg)
+    dX, dWg, dWu, dWd, dtw = layer.backward(to_dev(X), to_dev(dY))
+    torch.cuda.synchronize()
+    _say("train backward done on GPU")
+    fn = lambda n: host_weight_fn(cfg, n)
+    rng = np.random.default_rng(7)
+    tokens = np.sort(rng.choice(cfg.T, 24, replace=False))
+    rdX, rdwt = orc.backward_tokens(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), tokens)
+    check_close(to_f64(dX[torch.from_numpy(tokens).cuda()]), rdX, "dX[sampled tokens]")
+    check_close(dtw.cpu().numpy()[tokens], rdwt, "d_topk_w[sampled tokens]")
+    experts = [0, int(rng.integers(1, cfg.E - 1)), cfg.E - 1]
+    ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), experts=experts, want_dx=False,
+                       E=cfg.E)
+    for key, t in (("dWg", dWg), ("dWu", dWu), ("dWd", dWd)):
+        for e in experts:
+            check_close(to_f64(t[e]), ref["dW"][key][e], f"{key}[{e}]")
+    assert np.isfinite(to_f64(dX)).all()

@@ -1,0 +1,221 @@
+"""GPU parity of every call against the CPU oracle on small and ragged
+problems (several tiles, partial tiles, empty experts, degenerate k and E),
+plus determinism and NaN-poisoned unused experts.  Integer outputs must match
+bit for bit; floating-point outputs within 1e-2 + 2e-2*|oracle|."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+from grouped_gemm_router_amd import workloads as wl
+
+from gpu_helpers import check_close, device_weights, host_weight_fn, to_bits, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _B():
+    from grouped_gemm_router_amd import binding
+    return binding
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 rounding of the device conversion (combine with exact products)
+# ------------------------------------------------------------------------------------------
+def test_combine_rounds_to_nearest_even():
+    B = _B()
+    _say("combine rounding")
+    rng = np.random.default_rng(0)
+    T, H = 512, 256
+    O = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    for wv in (1 + 2.0 ** -9, 1 - 2.0 ** -9, 1 + 3 * 2.0 ** -9, 0.5 + 2.0 ** -10):
+        w = np.full((T, 1), wv, np.float32)
+        Y = B.combine(to_dev(O), torch.arange(T, dtype=torch.int32, device="cuda"), torch.from_numpy(w).cuda())
+        ref = orc.bf16_encode(orc.bf16_decode(O) * float(np.float32(wv)))
+        assert np.array_equal(to_bits(Y), ref)
+
+
+# ------------------------------------------------------------------------------------------
+# routing and dispatch: bit-exact on every workload's logits
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "prefill", "decode", "large_mxfp8", "train", "prefill_rankzipf"])
+def test_route_and_dispatch_bit_exact(name):
+    B = _B()
+    cfg = wl.config(name)
+    _say("route/dispatch", name)
+    logits = wl.make_logits(cfg)
+    idx, w = B.route(torch.from_numpy(logits).cuda(), cfg.k)
+    ridx, rw = orc.route(logits, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    wg = w.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(wg - rw) <= 1e-6 + 1e-5 * np.abs(rw))
+    got = B.dispatch(idx, cfg.E)
+    ref = orc.dispatch(ridx, cfg.E)
+    for g, r, n in zip(got, ref, ("offsets", "row_token", "row_slot", "slot_row")):
+        assert np.array_equal(g.cpu().numpy(), r), n
+
+
+def test_route_ties_and_signed_zeros():
+    B = _B()
+    _say("route ties")
+    T, E, k = 64, 96, 7
+    rng = np.random.default_rng(1)
+    logits = rng.integers(-2, 3, (T, E)).astype(np.float32)   # many exact ties
+    logits[0] = 0.0
+    logits[1] = -0.0
+    logits[2, ::2] = -0.0
+    logits[3] = np.float32(-3.5)
+    idx, w = B.route(torch.from_numpy(logits).cuda(), k)
+    ridx, rw = orc.route(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.all(np.abs(w.cpu().numpy() - rw) <= 1e-6 + 1e-5 * rw)
+    assert np.all(w.cpu().numpy()[0] == np.float32(1.0 / k))
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (1, 8, 8), (5, 3, 3), (3000, 7, 2), (9000, 1024, 32),
+                                   (4097, 64, 1), (0, 16, 4)])
+def test_dispatch_edge_cases(T, E, k):
+    B = _B()
+    _say("dispatch", T, E, k)
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.standard_normal((max(T, 1), E)).astype(np.float32)[:T]
+    ridx, _ = orc.route(logits, k) if T else (np.zeros((0, k), np.int32), None)
+    idx = torch.from_numpy(np.ascontiguousarray(ridx)).cuda()
+    got = B.dispatch(idx, E)
+    ref = orc.dispatch(ridx, E)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g.cpu().numpy(), r)
+
+
+# ------------------------------------------------------------------------------------------
+# packing and MXFP8 quantisation: bit-exact
+# ------------------------------------------------------------------------------------------
+def test_pack_weights_is_transpose():
+    B = _B()
+    _say("pack")
+    rng = np.random.default_rng(2)
+    W = wl.f32_to_bf16_bits(rng.standard_normal((3, 192, 320)).astype(np.float32))
+    Wt = B.pack_weights(to_dev(W))
+    assert np.array_equal(to_bits(Wt), np.ascontiguousarray(W.transpose(0, 2, 1)))
+
+
+def test_mx_quantize_bit_exact():
+    B = _B()
+    _say("mx quantize")
+    rng = np.random.default_rng(3)
+    x = wl.f32_to_bf16_bits((rng.standard_normal((257, 512)) * 10.0 ** rng.integers(-8, 8, (257, 1))).astype(np.float32))
+    x[5, 64:96] = 0                                    # all-zero block
+    x[6, :32] = 0x8000                                 # all -0.0
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    allbits = allbits[np.isfinite(orc.bf16_decode(allbits))]
+    allbits = allbits[: allbits.size // 32 * 32].reshape(-1, 32)
+    for arr in (x, allbits, np.ascontiguousarray(allbits[:, ::-1])):
+        q, s = B.mx_quantize(to_dev(arr))
+        rq, rs = orc.mx_quantize(orc.bf16_decode(arr))
+        assert np.array_equal(s.cpu().numpy(), rs)
+        assert np.array_equal(q.cpu().numpy(), rq)
+
+
+# ------------------------------------------------------------------------------------------
+# forward
+# ------------------------------------------------------------------------------------------
+def _run_forward(cfg, Wg, Wu, Wd, logits, X):
+    from grouped_gemm_router_amd.layer import MoELayer
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(Wg, Wu, Wd)
+    Y = layer.forward(torch.from_numpy(logits).cuda(), to_dev(X))
+    torch.cuda.synchronize()
+    return layer, layer.plan(cfg.T)
+
+
+def _oracle_forward(cfg, logits, X, wfn):
+    idx, w = orc.route(logits, cfg.k)
+    off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
+    h, O = orc.expert_mlp(X, row_token, off, wfn("gate"), wfn("up"), wfn("down"), mxfp8=cfg.dtype == "mxfp8")
+    return idx, w, off, h, O, orc.combine(O, slot_row, w)
+
+
+SMALL = [
+    wl.config("tiny"),
+    wl.config("tiny", name="ragged", T=300, H=320, I=192, E=5, k=3, seed=11),
+    wl.config("tiny", name="one_expert", T=77, E=1, k=1, seed=12),
+    wl.config("tiny", name="k_eq_E", T=40, E=6, k=6, seed=13),
+    wl.config("tiny", name="many_empty", T=9, E=200, k=2, seed=14),
+    wl.config("tiny", name="I64", T=600, H=128, I=64, E=4, k=2, seed=15),
+    wl.config("tiny", name="mx_small", T=96, H=256, I=128, E=6, k=2, dtype="mxfp8", seed=16),
+    wl.config("tiny", name="mx_ragged", T=333, H=384, I=256, E=5, k=3, dtype="mxfp8", seed=17),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_forward_small_vs_oracle(cfg):
+    _say("forward", cfg)
+    logits, X = wl.make_logits(cfg), wl.make_x(cfg)
+    Wg, Wu, Wd = (device_weights(cfg, n) for n in ("gate", "up", "down"))
+    layer, pl = _run_forward(cfg, Wg, Wu, Wd, logits, X)
+    idx, w, off, h, O, Y = _oracle_forward(cfg, logits, X, lambda n: host_weight_fn(cfg, n))
+    assert np.array_equal(pl["topk_idx"].cpu().numpy(), idx)
+    assert np.array_equal(pl["offsets"].cpu().numpy(), off)
+    check_close(to_f64(pl["H_rows"]), h, "h")
+    check_close(to_f64(pl["O_rows"]), O, "O")
+    check_close(to_f64(pl["Y"]), Y, "Y")
+
+
+def test_forward_deterministic_and_unused_experts_unread():
+    _say("determinism + NaN poisoning")
+    cfg = wl.config("tiny", name="poison", T=200, H=256, I=128, E=64, k=2, seed=21)
+    logits, X = wl.make_logits(cfg), wl.make_x(cfg)
+    idx, _ = orc.route(logits, cfg.k)
+    active = np.unique(idx)
+    assert len(active) < cfg.E
+    W_full = [device_weights(cfg, n) for n in ("gate", "up", "down")]
+    W_pois = [device_weights(cfg, n, experts=active) for n in ("gate", "up", "down")]
+    _, p1 = _run_forward(cfg, *W_full, logits, X)
+    y1 = to_bits(p1["Y"]).copy()
+    _, p2 = _run_forward(cfg, *W_full, logits, X)
+    assert np.array_equal(to_bits(p2["Y"]), y1)
+    _, p3 = _run_forward(cfg, *W_pois, logits, X)
+    assert np.array_equal(to_bits(p3["Y"]), y1)
+    assert np.isfinite(to_f64(p3["Y"])).all()
+
+
+# ------------------------------------------------------------------------------------------
+# backward
+# ------------------------------------------------------------------------------------------
+BWD = [
+    wl.config("tiny", backward=True),
+    wl.config("tiny", name="bwd_ragged", T=300, H=320, I=192, E=5, k=3, seed=31, backward=True),
+    wl.config("tiny", name="bwd_empty", T=6, H=128, I=64, E=40, k=2, seed=32, backward=True),
+    wl.config("tiny", name="bwd_long", T=700, H=256, I=128, E=2, k=1, seed=33, backward=True),
+]
+
+
+@pytest.mark.parametrize("cfg", BWD, ids=[c.name for c in BWD])
+def test_backward_small_vs_oracle(cfg):
+    _say("backward", cfg)
+    from grouped_gemm_router_amd.layer import MoELayer
+    logits, X, dY = wl.make_logits(cfg), wl.make_x(cfg), wl.make_dy(cfg)
+    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k).load_weights(W["gate"], W["up"], W["down"])
+    layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=True)
+    dX, dWg, dWu, dWd, dtw = layer.backward(to_dev(X), to_dev(dY))
+    torch.cuda.synchronize()
+    idx, w = orc.route(logits, cfg.k)
+    fn = lambda n: host_weight_fn(cfg, n)
+    ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), E=cfg.E)
+    check_close(to_f64(dX), ref["dX"], "dX")
+    check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w")
+    g = {"dWg": to_f64(dWg), "dWu": to_f64(dWu), "dWd": to_f64(dWd)}
+    for key in ("dWg", "dWu", "dWd"):
+        for e in range(cfg.E):
+            check_close(g[key][e], ref["dW"][key][e], f"{key}[{e}]")
+    # a second backward gives the same bits (fixed reduction order, no atomics)
+    first = [to_bits(t).copy() for t in (dX, dWg, dWu, dWd)] + [dtw.cpu().numpy().copy()]
+    layer.backward(to_dev(X), to_dev(dY))
+    torch.cuda.synchronize()
+    again = [to_bits(t) for t in (dX, dWg, dWu, dWd)] + [dtw.cpu().numpy()]
+    for a, b in zip(first, again):
+        assert np.array_equal(a, b)
