@@ -49,7 +49,7 @@ size_t mlp_ws(const moe_problem* p) {
 size_t bwd_ws(const moe_problem* p) {
   const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
   const size_t nparts = moe::bwd_nparts(p->I);
-  return align_up(A * I * 4) + align_up(A * 2 * I * 2) + align_up(A * I * 2) + align_up(A * H * 4) +
+  return align_up(A * I * 4) + 2 * align_up(A * 2 * I * 2) + align_up(A * I * 2) + align_up(A * H * 4) +
          align_up(A * nparts * 4);
 }
 
@@ -263,6 +263,8 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   a.P = (float*)w8;
   w8 += align_up(A * I * 4);
   a.dGU = (uint16_t*)w8;
+  w8 += align_up(A * 2 * I * 2);
+  a.dGU_lo = (uint16_t*)w8;
   w8 += align_up(A * 2 * I * 2);
   a.Hrows = (uint16_t*)w8;
   w8 += align_up(A * I * 2);

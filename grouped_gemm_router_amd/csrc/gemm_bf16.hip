@@ -91,29 +91,30 @@ struct SrcGateUpWT {
 // Row sources of the weight-gradient GEMMs (rows are the contraction index).
 struct MNSrcH {
   static constexpr bool SCALED = false;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r) {
+  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int) {
     return p.Hrows + (size_t)r * p.I;
   }
   __device__ static float scale(const GemmArgs&, int) { return 1.f; }
 };
 struct MNSrcDO {  // dO = bf16(w * dY[token])
   static constexpr bool SCALED = true;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r) {
+  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int) {
     return p.dY + (size_t)p.row_token[r] * p.H;
   }
   __device__ static float scale(const GemmArgs& p, int r) { return p.topk_w[p.row_slot[r]]; }
 };
 struct MNSrcX {
   static constexpr bool SCALED = false;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r) {
+  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int) {
     return p.X + (size_t)p.row_token[r] * p.H;
   }
   __device__ static float scale(const GemmArgs&, int) { return 1.f; }
 };
+// [dg | du] rows: the bf16 values in the first pass, their bf16 remainders in the second.
 struct MNSrcDGU {
   static constexpr bool SCALED = false;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r) {
-    return p.dGU + (size_t)r * 2 * p.I;
+  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int phase) {
+    return (phase ? p.dGU_lo : p.dGU) + (size_t)r * 2 * p.I;
   }
   __device__ static float scale(const GemmArgs&, int) { return 1.f; }
 };
@@ -123,6 +124,7 @@ struct MNSrcDGU {
 // ------------------------------------------------------------------------
 template <class C, class SrcA, class SrcB>
 struct RowOpsBase {
+  static constexpr int PHASES = 1;
   using Sched = RowGroups<C::BM, C::BN, C::NT>;
   using ALoad = KRows<C::BM, C::NT, SrcA, GemmArgs>;
   using BLoad = KRows<C::BN, C::NT, SrcB, GemmArgs>;
@@ -214,6 +216,17 @@ struct BwdPOps : RowOpsBase<C, SrcDYRows, SrcDownWT> {
   }
 };
 
+// v = hi + lo with hi = bf16(v), lo = bf16(v - hi): stores both (4 values).
+__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const float (&v)[4]) {
+  uint2 h, l;
+  h.x = pack_bf16x2(v[0], v[1]);
+  h.y = pack_bf16x2(v[2], v[3]);
+  l.x = pack_bf16x2(v[0] - bf16_to_f32(h.x & 0xffffu), v[1] - bf16_to_f32(h.x >> 16));
+  l.y = pack_bf16x2(v[2] - bf16_to_f32(h.y & 0xffffu), v[3] - bf16_to_f32(h.y >> 16));
+  *reinterpret_cast<uint2*>(hi) = h;
+  *reinterpret_cast<uint2*>(lo) = l;
+}
+
 // Recompute G, U; with P give h, the router-weight partial sums <h, P>, dg and du.
 template <class C>
 struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
@@ -234,6 +247,7 @@ struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
         const float* Prow = p.P + (size_t)r * p.I + hcol0;
         uint16_t* hrow = p.Hrows + (size_t)r * p.I + hcol0;
         uint16_t* grow = p.dGU + (size_t)r * 2 * p.I + hcol0;
+        uint16_t* lrow = p.dGU_lo + (size_t)r * 2 * p.I + hcol0;
 #pragma unroll
         for (int fn = 0; fn < C::FN / 2; ++fn)
 #pragma unroll
@@ -254,8 +268,8 @@ struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
               dg[j] = dh * u * (sg * (1.f + g * (1.f - sg)));
             }
             store_bf16x4(hrow + o, hv[0], hv[1], hv[2], hv[3]);
-            store_bf16x4(grow + o, dg[0], dg[1], dg[2], dg[3]);
-            store_bf16x4(grow + p.I + o, du[0], du[1], du[2], du[3]);
+            store_split4(grow + o, lrow + o, dg);
+            store_split4(grow + p.I + o, lrow + p.I + o, du);
           }
       }
       // the other half of this row's columns sits in lane ^ 32
@@ -280,6 +294,7 @@ struct BwdDXOps : RowOpsBase<C, SrcDGURows, SrcGateUpWT> {
 
 template <class C, class SrcA, class SrcB>
 struct WgOpsBase {
+  static constexpr int PHASES = 1;
   using Sched = WeightGrad<C::BM, C::BN, C::NT>;
   using ALoad = MNRows<C::BM, C::NT, SrcA, GemmArgs>;
   using BLoad = MNRows<C::BN, C::NT, SrcB, GemmArgs>;
@@ -330,6 +345,8 @@ struct BwdDWDownOps : WgOpsBase<C, MNSrcH, MNSrcDO> {
 template <class C>
 struct BwdDWGateUpOps : WgOpsBase<C, MNSrcX, MNSrcDGU> {
   using B = WgOpsBase<C, MNSrcX, MNSrcDGU>;
+  // dg and du enter as bf16 value + bf16 remainder: two passes over the rows
+  static constexpr int PHASES = 2;
   __device__ static void init_sched(typename B::Sched& s, const GemmArgs& p, int*, int*) {
     s.init(p.offsets, p.E, p.H, 2 * p.I);
   }

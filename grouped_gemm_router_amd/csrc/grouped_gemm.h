@@ -217,7 +217,7 @@ struct KRows {
       }
     }
   }
-  __device__ void load(int k0) {
+  __device__ void load(int k0, int /*phase*/) {
     const long off = (k0 < ksplit) ? (long)k0 : delta + (k0 - ksplit);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
@@ -235,9 +235,9 @@ struct KRows {
 // ---------------------------------------------------------------------------
 // Loaders: rows are the contraction index (weight-gradient operands)
 // ---------------------------------------------------------------------------
-// Src must provide: __device__ const uint16_t* row(const P&, const Tile&, int r) for an absolute
-// expert-major row r in [k_lo, k_hi), pointing at element 0 of the MN axis; float scale(const P&,
-// int r) and static constexpr bool SCALED.
+// Src must provide: __device__ const uint16_t* row(const P&, const Tile&, int r, int phase) for an
+// absolute expert-major row r in [k_lo, k_hi), pointing at element 0 of the MN axis (phase: which
+// pass over the rows, see Ops::PHASES); float scale(const P&, int r) and static constexpr bool SCALED.
 template <int COLS, int NT, class Src, class P>
 struct MNRows {
   static constexpr int BLOCKS = COLS;            // 8 (k) x COLS/8 (mn) blocks of 8x8
@@ -260,7 +260,7 @@ struct MNRows {
       mn_off[i] = mn0 + mb * 8;
     }
   }
-  __device__ void load(int k0) {
+  __device__ void load(int k0, int phase) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       int b = threadIdx.x + i * NT;
@@ -270,7 +270,7 @@ struct MNRows {
         int r = tl.k_lo + k0 + kb * 8 + j;
         bool ok = (b < BLOCKS) && (r < tl.k_hi) && (mn_off[i] < mn_lim);
         if (ok) {
-          reg[i][j] = *reinterpret_cast<const uint4*>(Src::row(*pp, tl, r) + mn_off[i]);
+          reg[i][j] = *reinterpret_cast<const uint4*>(Src::row(*pp, tl, r, phase) + mn_off[i]);
           if constexpr (Src::SCALED) scl[i][j] = Src::scale(*pp, r);
         } else {
           reg[i][j] = make_uint4(0, 0, 0, 0);
@@ -387,7 +387,10 @@ __device__ __forceinline__ void grouped_gemm_body(const P& p) {
     typename Ops::ALoad al;
     typename Ops::BLoad bl;
     Ops::init_loaders(al, bl, p, tl);
-    const int nk = (tl.k_hi - tl.k_lo + BK - 1) / BK;
+    // Ops::PHASES passes over the contraction range (the second pass of a
+    // two-phase GEMM adds the low-order bf16 part of one operand)
+    const int nk1 = (tl.k_hi - tl.k_lo + BK - 1) / BK;
+    const int nk = nk1 * Ops::PHASES;
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -400,16 +403,18 @@ __device__ __forceinline__ void grouped_gemm_body(const P& p) {
     if (nk > 0) {
       uint4* const As = smem;                       // stage s at As + s * LDS_A
       uint4* const Bs = smem + 2 * C::LDS_A;        // stage s at Bs + s * LDS_B
-      al.load(0);
-      bl.load(0);
+      al.load(0, 0);
+      bl.load(0, 0);
       al.store(As);
       bl.store(Bs);
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < nk) {
-          al.load((kt + 1) * BK);
-          bl.load((kt + 1) * BK);
+          const int ph = (kt + 1) / nk1;
+          const int k0 = (kt + 1 - ph * nk1) * BK;
+          al.load(k0, ph);
+          bl.load(k0, ph);
         }
         mma_ktile<C>(As + cur * C::LDS_A, Bs + cur * C::LDS_B, acc, wm, wn, lane);
         if (kt + 1 < nk) {

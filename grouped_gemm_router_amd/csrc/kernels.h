@@ -25,7 +25,8 @@ struct GemmArgs {
   uint16_t* Hrows;        // [A, I]
   uint16_t* Orows;        // [A, H]
   float* P;               // [A, I]
-  uint16_t* dGU;          // [A, 2I]
+  uint16_t* dGU;          // [A, 2I]  bf16(dg) | bf16(du)
+  uint16_t* dGU_lo;       // [A, 2I]  bf16 of the remainders (dg - bf16(dg), du - bf16(du))
   float* dXr;             // [A, H]
   float* dwt_part;        // [A, nparts]
   int nparts;

@@ -188,7 +188,7 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
  * Per row r (token t, slot s, expert e, weight w = topk_w[s]):
  *   G, U, h recomputed as in moe_expert_mlp;  P = dY[t] W_down[e]^T (fp32)
  *   d_topk_w[s] = <h, P>;  dh = w P
- *   du = bf16(dh * silu(G)),  dg = bf16(dh * U * silu'(G)),  dO = bf16(w dY[t])
+ *   du = dh * silu(G),  dg = dh * U * silu'(G),  dO = bf16(w dY[t])
  *   dX[t]      = bf16( sum_j (dg W_gate[e]^T + du W_up[e]^T) ), j ascending
  *   dW_gate[e] = bf16( sum_r X[t]^T dg ),  dW_up[e] = bf16( sum_r X[t]^T du )
  *   dW_down[e] = bf16( sum_r h^T dO )      (all sums in fp32, fixed order;

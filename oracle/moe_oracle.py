@@ -47,11 +47,11 @@ design notes of the repository):
 * Combine adds the k weighted expert rows of a token in slot order
   (descending logit), in high precision, then rounds once.
 * Backward: bf16 roundings are straight-through (identity) in the
-  derivative.  The materialised gradients dg, du (of the gate and up
-  pre-activations) and dO = w * dY (of the expert output rows) are rounded to
-  bf16, like h in the forward; dX and dW_* are rounded once after exact
-  accumulation; the router-weight gradient is <h_r, dY_t W_down^T> in fp32
-  range (no rounding).
+  derivative.  The gradient of the expert output rows dO = w * dY is rounded
+  to bf16 (it feeds a bf16 weight-gradient GEMM); the gradients dg, du of the
+  gate and up pre-activations are kept exact; dX and dW_* are rounded once
+  after exact accumulation; the router-weight gradient is <h_r, dY_t W_down^T>
+  (no rounding).
 """
 from __future__ import annotations
 
@@ -366,8 +366,8 @@ def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = Fals
 
     x_rows, dy_rows: [n, H] token inputs and output gradients of the rows;
     w_rows: [n] routing weights.  G, U, h are recomputed as in the forward.
-    P = dY W_down^T; dwt = <h, P>; dh = w P; du = bf16(dh * silu(G));
-    dg = bf16(dh * U * silu'(G)); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
+    P = dY W_down^T; dwt = <h, P>; dh = w P; du = dh * silu(G);
+    dg = dh * U * silu'(G); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
     dWg = x^T dg, dWu = x^T du, dWd = h^T dO (not yet rounded).
     Returns dict of float64 arrays.
     """
@@ -380,8 +380,8 @@ def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = Fals
     P = dy_rows @ wd.T
     dwt = np.sum(h * P, axis=1)
     dh = w_rows[:, None] * P
-    du = rnd(dh * silu(G))
-    dg = rnd(dh * U * dsilu(G))
+    du = dh * silu(G)
+    dg = dh * U * dsilu(G)
     dO = rnd(w_rows[:, None] * dy_rows)
     dXr = dg @ wg.T + du @ wu.T
     return {"dwt": dwt, "dXr": dXr, "dWg": x_rows.T @ dg, "dWu": x_rows.T @ du,

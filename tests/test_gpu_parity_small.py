@@ -166,7 +166,7 @@ def test_forward_small_vs_oracle(cfg):
 
 def test_forward_deterministic_and_unused_experts_unread():
     _say("determinism + NaN poisoning")
-    cfg = wl.config("tiny", name="poison", T=200, H=256, I=128, E=64, k=2, seed=21)
+    cfg = wl.config("tiny", name="poison", T=48, H=256, I=128, E=256, k=2, seed=21)
     logits, X = wl.make_logits(cfg), wl.make_x(cfg)
     idx, _ = orc.route(logits, cfg.k)
     active = np.unique(idx)
