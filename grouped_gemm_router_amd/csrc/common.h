@@ -26,6 +26,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // fp32 -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
+// Four fp32 values -> four bf16 at dst (8-byte aligned).
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_bf16x2(a, b);
+  v.y = pack_bf16x2(c, d);
+  *reinterpret_cast<uint2*>(dst) = v;
+}
+
 // sigmoid / silu in fp32 with the hardware exp2 and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
@@ -38,7 +46,11 @@ __device__ __forceinline__ int lds_chunk(int row, int chunk) {
   return row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7));
 }
 
-template <typename T>
-__device__ __forceinline__ T ldg_nt(const T* p) { return __builtin_nontemporal_load(p); }
+// 16-byte streaming load (nontemporal: data read once, keep it out of the way in the caches).
+__device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 }  // namespace moe

@@ -360,13 +360,6 @@ struct Frag {
   }
 };
 
-__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
-  uint2 v;
-  v.x = pack_bf16x2(a, b);
-  v.y = pack_bf16x2(c, d);
-  *reinterpret_cast<uint2*>(dst) = v;
-}
-
 // ---------------------------------------------------------------------------
 // The kernel body shared by every variant.  Sched is RowGroups or WeightGrad;
 // Ops supplies the loaders and the epilogue for one GEMM of the layer.

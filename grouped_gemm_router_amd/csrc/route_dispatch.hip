@@ -85,7 +85,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 // mask of lanes holding the same expert, so its rank among equal experts in
 // slot order is a popcount, and one lane per expert updates the running count.
 // No atomics anywhere: the positions are the same on every run.
-//   k_dispatch_count:   per-wave histograms  -> ws[(chunk*4 + wave) * E + e]
+//   k_dispatch_count:   per-wave histograms  -> ws[e * nsub + chunk*4 + wave]
 //   k_dispatch_scatter: offsets (scan of the totals), per-wave bases, then the
 //                       stable scatter of (row_token, row_slot, slot_row).
 // ---------------------------------------------------------------------------
@@ -111,7 +111,7 @@ __device__ __forceinline__ uint64_t match_key(int key) {
 }
 
 __global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restrict__ idx, long A, int E,
-                                                        int32_t* __restrict__ counts) {
+                                                        int nsub, int32_t* __restrict__ counts) {
   __shared__ int hist[4][DISPATCH_MAX_E];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < 4 * DISPATCH_MAX_E; e += 256) (&hist[0][0])[e] = 0;
@@ -129,7 +129,8 @@ __global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restric
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256)
-    for (int w = 0; w < 4; ++w) counts[((long)blockIdx.x * 4 + w) * E + e] = hist[w][e];
+    *reinterpret_cast<int4*>(counts + (long)e * nsub + blockIdx.x * 4) =
+        make_int4(hist[0][e], hist[1][e], hist[2][e], hist[3][e]);
 }
 
 __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restrict__ idx, long A, int E, int k,
@@ -141,36 +142,42 @@ __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restr
   __shared__ int base[4][DISPATCH_MAX_E];
   __shared__ int red[8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int my_sub0 = blockIdx.x * 4;
-  // per-expert totals and the prefix over earlier sub-chunks (4 experts per thread)
+  // per-expert totals and the prefix over earlier sub-chunks (4 experts per thread);
+  // counts are expert-major, so each expert's sub-chunk counts are read as int4
   int tot[4], pre[4][4];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int e = threadIdx.x * 4 + i;
-    tot[i] = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) pre[i][w] = 0;
+    const int e = threadIdx.x * 4 + i;
+    int before = 0, all = 0;
+    int4 mine = make_int4(0, 0, 0, 0);
     if (e < E) {
-      for (int sc = 0; sc < nsub; ++sc) {
-        int c = counts[(long)sc * E + e];
-        if (sc < my_sub0) {
-          pre[i][0] += c;
-        } else if (sc < my_sub0 + 4) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            if (sc - my_sub0 < w) pre[i][w] += c;
-        }
-        tot[i] += c;
+      const int4* c4 = reinterpret_cast<const int4*>(counts + (long)e * nsub);
+      const int nq = nsub / 4;
+      const int me = (int)blockIdx.x;
+      int q = 0;
+      for (; q + 4 <= nq; q += 4) {
+        int4 v0 = c4[q], v1 = c4[q + 1], v2 = c4[q + 2], v3 = c4[q + 3];
+        int s0 = v0.x + v0.y + v0.z + v0.w, s1 = v1.x + v1.y + v1.z + v1.w;
+        int s2 = v2.x + v2.y + v2.z + v2.w, s3 = v3.x + v3.y + v3.z + v3.w;
+        all += s0 + s1 + s2 + s3;
+        before += (q < me ? s0 : 0) + (q + 1 < me ? s1 : 0) + (q + 2 < me ? s2 : 0) + (q + 3 < me ? s3 : 0);
       }
+      for (; q < nq; ++q) {
+        int4 v = c4[q];
+        int sq = v.x + v.y + v.z + v.w;
+        all += sq;
+        if (q < me) before += sq;
+      }
+      mine = c4[me];
     }
-    sum += tot[i];
+    tot[i] = all;
+    pre[i][0] = before;
+    pre[i][1] = before + mine.x;
+    pre[i][2] = before + mine.x + mine.y;
+    pre[i][3] = before + mine.x + mine.y + mine.z;
+    sum += all;
   }
-  // pre[i][w] for w > 0 must also include the earlier sub-chunks
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int w = 1; w < 4; ++w) pre[i][w] += pre[i][0];
   // exclusive scan of the totals over experts
   int x = sum;
 #pragma unroll
@@ -222,7 +229,7 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* off
   long A = (long)T * k;
   int nchunks = (int)((A + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK);
   if (nchunks < 1) nchunks = 1;  // block 0 still writes the offsets when there are no slots
-  hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, A, E, ws);
+  hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, A, E, nchunks * 4, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), 0, s, idx, A, E, k, ws, nchunks * 4,

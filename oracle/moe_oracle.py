@@ -457,3 +457,34 @@ def backward_tokens(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, tokens, exact
             dwt[n, j] = r["dwt"][0]
         dX[n] = acc
     return rnd(dX), dwt
+
+
+def mx_requant_delta(h_exact, rel_eps: float = 2.0 ** -14):
+    """Rounding decisions of the MXFP8 requantisation of h that another correct
+    implementation may take the other way.
+
+    h is rounded to bf16 and then quantised to MXFP8 (both decisions on a value
+    that an fp32 implementation only knows to within a few fp32 ulps).  This
+    perturbs the exact h of every element by +-rel_eps * (|h| + max|h| of its
+    block / 64) -- far more than fp32 accumulation error -- and returns, per
+    element, the largest change of its MXFP8 value, plus the nominal MXFP8 h.
+    A decision within that distance of a boundary (an element code or, through
+    the block maximum, the block's E8M0 scale) can go either way; elsewhere the
+    change is exactly 0.
+    """
+    h = np.asarray(h_exact, dtype=np.float64)
+    K = h.shape[-1]
+    blk = np.abs(h).reshape(h.shape[:-1] + (K // 32, 32)).max(axis=-1)
+    slack = rel_eps * (np.abs(h) + np.repeat(blk, 32, axis=-1) / 64.0)
+    base = mx_fake_quant(bf16_round(h))
+    up = mx_fake_quant(bf16_round(h + slack))
+    dn = mx_fake_quant(bf16_round(h - slack))
+    return base, np.maximum(np.abs(up - base), np.abs(dn - base))
+
+
+def mx_down_ambiguity(G, U, wd):
+    """For O = MXFP8(h) W_down with h = bf16(silu(G) U): per element of O, the
+    largest change another valid rounding of the requantised h can cause
+    (|delta| @ |W_down as MXFP8|, delta from ``mx_requant_delta``)."""
+    _, delta = mx_requant_delta(silu(G) * np.asarray(U, dtype=np.float64))
+    return delta @ np.abs(mx_fake_quant(np.asarray(wd, dtype=np.float64).T).T)

@@ -134,8 +134,22 @@ def _run_forward(cfg, Wg, Wu, Wd, logits, X):
 def _oracle_forward(cfg, logits, X, wfn):
     idx, w = orc.route(logits, cfg.k)
     off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
-    h, O = orc.expert_mlp(X, row_token, off, wfn("gate"), wfn("up"), wfn("down"), mxfp8=cfg.dtype == "mxfp8")
-    return idx, w, off, h, O, orc.combine(O, slot_row, w)
+    mx = cfg.dtype == "mxfp8"
+    h, O = orc.expert_mlp(X, row_token, off, wfn("gate"), wfn("up"), wfn("down"), mxfp8=mx)
+    amb_O = amb_Y = None
+    if mx:
+        # valid alternative roundings of the requantised h (see mx_down_ambiguity)
+        Xv = orc.bf16_decode(X)
+        amb_O = np.zeros_like(O)
+        for e in range(cfg.E):
+            lo, hi = off[e], off[e + 1]
+            if hi > lo:
+                G, U, _, _ = orc.expert_forward_rows(Xv[row_token[lo:hi]], orc.bf16_decode(wfn("gate")(e)),
+                                                     orc.bf16_decode(wfn("up")(e)), orc.bf16_decode(wfn("down")(e)),
+                                                     mxfp8=True)
+                amb_O[lo:hi] = orc.mx_down_ambiguity(G, U, orc.bf16_decode(wfn("down")(e)))
+        amb_Y = sum(w[:, j:j + 1] * amb_O[slot_row.reshape(-1, cfg.k)[:, j]] for j in range(cfg.k))
+    return idx, w, off, h, O, orc.combine(O, slot_row, w), amb_O, amb_Y
 
 
 SMALL = [
@@ -156,12 +170,12 @@ def test_forward_small_vs_oracle(cfg):
     logits, X = wl.make_logits(cfg), wl.make_x(cfg)
     Wg, Wu, Wd = (device_weights(cfg, n) for n in ("gate", "up", "down"))
     layer, pl = _run_forward(cfg, Wg, Wu, Wd, logits, X)
-    idx, w, off, h, O, Y = _oracle_forward(cfg, logits, X, lambda n: host_weight_fn(cfg, n))
+    idx, w, off, h, O, Y, amb_O, amb_Y = _oracle_forward(cfg, logits, X, lambda n: host_weight_fn(cfg, n))
     assert np.array_equal(pl["topk_idx"].cpu().numpy(), idx)
     assert np.array_equal(pl["offsets"].cpu().numpy(), off)
     check_close(to_f64(pl["H_rows"]), h, "h")
-    check_close(to_f64(pl["O_rows"]), O, "O")
-    check_close(to_f64(pl["Y"]), Y, "Y")
+    check_close(to_f64(pl["O_rows"]), O, "O", ambiguity=amb_O)
+    check_close(to_f64(pl["Y"]), Y, "Y", ambiguity=amb_Y)
 
 
 def test_forward_deterministic_and_unused_experts_unread():

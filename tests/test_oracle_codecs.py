@@ -121,3 +121,26 @@ def test_mx_quantize_lossless_for_representable_blocks():
     codes, scales = orc.mx_quantize(v)
     assert (scales == 130).all()
     assert np.array_equal(orc.mx_dequantize(codes, scales), v)
+
+
+def test_mx_requant_delta_marks_only_ambiguous_decisions():
+    rng = np.random.default_rng(8)
+    # values sitting exactly between two E4M3 codes (after bf16 rounding) at scale 2^0
+    c = np.array([0x40, 0x42, 0x50, 0x60], np.uint8)   # even mantissas: the tie rounds down to c
+    lo, hi = orc.e4m3_decode(c), orc.e4m3_decode(c + 1)
+    row = np.full(32, 1.0)
+    row[0] = 256.0                                   # amax 256: shared exponent 0
+    mid = (lo + hi) / 2                              # an E4M3 tie, itself a bf16 value
+    ulp = 2.0 ** (np.floor(np.log2(mid)) - 7)
+    row[1:5] = mid + ulp / 2                         # bf16 rounds it to mid (tie -> even code) or above
+    row[5:9] = lo * (1 + 2.0 ** -12) + 0.0           # clearly inside a code interval
+    base, delta = orc.mx_requant_delta(row[None])
+    assert np.array_equal(base[0], orc.mx_fake_quant(orc.bf16_round(row))[None][0])
+    assert np.all(delta[0, 1:5] > 0)                 # a tie can round either way
+    assert np.all(delta[0, 5:9] == 0) and delta[0, 0] == 0
+    # random data: most decisions are unambiguous, and every delta is one code step or a scale step
+    v = rng.standard_normal((64, 256))
+    base, delta = orc.mx_requant_delta(v)
+    assert np.mean(delta > 0) < 0.01
+    nz = delta > 0
+    assert np.all(delta[nz] <= np.abs(base[nz]) * 0.25 + 2.0 ** -9 * 4)
