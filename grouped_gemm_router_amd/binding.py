@@ -13,7 +13,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+LIB_PATH = os.environ.get("MOE_LIBRARY", os.path.join(_PKG, "libmoe.so"))
 
 MOE_OK = 0
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE", 3: "MOE_ERR_WORKSPACE",

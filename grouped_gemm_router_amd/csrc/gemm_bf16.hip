@@ -1,93 +1,96 @@
 // bf16 grouped GEMMs of the MoE layer: forward gate/up + SwiGLU, forward down,
 // and the five GEMMs of the backward.  See grouped_gemm.h for the template.
+#include "gemm_rows.h"
 #include "grouped_gemm.h"
 #include "kernels.h"
 
 namespace moe {
 
-using CfgMain = TileCfg<256, 256, 2, 2>;
+using CfgMain = TileCfg<256, 256, 2, 2>;          // weight-gradient GEMMs (register-transposed loads)
+#ifndef MOE_ROWS_WAVES_N
+#define MOE_ROWS_WAVES_N 4
+#endif
+#ifndef MOE_ROWS_BK
+#define MOE_ROWS_BK 64
+#endif
+// row-grouped GEMMs: 256 x 256 tiles, direct-to-LDS loads, 128 KB of LDS stages
+using CfgRows = RowCfg<256, 256, 2, MOE_ROWS_WAVES_N, MOE_ROWS_BK, (MOE_ROWS_BK == 32 ? 4 : 2)>;
+
+// ------------------------------------------------------------------------
+// Row sources of the direct-to-LDS row-grouped GEMMs: a wave-uniform base and
+// a 32-bit element offset per row; rows past the expert's segment (columns past
+// N) are clamped to a valid one and their results are never stored.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ int clamp_row(const Tile& t, int row) { return min(t.m0 + row, t.m_end - 1); }
+
+struct RSrcX {
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile&, int, int k0) { return p.X + k0; }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)p.row_token[clamp_row(t, row)] * (uint32_t)p.H;
+  }
+};
+struct RSrcDY {
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile&, int, int k0) { return p.dY + k0; }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)p.row_token[clamp_row(t, row)] * (uint32_t)p.H;
+  }
+};
+struct RSrcH {
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile&, int, int k0) { return p.Hrows + k0; }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)clamp_row(t, row) * (uint32_t)p.I;
+  }
+};
+struct RSrcDGU {
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile&, int, int k0) { return p.dGU + k0; }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)clamp_row(t, row) * (uint32_t)(2 * p.I);
+  }
+};
+// Packed gate / up weights [E, I, H].  Inside every 32-row MFMA fragment of the
+// B tile, rows 0-15 are gate columns and rows 16-31 the up columns of the same
+// 16 intermediate indices, so an accumulator lane holds each (gate, up) pair
+// at items v and v + 8 of one fragment.
+template <class C>
+struct RSrcGateUpW {
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int row0, int k0) {
+    const bool up = (row0 % 32) >= 16;
+    return (up ? p.Wu_t : p.Wg_t) + (size_t)t.e * p.I * p.H + k0;
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    const int col = t.nt * (C::BN / 2) + (row / 32) * 16 + (row % 16);
+    return (uint32_t)min(col, p.I - 1) * (uint32_t)p.H;
+  }
+};
+struct RSrcDownW {       // packed [E, H, I]
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
+    return p.Wd_t + (size_t)t.e * p.H * p.I + k0;
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
+  }
+};
+struct RSrcDownWT {      // W_down [E, I, H] read as [E, N = I, K = H]
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
+    return p.Wd + (size_t)t.e * p.I * p.H + k0;
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.I - 1) * (uint32_t)p.H;
+  }
+};
+struct RSrcGateUpWT {    // [W_gate | W_up] [E, H, I] read as [E, N = H, K = 2I]
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
+    const size_t e0 = (size_t)t.e * p.H * p.I;
+    return k0 < p.I ? p.Wg + e0 + k0 : p.Wu + e0 + (k0 - p.I);
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
+  }
+};
 
 // ------------------------------------------------------------------------
 // Operand sources
 // ------------------------------------------------------------------------
-// Token rows X[row_token[r]] (contraction axis H) for the rows of a tile.
-struct SrcXRows {
-  __device__ static int ksplit(const GemmArgs& p) { return p.H; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int row) {
-    int r = t.m0 + row;
-    return r < t.m_end ? p.X + (size_t)p.row_token[r] * p.H : nullptr;
-  }
-};
-struct SrcDYRows {
-  __device__ static int ksplit(const GemmArgs& p) { return p.H; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int row) {
-    int r = t.m0 + row;
-    return r < t.m_end ? p.dY + (size_t)p.row_token[r] * p.H : nullptr;
-  }
-};
-// Expert-major activation rows h (contraction axis I).
-struct SrcHRows {
-  __device__ static int ksplit(const GemmArgs& p) { return p.I; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int row) {
-    int r = t.m0 + row;
-    return r < t.m_end ? p.Hrows + (size_t)r * p.I : nullptr;
-  }
-};
-// Expert-major gradient rows [dg | du] (contraction axis 2I).
-struct SrcDGURows {
-  __device__ static int ksplit(const GemmArgs& p) { return 2 * p.I; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int row) {
-    int r = t.m0 + row;
-    return r < t.m_end ? p.dGU + (size_t)r * 2 * p.I : nullptr;
-  }
-};
-// Gate and up weight rows of the packed [E, I, H] layout, interleaved per wave
-// column group: the first half of every WTN rows are gate columns, the second
-// half the up columns of the same intermediate indices.
-template <class C>
-struct SrcGateUpW {
-  __device__ static int ksplit(const GemmArgs& p) { return p.H; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int rr) {
-    constexpr int half = C::WTN / 2;
-    int g = rr / C::WTN, within = rr % C::WTN;
-    bool up = within >= half;
-    int col = t.nt * (C::BN / 2) + g * half + (within % half);
-    return col < p.I ? (up ? p.Wu_t : p.Wg_t) + ((size_t)t.e * p.I + col) * p.H : nullptr;
-  }
-};
-// Packed down weights [E, H, I]: output column n = hidden index.
-struct SrcDownW {
-  __device__ static int ksplit(const GemmArgs& p) { return p.I; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int rr) {
-    int n = t.n0 + rr;
-    return n < p.H ? p.Wd_t + ((size_t)t.e * p.H + n) * p.I : nullptr;
-  }
-};
-// W_down in the math layout [E, I, H] read as [E, N = I, K = H] (P = dY W_down^T).
-struct SrcDownWT {
-  __device__ static int ksplit(const GemmArgs& p) { return p.H; }
-  __device__ static long delta(const GemmArgs&) { return 0; }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int rr) {
-    int n = t.n0 + rr;
-    return n < p.I ? p.Wd + ((size_t)t.e * p.I + n) * p.H : nullptr;
-  }
-};
-// [W_gate | W_up] in the math layout [E, H, I] read as [E, N = H, K = 2I]:
-// columns k >= I come from W_up at the same offset.
-struct SrcGateUpWT {
-  __device__ static int ksplit(const GemmArgs& p) { return p.I; }
-  __device__ static long delta(const GemmArgs& p) { return (long)(p.Wu - p.Wg); }
-  __device__ static const uint16_t* rows(const GemmArgs& p, const Tile& t, int rr) {
-    int n = t.n0 + rr;
-    return n < p.H ? p.Wg + ((size_t)t.e * p.H + n) * p.I : nullptr;
-  }
-};
 // Row sources of the weight-gradient GEMMs (rows are the contraction index).
 struct MNSrcH {
   static constexpr bool SCALED = false;
@@ -122,45 +125,29 @@ struct MNSrcDGU {
 // ------------------------------------------------------------------------
 // Ops: schedule + loaders + epilogue of each GEMM
 // ------------------------------------------------------------------------
-template <class C, class SrcA, class SrcB>
+template <class C, class SrcA_, class SrcB_>
 struct RowOpsBase {
   static constexpr int PHASES = 1;
+  using SrcA = SrcA_;
+  using SrcB = SrcB_;
   using Sched = RowGroups<C::BM, C::BN, C::NT>;
-  using ALoad = KRows<C::BM, C::NT, SrcA, GemmArgs>;
-  using BLoad = KRows<C::BN, C::NT, SrcB, GemmArgs>;
-  __device__ static void init_loaders(ALoad& al, BLoad& bl, const GemmArgs& p, const Tile& t) {
-    al.init(p, t);
-    bl.init(p, t);
-  }
 };
 
 // h = bf16(silu(X Wg) * (X Wu))
 template <class C>
-struct FwdGateUpOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
-  __device__ static void init_sched(typename RowOpsBase<C, SrcXRows, SrcGateUpW<C>>::Sched& s,
+struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
-    const int hcol0 = t.nt * (C::BN / 2) + wn * (C::WTN / 2) + (lane >> 5) * 4;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int r = t.m0 + Frag<C>::row(wm, fm, lane);
-      if (r >= t.m_end) continue;
-      uint16_t* out = p.Hrows + (size_t)r * p.I + hcol0;
-#pragma unroll
-      for (int fn = 0; fn < C::FN / 2; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (hcol0 + fn * 32 + q * 8 >= p.I) continue;
-          float h[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            h[j] = silu_f32(acc[fm][fn][4 * q + j]) * acc[fm][fn + C::FN / 2][4 * q + j];
-          store_bf16x4(out + fn * 32 + q * 8, h[0], h[1], h[2], h[3]);
-        }
-    }
+                                  int wm, int wn, int lane, uint8_t* wlds) {
+    // fragment fn holds intermediate columns (wn * FN + fn) * 16 + [0, 16): items 4q + j (q = 0, 1)
+    // are gate and 4q + 8 + j the up values of column 8q + 4 * (lane / 32) + j
+    stage_store_bf16<C, C::FN * 16, 2>(
+        wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.nt * (C::BN / 2) + wn * C::FN * 16, p.I, lane,
+        [&](int fm, int fn, int q, int j) { return silu_f32(acc[fm][fn][4 * q + j]) * acc[fm][fn][4 * q + 8 + j]; },
+        [](int fn, int q) { return fn * 16 + q * 8; });
   }
 };
 
@@ -192,26 +179,29 @@ __device__ __forceinline__ void store_rows(T* base, int ld, int ncols, const Til
 
 // O = bf16(h Wd)
 template <class C>
-struct FwdDownOps : RowOpsBase<C, SrcHRows, SrcDownW> {
-  __device__ static void init_sched(typename RowOpsBase<C, SrcHRows, SrcDownW>::Sched& s,
+struct FwdDownOps : RowOpsBase<C, RSrcH, RSrcDownW> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcH, RSrcDownW>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, p.I, pre, red);
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
-    store_rows<C, uint16_t>(p.Orows, p.H, p.H, t, acc, wm, wn, lane);
+                                  int wm, int wn, int lane, uint8_t* wlds) {
+    stage_store_bf16<C, C::WTN, 4>(
+        wlds, p.Orows, p.H, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.H, lane,
+        [&](int fm, int fn, int q, int j) { return acc[fm][fn][4 * q + j]; },
+        [](int fn, int q) { return fn * 32 + q * 8; });
   }
 };
 
 // P = dY[token] W_down^T (fp32)
 template <class C>
-struct BwdPOps : RowOpsBase<C, SrcDYRows, SrcDownWT> {
-  __device__ static void init_sched(typename RowOpsBase<C, SrcDYRows, SrcDownWT>::Sched& s,
+struct BwdPOps : RowOpsBase<C, RSrcDY, RSrcDownWT> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDY, RSrcDownWT>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.I, p.H, pre, red);
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
+                                  int wm, int wn, int lane, uint8_t*) {
     store_rows<C, float>(p.P, p.I, p.I, t, acc, wm, wn, lane);
   }
 };
@@ -229,14 +219,14 @@ __device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const f
 
 // Recompute G, U; with P give h, the router-weight partial sums <h, P>, dg and du.
 template <class C>
-struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
-  __device__ static void init_sched(typename RowOpsBase<C, SrcXRows, SrcGateUpW<C>>::Sched& s,
+struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
-    const int hcol0 = t.nt * (C::BN / 2) + wn * (C::WTN / 2) + (lane >> 5) * 4;
+                                  int wm, int wn, int lane, uint8_t*) {
+    // same (gate, up) pairing as the forward: items 4q + j and 4q + 8 + j of fragment fn
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int r = t.m0 + Frag<C>::row(wm, fm, lane);
@@ -244,22 +234,22 @@ struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
       float dot = 0.f;
       if (rv) {
         const float w = p.topk_w[p.row_slot[r]];
-        const float* Prow = p.P + (size_t)r * p.I + hcol0;
-        uint16_t* hrow = p.Hrows + (size_t)r * p.I + hcol0;
-        uint16_t* grow = p.dGU + (size_t)r * 2 * p.I + hcol0;
-        uint16_t* lrow = p.dGU_lo + (size_t)r * 2 * p.I + hcol0;
+        const float* Prow = p.P + (size_t)r * p.I;
+        uint16_t* hrow = p.Hrows + (size_t)r * p.I;
+        uint16_t* grow = p.dGU + (size_t)r * 2 * p.I;
+        uint16_t* lrow = p.dGU_lo + (size_t)r * 2 * p.I;
 #pragma unroll
-        for (int fn = 0; fn < C::FN / 2; ++fn)
+        for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int o = fn * 32 + q * 8;
-            if (hcol0 + o >= p.I) continue;
-            const float4 P4 = *reinterpret_cast<const float4*>(Prow + o);
+          for (int q = 0; q < 2; ++q) {
+            const int col = t.nt * (C::BN / 2) + (wn * C::FN + fn) * 16 + q * 8 + (lane >> 5) * 4;
+            if (col >= p.I) continue;
+            const float4 P4 = *reinterpret_cast<const float4*>(Prow + col);
             const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
             float hv[4], dg[4], du[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float g = acc[fm][fn][4 * q + j], u = acc[fm][fn + C::FN / 2][4 * q + j];
+              const float g = acc[fm][fn][4 * q + j], u = acc[fm][fn][4 * q + 8 + j];
               const float sg = sigmoid_f32(g);
               hv[j] = bf16_to_f32(f32_to_bf16(g * sg * u));
               dot += hv[j] * Pv[j];
@@ -267,9 +257,9 @@ struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
               du[j] = dh * (g * sg);
               dg[j] = dh * u * (sg * (1.f + g * (1.f - sg)));
             }
-            store_bf16x4(hrow + o, hv[0], hv[1], hv[2], hv[3]);
-            store_split4(grow + o, lrow + o, dg);
-            store_split4(grow + p.I + o, lrow + p.I + o, du);
+            store_bf16x4(hrow + col, hv[0], hv[1], hv[2], hv[3]);
+            store_split4(grow + col, lrow + col, dg);
+            store_split4(grow + p.I + col, lrow + p.I + col, du);
           }
       }
       // the other half of this row's columns sits in lane ^ 32
@@ -281,13 +271,13 @@ struct BwdRecomputeOps : RowOpsBase<C, SrcXRows, SrcGateUpW<C>> {
 
 // dXr = [dg | du] [W_gate | W_up]^T (fp32 rows)
 template <class C>
-struct BwdDXOps : RowOpsBase<C, SrcDGURows, SrcGateUpWT> {
-  __device__ static void init_sched(typename RowOpsBase<C, SrcDGURows, SrcGateUpWT>::Sched& s,
+struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDGU, RSrcGateUpWT>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, 2 * p.I, pre, red);
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
+                                  int wm, int wn, int lane, uint8_t*) {
     store_rows<C, float>(p.dXr, p.H, p.H, t, acc, wm, wn, lane);
   }
 };
@@ -364,18 +354,22 @@ struct BwdDWGateUpOps : WgOpsBase<C, MNSrcX, MNSrcDGU> {
 // ------------------------------------------------------------------------
 // Kernels and launchers
 // ------------------------------------------------------------------------
-#define MOE_GEMM_KERNEL(NAME, OPS)                                                 \
+#define MOE_ROWS_KERNEL(NAME, OPS)                                                 \
+  __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {          \
+    rows_gemm_body<CfgRows, OPS<CfgRows>, GemmArgs>(p);                            \
+  }
+#define MOE_WG_KERNEL(NAME, OPS)                                                   \
   __global__ void __launch_bounds__(CfgMain::NT) NAME(const GemmArgs p) {          \
     grouped_gemm_body<CfgMain, OPS<CfgMain>, GemmArgs>(p);                         \
   }
 
-MOE_GEMM_KERNEL(k_fwd_gateup, FwdGateUpOps)
-MOE_GEMM_KERNEL(k_fwd_down, FwdDownOps)
-MOE_GEMM_KERNEL(k_bwd_p, BwdPOps)
-MOE_GEMM_KERNEL(k_bwd_recompute, BwdRecomputeOps)
-MOE_GEMM_KERNEL(k_bwd_dx_rows, BwdDXOps)
-MOE_GEMM_KERNEL(k_bwd_dw_down, BwdDWDownOps)
-MOE_GEMM_KERNEL(k_bwd_dw_gateup, BwdDWGateUpOps)
+MOE_ROWS_KERNEL(k_fwd_gateup, FwdGateUpOps)
+MOE_ROWS_KERNEL(k_fwd_down, FwdDownOps)
+MOE_ROWS_KERNEL(k_bwd_p, BwdPOps)
+MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
+MOE_ROWS_KERNEL(k_bwd_dx_rows, BwdDXOps)
+MOE_WG_KERNEL(k_bwd_dw_down, BwdDWDownOps)
+MOE_WG_KERNEL(k_bwd_dw_gateup, BwdDWGateUpOps)
 
 template <class C>
 static int row_grid(const GemmArgs& a, int N) {
@@ -395,26 +389,26 @@ static int wg_grid(const GemmArgs& a, int M, int N) {
 }
 
 hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_fwd_gateup, dim3(row_grid<CfgMain>(a, 2 * a.I)), dim3(CfgMain::NT), 0, s, a);
+  hipLaunchKernelGGL(k_fwd_gateup, dim3(row_grid<CfgRows>(a, 2 * a.I)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_fwd_down, dim3(row_grid<CfgMain>(a, a.H)), dim3(CfgMain::NT), 0, s, a);
+  hipLaunchKernelGGL(k_fwd_down, dim3(row_grid<CfgRows>(a, a.H)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_p, dim3(row_grid<CfgMain>(a, a.I)), dim3(CfgMain::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_p, dim3(row_grid<CfgRows>(a, a.I)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 int bwd_nparts(int I) {
-  return ((2 * I + CfgMain::BN - 1) / CfgMain::BN) * CfgMain::WAVES_N;
+  return ((2 * I + CfgRows::BN - 1) / CfgRows::BN) * CfgRows::WAVES_N;
 }
 hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_recompute, dim3(row_grid<CfgMain>(a, 2 * a.I)), dim3(CfgMain::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_recompute, dim3(row_grid<CfgRows>(a, 2 * a.I)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dx_rows, dim3(row_grid<CfgMain>(a, a.H)), dim3(CfgMain::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_dx_rows, dim3(row_grid<CfgRows>(a, a.H)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s) {
