@@ -12,11 +12,47 @@ namespace moe {
 // registers; k rounds of a wave arg-max pick the experts in descending logit
 // order, ties to the lowest index.  The weights are exp(l_j - l_max) over the
 // chosen logits, normalised by their sum (softmax over E renormalised over k).
+//
+// The arg-max runs on 64-bit keys that order exactly like (logit, -index):
+// high word = the fp32 logit mapped to an unsigned integer of the same order
+// (-0.0 first turned into +0.0), low word = ~index.  Inside each 16-lane row the
+// maximum key is spread with DPP lane permutations (no LDS round trip); the four
+// row maxima are combined through readlane.
 // ---------------------------------------------------------------------------
 constexpr int ROUTE_MAX_PER_LANE = 16;
 
-__device__ __forceinline__ bool route_better(float v1, int i1, float v2, int i2) {
-  return v1 > v2 || (v1 == v2 && i1 < i2);
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~e);
+}
+__device__ __forceinline__ float route_key_logit(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum key of the wave (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = max_u64(k, dpp_u64<0xb1>(k));    // quad_perm [1,0,3,2]: lane ^ 1
+  k = max_u64(k, dpp_u64<0x4e>(k));    // quad_perm [2,3,0,1]: lane ^ 2
+  k = max_u64(k, dpp_u64<0x141>(k));   // row_half_mirror: the other quad of each 8
+  k = max_u64(k, dpp_u64<0x140>(k));   // row_mirror: the other half of each 16
+  return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
 }
 
 __global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits, int T, int E, int k,
@@ -25,50 +61,31 @@ __global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  float v[ROUTE_MAX_PER_LANE];
-  uint32_t taken = 0;
+  uint64_t key[ROUTE_MAX_PER_LANE];
 #pragma unroll
   for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
-    int e = lane + 64 * i;
-    v[i] = (e < E) ? row[e] : 0.f;
-    if (e >= E) taken |= 1u << i;
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? route_key(row[e], e) : 0ull;   // 0 sorts below every real key
   }
-  float sel_v = 0.f;   // lane j < k keeps the j-th chosen logit
-  int sel_i = 0;
-  float top = 0.f;
+  uint64_t mine = 0;                                    // lane j < k keeps the j-th chosen key
   for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
-      int e = lane + 64 * i;
-      if (!(taken & (1u << i)) && route_better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
+    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) best = max_u64(best, key[i]);
+    const uint64_t top = wave_max_key(best);
+    const int e = (int)~(uint32_t)top;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
-      if (route_better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      sel_v = bv;
-      sel_i = bi;
-    }
-    if (j == 0) top = bv;
+    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i)
+      if (lane + 64 * i == e) key[i] = 0ull;            // taken
+    if (lane == j) mine = top;
   }
-  float ex = (lane < k) ? expf(sel_v - top) : 0.f;
+  const float first = route_key_logit(readlane_u64(mine, 0));
+  const float ex = (lane < k) ? expf(route_key_logit(mine) - first) : 0.f;
   float sum = ex;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
   if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = sel_i;
+    topk_idx[(size_t)t * k + lane] = (int)~(uint32_t)mine;
     topk_w[(size_t)t * k + lane] = ex / sum;
   }
 }
@@ -117,9 +134,15 @@ __global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restric
   for (int e = threadIdx.x; e < 4 * DISPATCH_MAX_E; e += 256) (&hist[0][0])[e] = 0;
   __syncthreads();
   const long base = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
+  int ids[DISPATCH_WAVE_SLOTS / 64];          // all of this wave's ids in flight at once
+#pragma unroll
   for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
-    long s = base + g * 64 + lane;
-    int e = (s < A) ? idx[s] : -1;
+    const long s = base + g * 64 + lane;
+    ids[g] = (s < A) ? idx[s] : -1;
+  }
+#pragma unroll
+  for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
+    int e = ids[g];
     if (e >= E) e = -1;                       // out-of-range ids are skipped
     int key = (e >= 0) ? e : 0x400;
     uint64_t m = match_key(key);
@@ -205,9 +228,16 @@ __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restr
   // stable scatter of this wave's 1024 slots
   const long sbase = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int ids[DISPATCH_WAVE_SLOTS / 64];
+#pragma unroll
+  for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
+    const long s = sbase + g * 64 + lane;
+    ids[g] = (s < A) ? idx[s] : -1;
+  }
+#pragma unroll
   for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
     long s = sbase + g * 64 + lane;
-    int e = (s < A) ? idx[s] : -1;
+    int e = ids[g];
     if (e >= E) e = -1;                       // out-of-range ids are skipped
     int key = (e >= 0) ? e : 0x400;
     uint64_t m = match_key(key);
