@@ -15,9 +15,24 @@
 // and never stored, so every load is unconditional.
 #pragma once
 
+#include <type_traits>
+
 #include "grouped_gemm.h"
 
+#ifndef MOE_ROWS_LPS
+#define MOE_ROWS_LPS 4
+#endif
+
 namespace moe {
+
+// Calls f(std::integral_constant<int, i>) for i in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NST_>
 struct RowCfg {
@@ -41,6 +56,21 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One direct global->LDS load: 64 lanes x 16 bytes from base + voff (per lane) to
+// LDS [lds, lds + 1024) (lane l at lds + 16 l).  Written as inline assembly so that
+// the compiler's wait insertion, which cannot tell the LDS range it writes from
+// the stage being read, does not make every later LDS read wait for it; the
+// loops wait for these loads explicitly (s_waitcnt vmcnt) before the barrier
+// that publishes a stage.
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "m0");
+}
+
 // Loader of one operand: rows [0, ROWS) of the tile.  Src provides
 //   static const uint16_t* base(const P&, const Tile&, int row0, int k0): wave-uniform base of the
 //       rows [row0, row0 + 64 / CPR) for k-tile k0 (element 0 of the k-tile);
@@ -50,7 +80,7 @@ template <class C, int ROWS, class Src, class P>
 struct DirectRows {
   static constexpr int INST = ROWS * C::CPR / 64;        // load instructions per stage
   static constexpr int PER = INST / C::NW;               // ... per wave
-  uint32_t off[PER];
+  uint32_t off[PER];                                     // byte offsets from the wave-uniform base
 
   __device__ void init(const P& p, const Tile& tl) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -59,76 +89,91 @@ struct DirectRows {
       const int s = (i * C::NW + wave) * 64 + lane;
       const int row = s / C::CPR;
       const int chunk = (s % C::CPR) ^ swz<C::CPR>(row);
-      off[i] = Src::row_off(p, tl, row) + chunk * 8;
+      off[i] = (Src::row_off(p, tl, row) + chunk * 8) * 2u;
     }
+  }
+  // Issue load instruction i (< PER) of k-tile k0 into the stage at `lds` (uint4 slots):
+  // scalar base + 32-bit vector offset.
+  __device__ void issue_one(const P& p, const Tile& tl, int k0, uint4* lds, int i) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (i * C::NW + wave) * 64;
+    const uint8_t* b = reinterpret_cast<const uint8_t*>(Src::base(p, tl, S / C::CPR, k0));
+    lds_dma16(b, off[i], lds_addr(lds + S));
   }
   // Issue the loads of k-tile k0 into the stage at `lds` (uint4 slots).
   __device__ void issue(const P& p, const Tile& tl, int k0, uint4* lds) const {
-    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int S = (i * C::NW + wave) * 64;
-      const uint16_t* b = Src::base(p, tl, S / C::CPR, k0);
-      __builtin_amdgcn_global_load_lds(b + off[i], lds + S, 16, 0, 0);
+    for (int i = 0; i < PER; ++i) issue_one(p, tl, k0, lds, i);
+  }
+};
+
+// Byte offsets of this lane's MFMA operand chunks inside a stage, for sub-step 0.
+// Chunk c of row r sits at position c ^ swz(r); a lane of half h reads chunk
+// 2 kk + h = (2 kk) ^ h at sub-step kk, so its position is (swz(r) ^ h) ^ 2 kk and
+// the byte offset is base ^ (32 kk): one XOR per read, no per-sub-step table.
+template <class C>
+struct FragAddr {
+  uint32_t a[C::FM], b[C::FN];
+  __device__ void init(int wm, int wn, int lane) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int r = wm * C::WTM + fm * 32 + (lane & 31);
+      a[fm] = (uint32_t)(r * C::CPR + (swz<C::CPR>(r) ^ h)) * 16u;
+    }
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int r = wn * C::WTN + fn * 32 + (lane & 31);
+      b[fn] = (uint32_t)(C::A_SLOTS + r * C::CPR + (swz<C::CPR>(r) ^ h)) * 16u;
     }
   }
 };
 
-// L2 warming: one 16-byte load per tile row and k-tile, issued a few k-tiles
-// ahead of the real loads into a dummy LDS slot.  Rows [0, BM) are operand A,
-// [BM, BM + BN) operand B; lane l of wave w takes row w * 64 + l (and + NW * 64 ...).
-// It is the newest vector-memory instruction of its k step, so the waits for the
-// real loads (vmcnt is retired in issue order) never wait for it.
-template <class C, class SrcA, class SrcB, class P>
-struct RowPrefetch {
-  static constexpr int ROWS = C::BM + C::BN;
-  static constexpr int PER = (ROWS + 64 * C::NW - 1) / (64 * C::NW);
-  __device__ static void issue(const P& p, const Tile& tl, int k0, uint4* dummy) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One k-tile: BK / 16 MFMA sub-steps, the operand reads of sub-step kk + 1 in
+// flight under the MFMAs of sub-step kk (two register sets).  With LOADS, the
+// NLOAD global->LDS load instructions of a later k-tile (issue(j), j < NLOAD)
+// are spread over the sub-steps, one between two MFMAs, so that no wave stalls
+// on a burst of vector-memory issues before its MFMAs.
+template <class C, bool LOADS, int NLOAD, class Issue>
+__device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragAddr<C>& fa,
+                                               f32x16 (&acc)[C::FM][C::FN], Issue issue) {
+  constexpr int KK = C::BK / 16;
+  constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+  constexpr int LPS = MOE_ROWS_LPS < NLOAD ? MOE_ROWS_LPS : NLOAD;   // loads per sub-step, front-loaded
+  static_assert(!LOADS || LPS * KK >= NLOAD, "every load of the k-tile must be issued");
+  bf16x8 a[2][C::FM], b[2][C::FN];
+  auto load = [&](int kk, int buf) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int row = (i * C::NW + wave) * 64 + lane;
-      if (row < C::BM) {
-        __builtin_amdgcn_global_load_lds(SrcA::base(p, tl, row, k0) + SrcA::row_off(p, tl, row), dummy, 16, 0, 0);
-      } else if (row < ROWS) {
-        const int rb = row - C::BM;
-        __builtin_amdgcn_global_load_lds(SrcB::base(p, tl, rb, k0) + SrcB::row_off(p, tl, rb), dummy, 16, 0, 0);
-      }
-    }
-  }
-};
-
-template <class C>
-__device__ __forceinline__ void load_frags(const uint4* As, const uint4* Bs, int kk, int wm, int wn, int lane,
-                                           bf16x8 (&a)[C::FM], bf16x8 (&b)[C::FN]) {
-  const int ch = kk * 2 + (lane >> 5);
+    for (int fm = 0; fm < C::FM; ++fm)
+      a[buf][fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.a[fm] ^ (32u * kk))));
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int r = wm * C::WTM + fm * 32 + (lane & 31);
-    a[fm] = __builtin_bit_cast(bf16x8, As[r * C::CPR + (ch ^ swz<C::CPR>(r))]);
-  }
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int r = wn * C::WTN + fn * 32 + (lane & 31);
-    b[fn] = __builtin_bit_cast(bf16x8, Bs[r * C::CPR + (ch ^ swz<C::CPR>(r))]);
-  }
-}
-
-// One k-tile: BK / 16 MFMA sub-steps.  (Double-buffering the operand registers
-// across sub-steps measured no faster: the loop is bound by global load latency.)
-template <class C>
-__device__ __forceinline__ void mma_ktile_rows(const uint4* As, const uint4* Bs, f32x16 (&acc)[C::FM][C::FN],
-                                               int wm, int wn, int lane) {
-#pragma unroll
-  for (int kk = 0; kk < C::BK / 16; ++kk) {
-    bf16x8 a[C::FM], b[C::FN];
-    load_frags<C>(As, Bs, kk, wm, wn, lane, a, b);
+    for (int fn = 0; fn < C::FN; ++fn)
+      b[buf][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.b[fn] ^ (32u * kk))));
+  };
+  load(0, 0);
+  static_for<0, KK>([&](auto kkc) {
+    constexpr int kk = decltype(kkc)::value;
+    constexpr int J0 = kk * LPS, J1 = (kk + 1) * LPS < NLOAD ? (kk + 1) * LPS : NLOAD;
+    constexpr int NL = LOADS && J1 > J0 ? J1 - J0 : 0;
+    if constexpr (kk + 1 < KK) load(kk + 1, (kk + 1) & 1);
+    static_for<0, NL>([&](auto jc) { issue(J0 + decltype(jc)::value); });
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[fn], a[fm], acc[fm][fn], 0, 0, 0);
-  }
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][fn], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+    // issue order: the next sub-step's LDS reads early, between the first MFMAs,
+    // then the global loads one per MFMA
+    constexpr int EARLY = kk + 1 < KK ? 2 : 0;
+    if constexpr (kk + 1 < KK) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR - NR / 2, 0);
+    }
+    if constexpr (NM - EARLY > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - EARLY, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 template <int N>
@@ -161,18 +206,12 @@ struct RowEpiLds {
 template <class C, class Ops, class P>
 __device__ __forceinline__ void rows_gemm_body(const P& p) {
   __shared__ uint4 smem[C::NST * C::STAGE];
-  __shared__ uint4 dummy[64];
   __shared__ int sched_lds[1024 + 1 + C::NT / 64 + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   using AL = DirectRows<C, C::BM, typename Ops::SrcA, P>;
   using BL = DirectRows<C, C::BN, typename Ops::SrcB, P>;
-  using PF = RowPrefetch<C, typename Ops::SrcA, typename Ops::SrcB, P>;
   constexpr int PERK = AL::PER + BL::PER;                 // real load instructions per k-tile per wave
-  // L2 warming measured slower on the prefill and training shapes (extra requests and
-  // in-order vmcnt waits on warming loads outweigh the misses they save): off.
-  constexpr bool PREFETCH = false;
-  constexpr int PF_DIST = 3;                              // k-tiles ahead of the one being computed
 
   typename Ops::Sched sched;
   Ops::init_sched(sched, p, sched_lds, sched_lds + 1025);
@@ -180,6 +219,8 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
   walk.init(sched.total);
   if (!walk.valid()) return;
   Tile tl = sched.tile(walk.t);
+  FragAddr<C> fa;
+  fa.init(wm, wn, lane);
   AL al;
   BL bl;
   al.init(p, tl);
@@ -192,9 +233,6 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
       al.issue(p, tl, s * C::BK, smem + s * C::STAGE);
       bl.issue(p, tl, s * C::BK, smem + s * C::STAGE + C::A_SLOTS);
     }
-  if constexpr (PREFETCH) {
-    for (int s = 1; s < PF_DIST && s < nk; ++s) PF::issue(p, tl, s * C::BK, dummy);
-  }
   while (true) {
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -203,31 +241,26 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
-    bool pf_last = false;                                 // did the previous k step issue a prefetch?
-    for (int kt = 0; kt < nk; ++kt) {
-      if constexpr (PREFETCH) {
-        if (kt == 0) wait_vmcnt<0>();
-        else if (pf_last) wait_vmcnt<1>();
-        else wait_vmcnt<0>();
-      } else {
-        const int ahead = nk - 1 - kt;                    // k-tiles issued after this one (capped)
-        if (kt == 0) wait_vmcnt<0>();
-        else wait_ktiles<C::NST, PERK>(ahead < C::NST - 2 ? ahead : C::NST - 2);
-      }
+    // k step kt: wait for k-tile kt, then compute it while (LOADS) issuing k-tile kt + NST - 1
+    auto kstep = [&](int kt, auto loads) {
+      const int ahead = nk - 1 - kt;                      // k-tiles issued after this one (capped)
+      if (kt == 0) wait_vmcnt<0>();
+      else wait_ktiles<C::NST, PERK>(ahead < C::NST - 2 ? ahead : C::NST - 2);
       __syncthreads();
       const int nxt = kt + C::NST - 1;
-      if (nxt < nk) {
-        uint4* st = smem + (nxt % C::NST) * C::STAGE;
-        al.issue(p, tl, nxt * C::BK, st);
-        bl.issue(p, tl, nxt * C::BK, st + C::A_SLOTS);
-      }
-      if constexpr (PREFETCH) {
-        pf_last = kt + PF_DIST < nk;
-        if (pf_last) PF::issue(p, tl, (kt + PF_DIST) * C::BK, dummy);
-      }
-      const uint4* cur = smem + (kt % C::NST) * C::STAGE;
-      mma_ktile_rows<C>(cur, cur + C::A_SLOTS, acc, wm, wn, lane);
-    }
+      uint4* st = smem + (nxt % C::NST) * C::STAGE;
+      auto issue = [&](int j) {
+        if (j < AL::PER) al.issue_one(p, tl, nxt * C::BK, st, j);
+        else bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
+      };
+      const uint8_t* cur = reinterpret_cast<const uint8_t*>(smem + (kt % C::NST) * C::STAGE);
+      mma_ktile_rows<C, decltype(loads)::value, PERK>(cur, fa, acc, issue);
+    };
+    // the last NST - 1 k steps issue nothing: peeled, not branched, so that the
+    // two instantiations never meet inside one loop body
+    int kt = 0;
+    for (; kt < nk - (C::NST - 1); ++kt) kstep(kt, std::true_type{});
+    for (; kt < nk; ++kt) kstep(kt, std::false_type{});
     // every wave is past its last LDS read before any stage is refilled
     __syncthreads();
     const Tile done = tl;
@@ -245,9 +278,6 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
           al.issue(p, tl, s * C::BK, smem + s * C::STAGE);
           bl.issue(p, tl, s * C::BK, smem + s * C::STAGE + C::A_SLOTS);
         }
-      if constexpr (PREFETCH) {
-        for (int s = 1; s < PF_DIST && s < nk; ++s) PF::issue(p, tl, s * C::BK, dummy);
-      }
     }
     uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + (C::NST - 1) * C::STAGE) + wave * RowEpiLds<C>::BYTES;
     Ops::epilogue(p, done, acc, wm, wn, lane, wave_lds);
@@ -266,9 +296,14 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
 template <class C, int CW, int NQ, class Val, class Col>
 __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, int ld, int row0, int row_end,
                                                  int col0, int ncols, int lane, Val val, Col col_of) {
-  constexpr int PITCH = CW * 2 + 16;                     // bytes per staged row (16-byte aligned)
   constexpr int CPRW = CW * 2 / 16;                      // 16-byte chunks per row
+  // Rows padded by 16 bytes where the scratch allows it, else unpadded 128-byte
+  // rows with chunk c of row r stored at c ^ ((r >> 1) & 7).
+  constexpr bool SWZ = 32 * (CW * 2 + 16) > RowEpiLds<C>::BYTES;
+  constexpr int PITCH = SWZ ? CW * 2 : CW * 2 + 16;
   static_assert(32 * PITCH <= RowEpiLds<C>::BYTES, "staging area too small");
+  static_assert(!SWZ || CPRW == 8, "swizzled staging needs 128-byte rows");
+  auto pos = [](int r, int ch) { return SWZ ? (ch ^ ((r >> 1) & 7)) : ch; };
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int r = lane & 31;
@@ -280,14 +315,14 @@ __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, i
         uint2 v;
         v.x = pack_bf16x2(val(fm, fn, q, 0), val(fm, fn, q, 1));
         v.y = pack_bf16x2(val(fm, fn, q, 2), val(fm, fn, q, 3));
-        *reinterpret_cast<uint2*>(wlds + r * PITCH + c * 2) = v;
+        *reinterpret_cast<uint2*>(wlds + r * PITCH + pos(r, c >> 3) * 16 + (c & 7) * 2) = v;
       }
     // read back 16-byte chunks: 64 / CPRW rows per step
 #pragma unroll
     for (int i = 0; i < 32 * CPRW / 64; ++i) {
       const int idx = i * 64 + lane;
       const int rr = idx / CPRW, ch = idx % CPRW;
-      const uint4 v = *reinterpret_cast<const uint4*>(wlds + rr * PITCH + ch * 16);
+      const uint4 v = *reinterpret_cast<const uint4*>(wlds + rr * PITCH + pos(rr, ch) * 16);
       const int grow = row0 + fm * 32 + rr;
       const int gcol = col0 + ch * 8;
       if (grow < row_end && gcol < ncols) *reinterpret_cast<uint4*>(out + (size_t)grow * ld + gcol) = v;

@@ -128,12 +128,13 @@ struct RowGroups {
       int mid = (lo + hi + 1) >> 1;
       if (prefix[mid] <= mt) lo = mid; else hi = mid - 1;
     }
+    // every lane computes the same tile: keep its fields in scalar registers
     Tile tl;
-    tl.e = lo;
-    tl.m0 = offsets[lo] + (mt - prefix[lo]) * BM;
-    tl.m_end = offsets[lo + 1];
-    tl.n0 = nt * BN;
-    tl.nt = nt;
+    tl.e = __builtin_amdgcn_readfirstlane(lo);
+    tl.m0 = __builtin_amdgcn_readfirstlane(offsets[lo] + (mt - prefix[lo]) * BM);
+    tl.m_end = __builtin_amdgcn_readfirstlane(offsets[lo + 1]);
+    tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
+    tl.nt = __builtin_amdgcn_readfirstlane(nt);
     tl.k_lo = 0;
     tl.k_hi = K;
     return tl;
