@@ -35,7 +35,24 @@ def parse():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the warmup, copy 1 GiB device to device three times (the known-size "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def recorded_traffic(workload):
+    """HBM bytes of one moe_expert_mlp call from the committed counter runs, or None when there are
+    none for this workload or the library sources changed since they were taken."""
+    from grouped_gemm_router_amd import profile_tools as pt
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha") != pt.source_hash():
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def device_weights(cfg, name, experts=None):
@@ -132,6 +149,14 @@ def main():
         if cfg.backward:
             layer.backward(X, dY)
 
+    if args.copy_calibration:
+        from grouped_gemm_router_amd.profile_tools import COPY_BYTES
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -195,13 +220,13 @@ def main():
             achieved = (weight_bytes + cfg.A * (cfg.H + cfg.I) * 2 * 2) / (mlp_ms * 1e-3) / 1e9
             out["roofline"] = {"kernel": "moe_expert_mlp (gate/up+SwiGLU and down)", "bound": "hbm",
                                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                               "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                               "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": recorded_traffic(cfg.name),
                                "avg_launch_ms": round(mlp_ms, 5)}
         else:
             achieved = mlp_flops / (mlp_ms * 1e-3) / 1e12
             out["roofline"] = {"kernel": "moe_expert_mlp (gate/up+SwiGLU and down grouped GEMMs)",
                                "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                               "frac": round(achieved / peak, 4), "traffic": None,
+                               "frac": round(achieved / peak, 4), "traffic": recorded_traffic(cfg.name),
                                "avg_launch_ms": round(mlp_ms, 5)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, logits_np, X_np, dY_np)

@@ -1,0 +1,180 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+Usage (from the repository root, after the profiling runs):
+
+  python -m grouped_gemm_router_amd.profile_tools stats <rocprof-dir> <out.md> --cmd "<command>" --title "<title>"
+      kernel table (calls, average / min / max duration, share of GPU time) from
+      <rocprof-dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace --stats --output-format csv -o run)
+
+  python -m grouped_gemm_router_amd.profile_tools traffic --fetch <dir> --write <dir> --workload <name> \\
+      --out <traffic.json> [--md <out.md>] [--cmd-fetch "<command>"] [--cmd-write "<command>"]
+      HBM traffic of one moe_expert_mlp call from two counter runs (rocprofv3 --pmc FETCH_SIZE,
+      then --pmc WRITE_SIZE, --output-format csv -o run) of ``bench.py --copy-calibration``.  Each
+      counter is scaled by what it reads for the calibration copy of a known number of bytes.
+
+The traffic record carries a hash of the library sources; bench.py reports it
+only while the kernels are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_BYTES = 1 << 30                    # bytes moved by bench.py --copy-calibration per copy
+COPY_KERNEL = "copyBuffer"              # the HIP runtime's device-to-device copy kernel
+MLP_KERNELS = {                         # kernels of one moe_expert_mlp call, per workload kind
+    "bf16": ("k_fwd_gateup", "k_fwd_down"),
+    "decode": ("k_decode_gateup", "k_decode_down"),
+    "mxfp8": ("k_mx_quantize", "k_mx_gateup", "k_mx_down"),
+}
+
+
+def source_hash() -> str:
+    """sha256 over the library sources (kernels, host code, header)."""
+    h = hashlib.sha256()
+    files = [os.path.join(ROOT, "include", "moe.h")]
+    csrc = os.path.join(PKG, "csrc")
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h", ".cpp"))]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("moe::", "")
+
+
+def stats_md(src: str, out: str, cmd: str, title: str, note: str = "") -> None:
+    rows = list(csv.DictReader(open(os.path.join(src, "run_kernel_stats.csv"))))
+    agent = list(csv.DictReader(open(os.path.join(src, "run_agent_info.csv"))))
+    gpus = [a for a in agent if a.get("Agent_Type", "").upper() == "GPU"]
+    dev = gpus[0].get("Name", "?") if gpus else "?"
+    lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
+             f"Device: {dev}.  Per-kernel durations from the kernel trace (`run_kernel_stats.csv`).", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        n = r["Name"].replace("|", "/")
+        if len(n) > 90:
+            n = n[:87] + "..."
+        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} "
+                     f"| {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(src: str, counter: str) -> dict:
+    """kernel short name -> list of (dispatch id, counter value summed over instances / XCDs)."""
+    acc = collections.defaultdict(float)
+    name_of = {}
+    for r in csv.DictReader(open(os.path.join(src, "run_counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        acc[d] += float(r["Counter_Value"])
+        name_of[d] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for d in sorted(acc):
+        out[_short(name_of[d])].append((d, acc[d]))
+    return out
+
+
+def _kind(workload: str) -> str:
+    if workload.startswith("decode") or workload == "tiny":
+        return "decode"
+    if "mxfp8" in workload:
+        return "mxfp8"
+    return "bf16"
+
+
+def traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one moe_expert_mlp call, scaled by the copy."""
+    res = {"workload": workload, "source_sha": source_hash(), "copy_bytes": COPY_BYTES}
+    for counter, src in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _per_dispatch(src, counter)
+        copy = sorted(v for k, vals in per.items() if COPY_KERNEL in k for _, v in vals)
+        if not copy:
+            raise SystemExit(f"no {COPY_KERNEL} dispatch in {src}: run bench.py with --copy-calibration")
+        copy_kib = copy[len(copy) // 2]
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        kernels = MLP_KERNELS[_kind(workload)]
+        main = [k for k in kernels if k != "k_mx_quantize"][0]      # one dispatch per call
+        calls = per.get(main, [])
+        if not calls:
+            raise SystemExit(f"no {main} dispatch in {src}")
+        first = calls[0][0]
+        call = 0.0
+        detail = {}
+        for k in kernels:
+            # per-call dispatches only (weight quantisation at load time comes before the first call;
+            # a call's input quantisation is the dispatch just before its first GEMM)
+            vals = [v for d, v in per.get(k, []) if d >= first - 1]
+            if not vals:
+                continue
+            b = sum(vals) / len(calls) * 1024.0 * factor
+            detail[k] = round(b)
+            call += b
+        res[counter] = {"copy_kib_read": copy_kib, "factor": factor, "calls": len(calls),
+                        "per_kernel_bytes": detail, "call_bytes": round(call)}
+    res["traffic_bytes"] = res["FETCH_SIZE"]["call_bytes"] + res["WRITE_SIZE"]["call_bytes"]
+    return res
+
+
+def traffic_md(t: dict, out: str, cmd_fetch: str, cmd_write: str) -> None:
+    lines = [f"# HBM traffic of one moe_expert_mlp call, workload {t['workload']}", "",
+             "Commands (repository root, one MI355X; one counter per run):", "", "```", cmd_fetch, cmd_write, "```", "",
+             f"Calibration: the counters read for a device-to-device copy of {t['copy_bytes']} bytes "
+             "(the HIP runtime's copy kernel, run by `--copy-calibration`) give the scale factor "
+             "bytes / (KiB read x 1024) applied to every kernel.", "",
+             "| counter | copy reads (KiB) | factor | per kernel (bytes per launch) | per call (bytes) |",
+             "|---|---:|---:|---|---:|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = t[c]
+        per = ", ".join(f"{k}: {v / 1e6:.1f} MB" for k, v in d["per_kernel_bytes"].items())
+        lines.append(f"| {c} | {d['copy_kib_read']:.0f} | {d['factor']:.4f} | {per} | {d['call_bytes'] / 1e6:.1f} MB |")
+    lines += ["", f"Total per call: {t['traffic_bytes'] / 1e6:.1f} MB.  Library source sha256: `{t['source_sha']}`."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="action", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("src")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--note", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--md")
+    t.add_argument("--cmd-fetch", default="")
+    t.add_argument("--cmd-write", default="")
+    a = ap.parse_args(argv)
+    if a.action == "stats":
+        stats_md(a.src, a.out, a.cmd, a.title, a.note)
+    else:
+        res = traffic(a.fetch, a.write, a.workload)
+        with open(a.out, "w") as fh:
+            json.dump(res, fh, indent=1)
+        if a.md:
+            traffic_md(res, a.md, a.cmd_fetch, a.cmd_write)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

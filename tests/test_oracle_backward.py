@@ -120,3 +120,16 @@ def test_rounded_mode_close_to_exact():
     for key in ("dWg", "dWu", "dWd"):
         for e in range(6):
             assert rel(gr["dW"][key][e], ge["dW"][key][e]) < 1e-2
+
+
+def test_backward_tokens_matches_full_backward():
+    """The per-token path used for sampled checks at full size equals the
+    per-expert backward (itself pinned to autograd above), exactly in exact
+    mode and after bf16 rounding of dX otherwise."""
+    X, Wg, Wu, Wd, dY, idx, w = _problem(4, T=16, E=6, k=3)
+    toks = np.array([0, 3, 7, 15])
+    for exact in (True, False):
+        full = orc.backward(X, dY, idx, w, Wg, Wu, Wd, exact=exact)
+        dX, dwt = orc.backward_tokens(X, dY, idx, w, Wg, Wu, Wd, toks, exact=exact)
+        np.testing.assert_allclose(dX, full["dX"][toks], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(dwt, full["d_topk_w"][toks], rtol=1e-12, atol=1e-14)
