@@ -41,7 +41,7 @@ moe_status check_problem(const moe_problem* p) {
 }
 
 size_t mlp_ws(const moe_problem* p) {
-  if (p->dtype != MOE_DTYPE_MXFP8) return 0;
+  if (p->dtype != MOE_DTYPE_MXFP8) return p->T <= moe::DECODE_MAX_T ? align_up(moe::decode_ws_bytes(p->E)) : 0;
   const size_t T = p->T, H = p->H, I = p->I, A = (size_t)p->T * p->k;
   return align_up(T * H) + align_up(T * H / 32) + align_up(A * I) + align_up(A * I / 32);
 }
@@ -187,6 +187,7 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
     a.Wd_t = (const uint16_t*)Wd_t;
     a.Hrows = (uint16_t*)H_rows;
     a.Orows = (uint16_t*)O_rows;
+    a.wlist = (int32_t*)ws;
     if (p->T <= moe::DECODE_MAX_T) return from_hip(moe::launch_decode_mlp(a, st));
     hipError_t e = moe::launch_fwd_gateup(a, st);
     if (e == hipSuccess) e = moe::launch_fwd_down(a, st);

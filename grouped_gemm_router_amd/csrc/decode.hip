@@ -21,17 +21,18 @@
 namespace moe {
 
 constexpr int DEC_NT = 256;            // 4 waves
-constexpr int DEC_GROUPS = DECODE_MAX_T / 16;
 
-// Experts with rows, in expert order: list[0..count).  Returns count.
-__device__ int build_active_list(const int32_t* offsets, int E, int* list, int* red) {
+// Work list of (expert, group of 16 rows) entries for the experts that have
+// rows, in expert order: list[i] = e | (group << 16), i < count.  Returns count
+// (at most 4 * E entries: T <= 64).
+__device__ int build_group_list(const int32_t* offsets, int E, int* list, int* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int flags[4], sum = 0;
+  int cnt[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int e = threadIdx.x * 4 + i;
-    flags[i] = (e < E) && (offsets[e + 1] > offsets[e]);
-    sum += flags[i];
+    cnt[i] = (e < E) ? (offsets[e + 1] - offsets[e] + 15) >> 4 : 0;
+    sum += cnt[i];
   }
   int x = sum;
 #pragma unroll
@@ -49,9 +50,18 @@ __device__ int build_active_list(const int32_t* offsets, int E, int* list, int* 
   int pos = base + x - sum;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (flags[i]) list[pos++] = threadIdx.x * 4 + i;
+    for (int g = 0; g < cnt[i]; ++g) list[pos++] = (threadIdx.x * 4 + i) | (g << 16);
   __syncthreads();
   return total;
+}
+
+// The work list, built once per call: wl[0] = entry count, wl[1 + i] = entry i.
+__global__ void __launch_bounds__(DEC_NT) k_decode_prep(const int32_t* offsets, int E, int32_t* wl) {
+  __shared__ int list[4 * 1024];
+  __shared__ int red[8];
+  const int n = build_group_list(offsets, E, list, red);
+  for (int i = threadIdx.x; i < n; i += DEC_NT) wl[1 + i] = list[i];
+  if (threadIdx.x == 0) wl[0] = n;
 }
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -70,13 +80,9 @@ struct WaveStream {
     dst[1] = ldg_nt(q + 1);
   }
   static __device__ __forceinline__ void load_x(const uint16_t* x, int ks, uint4 (&dst)[2]) {
-    if (x) {
-      const uint4* q = reinterpret_cast<const uint4*>(x + ks * 64);
-      dst[0] = q[0];
-      dst[1] = q[1];
-    } else {
-      dst[0] = dst[1] = make_uint4(0, 0, 0, 0);
-    }
+    const uint4* q = reinterpret_cast<const uint4*>(x + ks * 64);
+    dst[0] = q[0];
+    dst[1] = q[1];
   }
 };
 
@@ -87,158 +93,141 @@ __device__ __forceinline__ f32x4 mfma2(const uint4 (&a)[2], const uint4 (&b)[2],
 
 constexpr int DEC_PF = 4;
 
-// gate/up + SwiGLU: unit = (expert, 16 intermediate columns), one wave.
+// Runs step(s) for k-steps 0..n-1 (step kk uses buffer kk % DEC_PF) with the
+// loads of step kk + DEC_PF issued right after step kk.  When n is a multiple
+// of DEC_PF the steady state has no conditional load, so the in-order vmcnt
+// waits the compiler places before each step leave the later buffers in flight
+// (a conditional issue makes it wait for every outstanding load instead).
+template <class Load, class Step>
+__device__ __forceinline__ void stream_steps(int n, Load load, Step step) {
+  if (n >= DEC_PF && n % DEC_PF == 0) {
+#pragma unroll
+    for (int s = 0; s < DEC_PF; ++s) load(s, s);
+    for (int ks = 0; ks < n - DEC_PF; ks += DEC_PF) {
+#pragma unroll
+      for (int s = 0; s < DEC_PF; ++s) {
+        step(s);
+        load(ks + s + DEC_PF, s);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < DEC_PF; ++s) step(s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < DEC_PF; ++s)
+      if (s < n) load(s, s);
+    for (int ks = 0; ks < n; ks += DEC_PF) {
+#pragma unroll
+      for (int s = 0; s < DEC_PF; ++s) {
+        if (ks + s < n) {
+          step(s);
+          if (ks + s + DEC_PF < n) load(ks + s + DEC_PF, s);
+        }
+      }
+    }
+  }
+}
+
+// Every unit covers one group of up to 16 rows of one expert (lane & 15 is
+// the row); lanes past the expert's last row read a valid row (the last one)
+// and their output columns are not stored, so no load is predicated and the
+// weight prefetch is never drained by a divergent branch.
+
+// gate/up + SwiGLU: one workgroup per unit (expert, row group, 16 intermediate
+// columns); its 4 waves split the contraction axis in 4 and their partial sums
+// are added through LDS in wave order before the epilogue.
 __global__ void __launch_bounds__(DEC_NT) k_decode_gateup(const GemmArgs p) {
-  __shared__ int list[1024];
-  __shared__ int red[8];
+  __shared__ f32x4 part[DEC_NT / 64 - 1][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nact = build_active_list(p.offsets, p.E, list, red);
   const int slabs = p.I / 16;
-  const int units = nact * slabs;
+  const int u = blockIdx.x;
+  if (u >= p.wlist[0] * slabs) return;                 // whole workgroup: no unit
+  const int ent = p.wlist[1 + u / slabs];
+  const int e = ent & 0xffff, g = ent >> 16;
+  const int i0 = (u % slabs) * 16;
+  const int r0 = p.offsets[e] + g * 16, n = min(p.offsets[e + 1] - r0, 16);
   const int ksteps = p.H / 64;
-  for (int u = blockIdx.x * 4 + wave; u < units; u += gridDim.x * 4) {
-    const int e = list[u / slabs];
-    const int i0 = (u % slabs) * 16;
-    const int r0 = p.offsets[e], n = p.offsets[e + 1] - r0;
-    const int ngroups = (n + 15) >> 4;
-    const size_t wrow = ((size_t)e * p.I + i0 + (lane & 15)) * p.H + (lane >> 4) * 16;
-    const uint16_t* wg = p.Wg_t + wrow;
-    const uint16_t* wu = p.Wu_t + wrow;
-    const uint16_t* xr[DEC_GROUPS];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int k_lo = wave_u * ksteps / 4, nks = (wave_u + 1) * ksteps / 4 - k_lo;
+  const size_t wrow = ((size_t)e * p.I + i0 + (lane & 15)) * p.H + (lane >> 4) * 16 + (size_t)k_lo * 64;
+  const uint16_t* wg = p.Wg_t + wrow;
+  const uint16_t* wu = p.Wu_t + wrow;
+  const int t = min(lane & 15, n - 1);
+  const uint16_t* xr = p.X + (size_t)p.row_token[r0 + t] * p.H + (lane >> 4) * 16 + (size_t)k_lo * 64;
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  uint4 bg[DEC_PF][2], bu[DEC_PF][2], bx[DEC_PF][2];
+  auto load = [&](int kk, int s) {
+    WaveStream<DEC_PF>::load(wg, kk, bg[s]);
+    WaveStream<DEC_PF>::load(wu, kk, bu[s]);
+    WaveStream<DEC_PF>::load_x(xr, kk, bx[s]);
+  };
+  auto step = [&](int s) {
+    ag = mfma2(bg[s], bx[s], ag);
+    au = mfma2(bu[s], bx[s], au);
+  };
+  stream_steps(nks, load, step);
+  if (wave > 0) {
+    part[wave - 1][0][lane] = ag;
+    part[wave - 1][1][lane] = au;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // D layout: lane holds row (lane & 15), features 4 * (lane >> 4) + v
+  if ((lane & 15) < n) {
 #pragma unroll
-    for (int g = 0; g < DEC_GROUPS; ++g) {
-      int t = g * 16 + (lane & 15);
-      xr[g] = (t < n) ? p.X + (size_t)p.row_token[r0 + t] * p.H + (lane >> 4) * 16 : nullptr;
+    for (int w = 0; w < DEC_NT / 64 - 1; ++w) {
+      ag += part[w][0][lane];
+      au += part[w][1][lane];
     }
-    f32x4 ag[DEC_GROUPS], au[DEC_GROUPS];
+    float h[4];
 #pragma unroll
-    for (int g = 0; g < DEC_GROUPS; ++g) ag[g] = au[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 bg[DEC_PF][2], bu[DEC_PF][2], bx[DEC_PF][2];
-#pragma unroll
-    for (int s = 0; s < DEC_PF; ++s) {
-      if (s < ksteps) {
-        WaveStream<DEC_PF>::load(wg, s, bg[s]);
-        WaveStream<DEC_PF>::load(wu, s, bu[s]);
-        WaveStream<DEC_PF>::load_x(xr[0], s, bx[s]);
-      }
-    }
-    for (int ks = 0; ks < ksteps; ks += DEC_PF) {
-#pragma unroll
-      for (int s = 0; s < DEC_PF; ++s) {
-        const int kk = ks + s;
-        if (kk < ksteps) {
-          ag[0] = mfma2(bg[s], bx[s], ag[0]);
-          au[0] = mfma2(bu[s], bx[s], au[0]);
-#pragma unroll
-          for (int g = 1; g < DEC_GROUPS; ++g) {
-            if (g < ngroups) {
-              uint4 x[2];
-              WaveStream<DEC_PF>::load_x(xr[g], kk, x);
-              ag[g] = mfma2(bg[s], x, ag[g]);
-              au[g] = mfma2(bu[s], x, au[g]);
-            }
-          }
-          const int nk = kk + DEC_PF;
-          if (nk < ksteps) {
-            WaveStream<DEC_PF>::load(wg, nk, bg[s]);
-            WaveStream<DEC_PF>::load(wu, nk, bu[s]);
-            WaveStream<DEC_PF>::load_x(xr[0], nk, bx[s]);
-          }
-        }
-      }
-    }
-    // D layout: lane holds token (lane & 15), features 4 * (lane >> 4) + v
-#pragma unroll
-    for (int g = 0; g < DEC_GROUPS; ++g) {
-      const int row = g * 16 + (lane & 15);
-      if (g < ngroups && row < n) {
-        float h[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) h[v] = silu_f32(ag[g][v]) * au[g][v];
-        store_bf16x4(p.Hrows + (size_t)(r0 + row) * p.I + i0 + 4 * (lane >> 4), h[0], h[1], h[2], h[3]);
-      }
-    }
+    for (int v = 0; v < 4; ++v) h[v] = silu_f32(ag[v]) * au[v];
+    store_bf16x4(p.Hrows + (size_t)(r0 + (lane & 15)) * p.I + i0 + 4 * (lane >> 4), h[0], h[1], h[2], h[3]);
   }
 }
 
-// down: unit = (expert, 16 hidden columns), one wave, whole intermediate axis.
+// down: one workgroup per (expert, row group, 64 hidden columns), one wave per
+// 16 columns over the whole intermediate axis.
 __global__ void __launch_bounds__(DEC_NT) k_decode_down(const GemmArgs p) {
-  __shared__ int list[1024];
-  __shared__ int red[8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nact = build_active_list(p.offsets, p.E, list, red);
-  const int slabs = p.H / 16;
-  const int units = nact * slabs;
+  const int slabs = p.H / 64;
+  const int u = blockIdx.x;
+  if (u >= p.wlist[0] * slabs) return;
+  const int ent = p.wlist[1 + u / slabs];
+  const int e = ent & 0xffff, g = ent >> 16;
+  const int h0 = (u % slabs) * 64 + wave * 16;
+  const int r0 = p.offsets[e] + g * 16, n = min(p.offsets[e + 1] - r0, 16);
   const int ksteps = p.I / 64;
-  for (int u = blockIdx.x * 4 + wave; u < units; u += gridDim.x * 4) {
-    const int e = list[u / slabs];
-    const int h0 = (u % slabs) * 16;
-    const int r0 = p.offsets[e], n = p.offsets[e + 1] - r0;
-    const int ngroups = (n + 15) >> 4;
-    const uint16_t* wd = p.Wd_t + ((size_t)e * p.H + h0 + (lane & 15)) * p.I + (lane >> 4) * 16;
-    const uint16_t* hr[DEC_GROUPS];
-#pragma unroll
-    for (int g = 0; g < DEC_GROUPS; ++g) {
-      int t = g * 16 + (lane & 15);
-      hr[g] = (t < n) ? p.Hrows + (size_t)(r0 + t) * p.I + (lane >> 4) * 16 : nullptr;
-    }
-    f32x4 acc[DEC_GROUPS];
-#pragma unroll
-    for (int g = 0; g < DEC_GROUPS; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 bw[DEC_PF][2], bx[DEC_PF][2];
-#pragma unroll
-    for (int s = 0; s < DEC_PF; ++s) {
-      if (s < ksteps) {
-        WaveStream<DEC_PF>::load(wd, s, bw[s]);
-        WaveStream<DEC_PF>::load_x(hr[0], s, bx[s]);
-      }
-    }
-    for (int ks = 0; ks < ksteps; ks += DEC_PF) {
-#pragma unroll
-      for (int s = 0; s < DEC_PF; ++s) {
-        const int kk = ks + s;
-        if (kk < ksteps) {
-          acc[0] = mfma2(bw[s], bx[s], acc[0]);
-#pragma unroll
-          for (int g = 1; g < DEC_GROUPS; ++g) {
-            if (g < ngroups) {
-              uint4 x[2];
-              WaveStream<DEC_PF>::load_x(hr[g], kk, x);
-              acc[g] = mfma2(bw[s], x, acc[g]);
-            }
-          }
-          const int nk = kk + DEC_PF;
-          if (nk < ksteps) {
-            WaveStream<DEC_PF>::load(wd, nk, bw[s]);
-            WaveStream<DEC_PF>::load_x(hr[0], nk, bx[s]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < DEC_GROUPS; ++g) {
-      const int row = g * 16 + (lane & 15);
-      if (g < ngroups && row < n)
-        store_bf16x4(p.Orows + (size_t)(r0 + row) * p.H + h0 + 4 * (lane >> 4), acc[g][0], acc[g][1], acc[g][2],
-                     acc[g][3]);
-    }
-  }
+  const uint16_t* wd = p.Wd_t + ((size_t)e * p.H + h0 + (lane & 15)) * p.I + (lane >> 4) * 16;
+  const uint16_t* hr = p.Hrows + (size_t)(r0 + min(lane & 15, n - 1)) * p.I + (lane >> 4) * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint4 bw[DEC_PF][2], bx[DEC_PF][2];
+  auto load = [&](int kk, int s) {
+    WaveStream<DEC_PF>::load(wd, kk, bw[s]);
+    WaveStream<DEC_PF>::load_x(hr, kk, bx[s]);
+  };
+  auto step = [&](int s) { acc = mfma2(bw[s], bx[s], acc); };
+  stream_steps(ksteps, load, step);
+  if ((lane & 15) < n)
+    store_bf16x4(p.Orows + (size_t)(r0 + (lane & 15)) * p.H + h0 + 4 * (lane >> 4), acc[0], acc[1], acc[2], acc[3]);
 }
 
-// Blocks of 4 waves; up to 8 blocks per CU resident, one pass over the units.
-static int decode_grid(long wave_units_upper) {
-  long blocks = (wave_units_upper + 3) / 4;
-  long cap = (long)num_cus() * 8;
-  long g = blocks < cap ? blocks : cap;
-  return (int)(g < 1 ? 1 : g);
-}
+size_t decode_ws_bytes(int E) { return (size_t)(1 + 4 * E) * sizeof(int32_t); }
 
 hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s) {
-  long active_upper = (long)a.T * a.k < a.E ? (long)a.T * a.k : a.E;
-  hipLaunchKernelGGL(k_decode_gateup, dim3(decode_grid(active_upper * (a.I / 16))), dim3(DEC_NT), 0, s, a);
+  hipLaunchKernelGGL(k_decode_prep, dim3(1), dim3(DEC_NT), 0, s, a.offsets, a.E, a.wlist);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
+  // one workgroup per possible unit: at most min(T*k, E) experts with rows, and
+  // at most T*k / 16 + (experts with rows) row groups; workgroups past the real
+  // unit count exit at once
+  const long rows = (long)a.T * a.k;
+  const long experts = rows < a.E ? rows : a.E;
+  const long groups = rows / 16 + experts;
+  hipLaunchKernelGGL(k_decode_gateup, dim3((unsigned)(groups * (a.I / 16))), dim3(DEC_NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_down, dim3(decode_grid(active_upper * (a.H / 16))), dim3(DEC_NT), 0, s, a);
+  hipLaunchKernelGGL(k_decode_down, dim3((unsigned)(groups * (a.H / 64))), dim3(DEC_NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct GemmArgs {
   uint16_t* dWg;
   uint16_t* dWu;
   uint16_t* dWd;
+  int32_t* wlist;         // small-token path: work list in the workspace
 };
 
 int num_cus();
@@ -63,6 +64,8 @@ hipError_t launch_bwd_token_reduce(const GemmArgs& a, const int32_t* slot_row, u
 
 // small-token path: every expert has at most T <= DECODE_MAX_T rows
 constexpr int DECODE_MAX_T = 64;
+// workspace of the small-token path: the (expert, row group) work list
+size_t decode_ws_bytes(int E);
 hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s);
 
 // MXFP8 expert GEMMs

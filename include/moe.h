@@ -163,7 +163,9 @@ MOE_API moe_status moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8
  *          requantised to MXFP8 along I before the down projection
  *   H_rows         [T*k, I] bf16 out (h, bf16 in both modes)
  *   O_rows         [T*k, H] bf16 out
- *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_EXPERT_MLP)
+ *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_EXPERT_MLP): the MXFP8
+ *                  codes of X and h; for bf16 with T <= 64 a work list of 4E+1 int32
+ *                  (bf16 with T > 64 needs none)
  */
 MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token,
                                   const int32_t* expert_offsets, const void* Wg_t,
