@@ -41,6 +41,8 @@ int num_cus();
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         hipStream_t s);
 size_t dispatch_ws_bytes(long A, int E);
+// dispatch of T*k <= DISPATCH_SMALL_A slots runs in one workgroup
+constexpr int DISPATCH_SMALL_A = 4096;
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* offsets,
                            int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
                            int32_t* ws, hipStream_t s);

@@ -8,7 +8,7 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router: one wave per token.  Each lane keeps up to 16 logits (E <= 1024) in
+// Router: one wave per token.  Each lane keeps E/64 (up to 16) logits in
 // registers; k rounds of a wave arg-max pick the experts in descending logit
 // order, ties to the lowest index.  The weights are exp(l_j - l_max) over the
 // chosen logits, normalised by their sum (softmax over E renormalised over k).
@@ -55,15 +55,14 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
   return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
 }
 
-__global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits, int T, int E, int k,
-                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  uint64_t key[ROUTE_MAX_PER_LANE];
+// Routes one token with one wave, NPL logits per lane (E <= 64 NPL): writes
+// its k expert ids (descending logit) and renormalised weights.
+template <int NPL>
+__device__ __forceinline__ void route_token_n(const float* __restrict__ row, int E, int k, int lane,
+                                              int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  uint64_t key[NPL];
 #pragma unroll
-  for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+  for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     key[i] = (e < E) ? route_key(row[e], e) : 0ull;   // 0 sorts below every real key
   }
@@ -71,11 +70,11 @@ __global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits,
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) best = max_u64(best, key[i]);
+    for (int i = 0; i < NPL; ++i) best = max_u64(best, key[i]);
     const uint64_t top = wave_max_key(best);
     const int e = (int)~(uint32_t)top;
 #pragma unroll
-    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i)
+    for (int i = 0; i < NPL; ++i)
       if (lane + 64 * i == e) key[i] = 0ull;            // taken
     if (lane == j) mine = top;
   }
@@ -85,9 +84,27 @@ __global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits,
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
   if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = (int)~(uint32_t)mine;
-    topk_w[(size_t)t * k + lane] = ex / sum;
+    idx_out[lane] = (int)~(uint32_t)mine;
+    w_out[lane] = ex / sum;
   }
+}
+
+// The smallest logits-per-lane count that holds E (the per-round work scales with it).
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
+                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  if (E <= 64) route_token_n<1>(row, E, k, lane, idx_out, w_out);
+  else if (E <= 128) route_token_n<2>(row, E, k, lane, idx_out, w_out);
+  else if (E <= 256) route_token_n<4>(row, E, k, lane, idx_out, w_out);
+  else if (E <= 512) route_token_n<8>(row, E, k, lane, idx_out, w_out);
+  else route_token_n<ROUTE_MAX_PER_LANE>(row, E, k, lane, idx_out, w_out);
+}
+
+__global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits, int T, int E, int k,
+                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
@@ -254,9 +271,91 @@ __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dispatch of a small batch (T*k <= DISPATCH_SMALL_A) in one workgroup of 16
+// waves and one launch: the same histogram / scan / stable scatter as
+// k_dispatch_count + k_dispatch_scatter, with each wave owning a contiguous
+// run of slots and its histogram row in LDS.
+// ---------------------------------------------------------------------------
+constexpr int DS_WAVES = 16;
+
+__global__ void __launch_bounds__(64 * DS_WAVES) k_dispatch_small(
+    const int32_t* __restrict__ idx, int A, int E, int k, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot, int32_t* __restrict__ slot_row) {
+  __shared__ int hist[DS_WAVES][DISPATCH_MAX_E];
+  __shared__ int red[DS_WAVES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < DS_WAVES * DISPATCH_MAX_E; i += 64 * DS_WAVES) (&hist[0][0])[i] = 0;
+  const int per = ((A + DS_WAVES - 1) / DS_WAVES + 63) / 64 * 64;     // slots per wave, whole groups of 64
+  const int s0 = wave * per;
+  int ids[DISPATCH_SMALL_A / DS_WAVES / 64];
+#pragma unroll
+  for (int g = 0; g < DISPATCH_SMALL_A / DS_WAVES / 64; ++g) {
+    const int s = s0 + g * 64 + lane;
+    int e = (g * 64 < per && s < A) ? idx[s] : -1;
+    ids[g] = (e >= 0 && e < E) ? e : 0x400;                           // out-of-range ids are skipped
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < DISPATCH_SMALL_A / DS_WAVES / 64; ++g) {
+    const int key = ids[g];
+    const uint64_t m = match_key(key);
+    if (key < 0x400 && (m >> lane) == 1ull) hist[wave][key] += __popcll(m);
+  }
+  __syncthreads();
+  // thread e: total of expert e, exclusive scan over experts, per-wave bases
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int w = 0; w < DS_WAVES; ++w) tot += hist[w][e];
+  int x = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int ex = x - tot;
+  for (int w = 0; w < wave; ++w) ex += red[w];
+  if (e < E) {
+    offsets[e] = ex;
+    if (e == E - 1) offsets[E] = ex + tot;
+    int run = ex;
+    for (int w = 0; w < DS_WAVES; ++w) {
+      const int c = hist[w][e];
+      hist[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // stable scatter of this wave's slots
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int g = 0; g < DISPATCH_SMALL_A / DS_WAVES / 64; ++g) {
+    const int s = s0 + g * 64 + lane;
+    const int key = ids[g];
+    const uint64_t m = match_key(key);
+    if (key < 0x400) {
+      const int pos = hist[wave][key] + __popcll(m & below);
+      row_token[pos] = s / k;
+      row_slot[pos] = s;
+      slot_row[s] = pos;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (key < 0x400 && (m >> lane) == 1ull) hist[wave][key] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* row_token,
                            int32_t* row_slot, int32_t* slot_row, int32_t* ws, hipStream_t s) {
   long A = (long)T * k;
+  if (A > 0 && A <= DISPATCH_SMALL_A) {
+    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(64 * DS_WAVES), 0, s, idx, (int)A, E, k, offsets, row_token,
+                       row_slot, slot_row);
+    return hipGetLastError();
+  }
   int nchunks = (int)((A + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK);
   if (nchunks < 1) nchunks = 1;  // block 0 still writes the offsets when there are no slots
   hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, A, E, nchunks * 4, ws);

@@ -59,6 +59,32 @@ def test_route_and_dispatch_bit_exact(name):
         assert np.array_equal(g.cpu().numpy(), r), n
 
 
+@pytest.mark.parametrize("name,T,E,k", [("tiny", 64, 8, 2), ("decode", 32, 256, 8), ("decode", 512, 256, 8),
+                                         ("decode", 513, 256, 8), ("large_mxfp8", 409, 512, 10),
+                                         ("ties", 97, 1024, 32), ("ties", 1, 3, 3), ("ties", 200, 100, 5)])
+def test_route_dispatch_shapes_bit_exact(name, T, E, k):
+    """Every logits-per-lane width of the router (E up to 64, 128, 256, 512,
+    1024) and both dispatch paths: one workgroup for T*k <= 4096 (all but the
+    513-token case), two-stage otherwise."""
+    B = _B()
+    _say("route+dispatch", name, T, E, k)
+    if name == "ties":
+        logits = np.random.default_rng(T).integers(-3, 4, (T, E)).astype(np.float32)
+        logits[0, ::3] = -0.0
+    else:
+        cfg = wl.config(name)
+        logits = np.ascontiguousarray(wl.make_logits(cfg)[:T, :E]) if T <= cfg.T else \
+            np.random.default_rng(T).standard_normal((T, E)).astype(np.float32)
+    idx, w = B.route(torch.from_numpy(logits).cuda(), k)
+    ridx, rw = orc.route(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.all(np.abs(w.cpu().numpy().astype(np.float64) - rw) <= 1e-6 + 1e-5 * np.abs(rw))
+    got = B.dispatch(idx, E)
+    ref = orc.dispatch(ridx, E)
+    for g, r, n in zip(got, ref, ("offsets", "row_token", "row_slot", "slot_row")):
+        assert np.array_equal(g.cpu().numpy(), r), n
+
+
 def test_route_ties_and_signed_zeros():
     B = _B()
     _say("route ties")
