@@ -2,170 +2,204 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and one E8M0 scale per
 // 32 contraction elements of every row (OCP Microscaling v1.0).
 //
-// Same persistent schedule, tile shape and LDS layout as the bf16 kernels: a
-// 128-byte LDS row now holds 128 E4M3 codes (one k-tile), next to one 32-bit
-// word per row holding the row's four scale bytes of that k-tile.
+// Same persistent row-group schedule, tile shape (256 x 256, 8 waves of
+// 128 x 64) and direct global->LDS loads as the bf16 row GEMMs: a k-tile is
+// 128 E4M3 codes, i.e. one 128-byte LDS row per tile row, exactly the bytes of
+// a bf16 k-tile of 64, so the loader and the chunk swizzle are shared (the code
+// arrays are addressed as 16-bit words).  Next to the data, each stage holds
+// one 32-bit word per tile row with the row's four scale bytes of the k-tile,
+// loaded by one dword-per-lane direct load per wave.
 //
 // Operand layout of the scaled MFMA (verified on the device): for a 64-long
 // k chunk, lane half h (= lane / 32) supplies bytes [16h, 16h+16) and
 // [32+16h, 32+16h+16) of its row, and its scale operand applies to the
 // 32-element block [32h, 32h+32).  So MFMA kk of a k-tile reads 16-byte chunks
 // 4kk+h and 4kk+2+h and scale byte 2kk+h.
-#include "grouped_gemm.h"
+#include "gemm_rows.h"
 #include "kernels.h"
 
 namespace moe {
 
-using CfgMx = TileCfg<256, 256, 2, 2>;
-constexpr int BKB = 128;                 // fp8 codes (bytes) per k-tile
-constexpr uint32_t SCALE_ONE = 0x7f7f7f7fu;
+// 256 x 256 tiles, k-tiles of 64 16-bit words (128 E4M3 codes), two stages
+using CfgMx = RowCfg<256, 256, 2, 4, 64, 2>;
 
-// K-contiguous rows of E4M3 codes and their E8M0 scales.  Src::rows(p, t, row, data, scales)
-// sets data (element k = 0 of the row) and scales (its first scale byte), or leaves them null
-// for a row of zeros.
-template <int ROWS, int NT, class Src>
-struct KRowsMx {
-  static constexpr int CHUNKS = ROWS * 8;
-  static constexpr int PER = (CHUNKS + NT - 1) / NT;
-  static constexpr int SPER = (ROWS + NT - 1) / NT;
-  const uint8_t* ptr[PER];
-  uint4 reg[PER];
-  const uint8_t* sptr[SPER];
-  uint32_t sreg[SPER];
+__device__ __forceinline__ int mx_clamp_row(const Tile& t, int row) { return min(t.m0 + row, t.m_end - 1); }
 
-  __device__ void init(const MxArgs& p, const Tile& tl) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NT;
-      const uint8_t *d = nullptr, *s = nullptr;
-      if (c < CHUNKS) Src::rows(p, tl, c >> 3, d, s);
-      ptr[i] = d ? d + (c & 7) * 16 : nullptr;
-    }
-#pragma unroll
-    for (int i = 0; i < SPER; ++i) {
-      const int r = threadIdx.x + i * NT;
-      const uint8_t *d = nullptr, *s = nullptr;
-      if (r < ROWS) Src::rows(p, tl, r, d, s);
-      sptr[i] = d ? s : nullptr;
-    }
+// Data sources (codes seen as 16-bit words: k0 and offsets count words) and the
+// byte address of each row's first scale (scale k-tile kt is 4 bytes further per kt).
+struct MxSrcX {        // gathered token rows of the quantised X
+  __device__ static const uint16_t* base(const MxArgs& p, const Tile&, int, int k0) {
+    return reinterpret_cast<const uint16_t*>(p.Xq) + k0;
   }
-  __device__ void load(int k0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      reg[i] = ptr[i] ? *reinterpret_cast<const uint4*>(ptr[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < SPER; ++i)
-      sreg[i] = sptr[i] ? *reinterpret_cast<const uint32_t*>(sptr[i] + k0 / 32) : SCALE_ONE;
+  __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)p.row_token[mx_clamp_row(t, row)] * (uint32_t)(p.H / 2);
   }
-  __device__ void store(uint4* lds, uint32_t* lds_s) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NT;
-      if (c < CHUNKS) lds[lds_chunk(c >> 3, c & 7)] = reg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < SPER; ++i) {
-      const int r = threadIdx.x + i * NT;
-      if (r < ROWS) lds_s[r] = sreg[i];
-    }
+  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
+    return p.Xs + (size_t)p.row_token[mx_clamp_row(t, row)] * (p.H / 32);
   }
 };
-
-struct SrcMxX {  // gathered token rows of the quantised X
-  __device__ static void rows(const MxArgs& p, const Tile& t, int row, const uint8_t*& d, const uint8_t*& s) {
-    const int r = t.m0 + row;
-    if (r < t.m_end) {
-      const size_t tok = (size_t)p.row_token[r];
-      d = p.Xq + tok * p.H;
-      s = p.Xs + tok * (p.H / 32);
-    }
-  }
-};
+// Packed gate / up codes [E, I, H], interleaved like the bf16 gate/up B tile:
+// inside every 32-row MFMA fragment rows 0-15 are gate and rows 16-31 the up
+// rows of the same 16 intermediate columns.
 template <class C>
-struct SrcMxGateUpW {  // packed [E, I, H] gate / up codes, interleaved per wave column group
-  __device__ static void rows(const MxArgs& p, const Tile& t, int rr, const uint8_t*& d, const uint8_t*& s) {
-    constexpr int half = C::WTN / 2;
-    const int g = rr / C::WTN, within = rr % C::WTN;
-    const bool up = within >= half;
-    const int col = t.nt * (C::BN / 2) + g * half + (within % half);
-    if (col < p.I) {
-      const size_t row = (size_t)t.e * p.I + col;
-      d = (up ? p.Wu : p.Wg) + row * p.H;
-      s = (up ? p.Su : p.Sg) + row * (p.H / 32);
-    }
+struct MxSrcGateUpW {
+  __device__ static int col(const MxArgs& p, const Tile& t, int row) {
+    return min(t.nt * (C::BN / 2) + (row / 32) * 16 + (row % 16), p.I - 1);
+  }
+  __device__ static const uint16_t* base(const MxArgs& p, const Tile& t, int row0, int k0) {
+    const bool up = (row0 % 32) >= 16;
+    return reinterpret_cast<const uint16_t*>(up ? p.Wu : p.Wg) + (size_t)t.e * p.I * (p.H / 2) + k0;
+  }
+  __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)col(p, t, row) * (uint32_t)(p.H / 2);
+  }
+  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
+    const bool up = (row % 32) >= 16;
+    return (up ? p.Su : p.Sg) + ((size_t)t.e * p.I + col(p, t, row)) * (p.H / 32);
   }
 };
-struct SrcMxH {  // expert-major quantised h rows
-  __device__ static void rows(const MxArgs& p, const Tile& t, int row, const uint8_t*& d, const uint8_t*& s) {
-    const int r = t.m0 + row;
-    if (r < t.m_end) {
-      d = p.Hq + (size_t)r * p.I;
-      s = p.Hs + (size_t)r * (p.I / 32);
-    }
+struct MxSrcH {        // expert-major quantised h rows
+  __device__ static const uint16_t* base(const MxArgs& p, const Tile&, int, int k0) {
+    return reinterpret_cast<const uint16_t*>(p.Hq) + k0;
+  }
+  __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)mx_clamp_row(t, row) * (uint32_t)(p.I / 2);
+  }
+  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
+    return p.Hs + (size_t)mx_clamp_row(t, row) * (p.I / 32);
   }
 };
-struct SrcMxDownW {  // packed [E, H, I] down codes
-  __device__ static void rows(const MxArgs& p, const Tile& t, int rr, const uint8_t*& d, const uint8_t*& s) {
-    const int n = t.n0 + rr;
-    if (n < p.H) {
-      const size_t row = (size_t)t.e * p.H + n;
-      d = p.Wd + row * p.I;
-      s = p.Sd + row * (p.I / 32);
-    }
+struct MxSrcDownW {    // packed down codes [E, H, I]
+  __device__ static const uint16_t* base(const MxArgs& p, const Tile& t, int, int k0) {
+    return reinterpret_cast<const uint16_t*>(p.Wd) + (size_t)t.e * p.H * (p.I / 2) + k0;
+  }
+  __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)(p.I / 2);
+  }
+  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
+    return p.Sd + ((size_t)t.e * p.H + min(t.n0 + row, p.H - 1)) * (p.I / 32);
   }
 };
 
+// Scale words of the tile rows: 4 dword loads of 64 lanes per operand; wave w
+// of group g (waves 0-3: A, 4-7: B) loads rows 64 w .. 64 w + 63 of its operand.
+struct MxScaleRows {
+  const uint8_t* ptr;
+  template <class SrcA, class SrcB>
+  __device__ void init(const MxArgs& p, const Tile& tl, int wave) {
+    const int row = (wave & 3) * 64 + (threadIdx.x & 63);
+    ptr = wave < 4 ? SrcA::scales(p, tl, row) : SrcB::scales(p, tl, row);
+  }
+  // this wave's 64 scale words of k-tile kt into lds (the operand's word array)
+  __device__ void issue(int kt, uint32_t* lds, int wave) const {
+    const uint8_t* a = ptr + (size_t)kt * 4;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(a), "s"(lds_addr(lds + (wave & 3) * 64))
+                 : "m0");
+  }
+};
+
+// Byte offset of this lane's chunk 4kk + h of its row, for kk = 0 (chunk c of
+// row r is at c ^ swz(r); chunk 4kk + 2 + h is at this ^ 32, kk = 1 at ^ 64).
 template <class C>
-__device__ __forceinline__ void mma_ktile_mx(const uint4* As, const uint32_t* As_s, const uint4* Bs,
-                                             const uint32_t* Bs_s, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
-                                             int lane) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    i32x8 a[C::FM], b[C::FN];
-    int sa[C::FM], sb[C::FN];
+struct MxFragAddr {
+  uint32_t a[C::FM], b[C::FN];
+  int ra, rb;                 // tile rows of fragment 0 (fragment f: + 32 f), for the scale words
+  __device__ void init(int wm, int wn, int lane) {
+    const int h = lane >> 5;
+    ra = wm * C::WTM + (lane & 31);
+    rb = wn * C::WTN + (lane & 31);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
-      const int row = wm * C::WTM + fm * 32 + (lane & 31);
-      const uint4 lo = As[lds_chunk(row, 4 * kk + h)], hi = As[lds_chunk(row, 4 * kk + 2 + h)];
-      a[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sa[fm] = (int)((As_s[row] >> (8 * (2 * kk + h))) & 0xffu);
+      const int r = ra + fm * 32;
+      a[fm] = (uint32_t)(r * C::CPR + (swz<C::CPR>(r) ^ h)) * 16u;
     }
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int row = wn * C::WTN + fn * 32 + (lane & 31);
-      const uint4 lo = Bs[lds_chunk(row, 4 * kk + h)], hi = Bs[lds_chunk(row, 4 * kk + 2 + h)];
-      b[fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sb[fn] = (int)((Bs_s[row] >> (8 * (2 * kk + h))) & 0xffu);
+      const int r = rb + fn * 32;
+      b[fn] = (uint32_t)(C::A_SLOTS + r * C::CPR + (swz<C::CPR>(r) ^ h)) * 16u;
     }
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[fn], a[fm], acc[fm][fn], 0, 0, 0, sb[fn],
-                                                                     0, sa[fm]);
   }
+};
+
+__device__ __forceinline__ i32x8 mx_operand(const uint8_t* stage, uint32_t off, int kk) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(stage + (off ^ (64u * kk)));
+  const uint4 hi = *reinterpret_cast<const uint4*>(stage + (off ^ (64u * kk + 32u)));
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Shared body: RowGroups schedule over the expert rows, two-stage LDS ring.
+// One k-tile: two 64-wide MFMA steps, each over both B fragments and the A
+// fragments two at a time; with LOADS the NLOAD direct loads of the next
+// k-tile (issue(j)) are issued with the first step.
+template <class C, bool LOADS, int NLOAD, class Issue>
+__device__ __forceinline__ void mma_ktile_mx(const uint8_t* stage, const uint32_t* sA, const uint32_t* sB,
+                                             const MxFragAddr<C>& fa, f32x16 (&acc)[C::FM][C::FN], int lane,
+                                             Issue issue) {
+  const int h = lane >> 5;
+  uint32_t wa[C::FM], wb[C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) wa[fm] = sA[fa.ra + 32 * fm];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) wb[fn] = sB[fa.rb + 32 * fn];
+  static_for<0, 2>([&](auto kkc) {
+    constexpr int kk = decltype(kkc)::value;
+    const int sh = 8 * (2 * kk + h);
+    i32x8 b[C::FN];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) b[fn] = mx_operand(stage, fa.b[fn], kk);
+    if constexpr (LOADS && kk == 0) static_for<0, NLOAD>([&](auto jc) { issue(decltype(jc)::value); });
+    static_for<0, C::FM / 2>([&](auto pc) {
+      constexpr int f0 = 2 * decltype(pc)::value;
+      const i32x8 a0 = mx_operand(stage, fa.a[f0], kk), a1 = mx_operand(stage, fa.a[f0 + 1], kk);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int sbn = (int)((wb[fn] >> sh) & 0xffu);
+        acc[f0][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[fn], a0, acc[f0][fn], 0, 0, 0, sbn, 0,
+                                                                      (int)((wa[f0] >> sh) & 0xffu));
+        acc[f0 + 1][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            b[fn], a1, acc[f0 + 1][fn], 0, 0, 0, sbn, 0, (int)((wa[f0 + 1] >> sh) & 0xffu));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
+// Persistent body (two stages; the bf16 row GEMM's pipeline with the scale
+// words added).  Waves 0-3 load the A scales, waves 4-7 the B scales.
 template <class C, class SrcA, class SrcB, class Epi>
-__device__ __forceinline__ void mx_gemm_body(const MxArgs& p, int N, int K) {
-  __shared__ uint4 smem[2 * (C::LDS_A + C::LDS_B)];
-  __shared__ uint32_t sscale[2 * (C::BM + C::BN)];
+__device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
+  __shared__ uint4 smem[2 * C::STAGE];
+  __shared__ uint32_t sscale[2][C::BM + C::BN];
   __shared__ int sched_lds[1024 + 1 + C::NT / 64 + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  using AL = DirectRows<C, C::BM, SrcA, MxArgs>;
+  using BL = DirectRows<C, C::BN, SrcB, MxArgs>;
+  constexpr int PERK = AL::PER + BL::PER + 1;             // data loads + one scale load per wave
+
   RowGroups<C::BM, C::BN, C::NT> sched;
-  sched.init(p.offsets, p.E, N, K, sched_lds, sched_lds + 1025);
+  sched.init(p.offsets, p.E, N, K / 2, sched_lds, sched_lds + 1025);   // K in 16-bit words
   XcdWalk walk;
   walk.init(sched.total);
-  for (; walk.valid(); walk.next()) {
-    const Tile tl = sched.tile(walk.t);
-    KRowsMx<C::BM, C::NT, SrcA> al;
-    KRowsMx<C::BN, C::NT, SrcB> bl;
+  if (!walk.valid()) return;
+  Tile tl = sched.tile(walk.t);
+  MxFragAddr<C> fa;
+  fa.init(wm, wn, lane);
+  AL al;
+  BL bl;
+  MxScaleRows sc;
+  auto init_loaders = [&]() {
     al.init(p, tl);
     bl.init(p, tl);
-    const int nk = K / BKB;
+    sc.init<SrcA, SrcB>(p, tl, wave);
+  };
+  auto issue_scales = [&](int kt, int st) { sc.issue(kt, &sscale[st][wave < 4 ? 0 : C::BM], wave); };
+  init_loaders();
+  int nk = (tl.k_hi - tl.k_lo) / C::BK;
+  al.issue(p, tl, 0, smem);
+  bl.issue(p, tl, 0, smem + C::A_SLOTS);
+  issue_scales(0, 0);
+  while (true) {
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -173,92 +207,79 @@ __device__ __forceinline__ void mx_gemm_body(const MxArgs& p, int N, int K) {
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
-    uint4* const As = smem;
-    uint4* const Bs = smem + 2 * C::LDS_A;
-    uint32_t* const As_s = sscale;
-    uint32_t* const Bs_s = sscale + 2 * C::BM;
-    al.load(0);
-    bl.load(0);
-    al.store(As, As_s);
-    bl.store(Bs, Bs_s);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        al.load((kt + 1) * BKB);
-        bl.load((kt + 1) * BKB);
-      }
-      mma_ktile_mx<C>(As + cur * C::LDS_A, As_s + cur * C::BM, Bs + cur * C::LDS_B, Bs_s + cur * C::BN, acc, wm,
-                      wn, lane);
-      if (kt + 1 < nk) {
-        al.store(As + (cur ^ 1) * C::LDS_A, As_s + (cur ^ 1) * C::BM);
-        bl.store(Bs + (cur ^ 1) * C::LDS_B, Bs_s + (cur ^ 1) * C::BN);
-      }
+    auto kstep = [&](int kt, auto loads) {
+      wait_vmcnt<0>();                                    // k-tile kt (and any earlier stores)
       __syncthreads();
+      const int nxt = kt + 1, ns = nxt & 1;
+      uint4* st = smem + ns * C::STAGE;
+      auto issue = [&](int j) {
+        if (j < AL::PER) al.issue_one(p, tl, nxt * C::BK, st, j);
+        else if (j < AL::PER + BL::PER) bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
+        else issue_scales(nxt, ns);
+      };
+      const int cs = kt & 1;
+      mma_ktile_mx<C, decltype(loads)::value, PERK>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE),
+                                                    &sscale[cs][0], &sscale[cs][C::BM], fa, acc, lane, issue);
+    };
+    int kt = 0;
+    for (; kt < nk - 1; ++kt) kstep(kt, std::true_type{});
+    kstep(kt, std::false_type{});
+    // every wave is past its last LDS read before any stage is refilled
+    __syncthreads();
+    const Tile done = tl;
+    walk.next();
+    const bool more = walk.valid();
+    if (more) {
+      // start the next tile's first k-tile, then run this tile's epilogue under it
+      tl = sched.tile(walk.t);
+      init_loaders();
+      nk = (tl.k_hi - tl.k_lo) / C::BK;
+      al.issue(p, tl, 0, smem);
+      bl.issue(p, tl, 0, smem + C::A_SLOTS);
+      issue_scales(0, 0);
     }
-    Epi::apply(p, tl, acc, wm, wn, lane);
+    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + C::STAGE) + wave * RowEpiLds<C>::BYTES;
+    Epi::apply(p, done, acc, wm, wn, lane, wave_lds);
+    if (!more) break;
+    // the scratch stage is the next tile's second stage: all waves must be done with it
+    __syncthreads();
   }
 }
 
 template <class C>
-struct MxSwiGLUEpi {  // h = bf16(silu(G) * U) -> Hrows
+struct MxSwiGLUEpi {  // h = bf16(silu(G) * U) -> Hrows (columns as in the bf16 gate/up GEMM)
   __device__ static void apply(const MxArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
-                               int lane) {
-    const int hcol0 = t.nt * (C::BN / 2) + wn * (C::WTN / 2) + (lane >> 5) * 4;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int r = t.m0 + Frag<C>::row(wm, fm, lane);
-      if (r >= t.m_end) continue;
-      uint16_t* out = p.Hrows + (size_t)r * p.I + hcol0;
-#pragma unroll
-      for (int fn = 0; fn < C::FN / 2; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (hcol0 + fn * 32 + q * 8 >= p.I) continue;
-          float h[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            h[j] = silu_f32(acc[fm][fn][4 * q + j]) * acc[fm][fn + C::FN / 2][4 * q + j];
-          store_bf16x4(out + fn * 32 + q * 8, h[0], h[1], h[2], h[3]);
-        }
-    }
+                               int lane, uint8_t* wlds) {
+    stage_store_bf16<C, C::FN * 16, 2>(
+        wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.nt * (C::BN / 2) + wn * C::FN * 16, p.I, lane,
+        [&](int fm, int fn, int q, int j) { return silu_f32(acc[fm][fn][4 * q + j]) * acc[fm][fn][4 * q + 8 + j]; },
+        [](int fn, int q) { return fn * 16 + q * 8; });
   }
 };
 
 template <class C>
 struct MxStoreOEpi {  // O = bf16(acc) -> Orows
   __device__ static void apply(const MxArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
-                               int lane) {
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int r = t.m0 + Frag<C>::row(wm, fm, lane);
-      if (r >= t.m_end) continue;
-      uint16_t* out = p.Orows + (size_t)r * p.H;
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = t.n0 + Frag<C>::col(wn, fn, q, lane);
-          if (n >= p.H) continue;
-          store_bf16x4(out + n, acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                       acc[fm][fn][4 * q + 3]);
-        }
-    }
+                               int lane, uint8_t* wlds) {
+    stage_store_bf16<C, C::WTN, 4>(
+        wlds, p.Orows, p.H, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.H, lane,
+        [&](int fm, int fn, int q, int j) { return acc[fm][fn][4 * q + j]; },
+        [](int fn, int q) { return fn * 32 + q * 8; });
   }
 };
 
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_gateup(const MxArgs p) {
-  mx_gemm_body<CfgMx, SrcMxX, SrcMxGateUpW<CfgMx>, MxSwiGLUEpi<CfgMx>>(p, 2 * p.I, p.H);
+  mx_rows_body<CfgMx, MxSrcX, MxSrcGateUpW<CfgMx>, MxSwiGLUEpi<CfgMx>>(p, 2 * p.I, p.H);
 }
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_down(const MxArgs p) {
-  mx_gemm_body<CfgMx, SrcMxH, SrcMxDownW, MxStoreOEpi<CfgMx>>(p, p.H, p.I);
+  mx_rows_body<CfgMx, MxSrcH, MxSrcDownW, MxStoreOEpi<CfgMx>>(p, p.H, p.I);
 }
 
 static int mx_grid(const MxArgs& a, int N) {
   long A = (long)a.T * a.k;
   long mt = A / CfgMx::BM + (a.E < A ? a.E : A) + 1;
   long tiles = mt * ((N + CfgMx::BN - 1) / CfgMx::BN);
-  long cap = (long)num_cus();
+  long cap = (long)num_cus();            // one ~136 KB-LDS block per CU
   long g = tiles < cap ? tiles : cap;
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
