@@ -270,6 +270,9 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   a.Hrows = (uint16_t*)w8;
   w8 += align_up(A * I * 2);
   a.dXr = (float*)w8;
+  // once dX is reduced, the weight-gradient operand rows reuse the dXr area
+  a.Xg = (uint16_t*)w8;
+  a.dO = (uint16_t*)(w8 + A * H * 2);
   w8 += align_up(A * H * 4);
   a.dwt_part = (float*)w8;
   a.dWg = (uint16_t*)dW_gate;
@@ -282,6 +285,7 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
     if (e == hipSuccess) e = moe::launch_bwd_recompute(a, st);
     if (e == hipSuccess) e = moe::launch_bwd_dx_rows(a, st);
     if (e == hipSuccess) e = moe::launch_bwd_token_reduce(a, slot_row, (uint16_t*)dX, d_topk_w, st);
+    if (e == hipSuccess) e = moe::launch_bwd_gather(a, st);
   }
   if (e == hipSuccess) e = moe::launch_bwd_dw_down(a, st);
   if (e == hipSuccess) e = moe::launch_bwd_dw_gateup(a, st);

@@ -38,14 +38,6 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 __device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
 
-// One 128-byte row of a 64-element bf16 k-tile is 8 chunks of 16 bytes.  The
-// chunk order is permuted per row so that the 32 rows one MFMA operand read
-// touches spread over all LDS banks, both for 8-lane and 16-lane phases of a
-// 128-bit read.
-__device__ __forceinline__ int lds_chunk(int row, int chunk) {
-  return row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7));
-}
-
 // 16-byte streaming load (nontemporal: data read once, keep it out of the way in the caches).
 __device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));

@@ -1,12 +1,11 @@
 // bf16 grouped GEMMs of the MoE layer: forward gate/up + SwiGLU, forward down,
-// and the five GEMMs of the backward.  See grouped_gemm.h for the template.
+// and the three row-grouped GEMMs of the backward (direct-to-LDS rows, gemm_rows.h).
 #include "gemm_rows.h"
 #include "grouped_gemm.h"
 #include "kernels.h"
 
 namespace moe {
 
-using CfgMain = TileCfg<256, 256, 2, 2>;          // weight-gradient GEMMs (register-transposed loads)
 #ifndef MOE_ROWS_WAVES_N
 #define MOE_ROWS_WAVES_N 4
 #endif
@@ -86,40 +85,6 @@ struct RSrcGateUpWT {    // [W_gate | W_up] [E, H, I] read as [E, N = H, K = 2I]
   __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
     return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
   }
-};
-
-// ------------------------------------------------------------------------
-// Operand sources
-// ------------------------------------------------------------------------
-// Row sources of the weight-gradient GEMMs (rows are the contraction index).
-struct MNSrcH {
-  static constexpr bool SCALED = false;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int) {
-    return p.Hrows + (size_t)r * p.I;
-  }
-  __device__ static float scale(const GemmArgs&, int) { return 1.f; }
-};
-struct MNSrcDO {  // dO = bf16(w * dY[token])
-  static constexpr bool SCALED = true;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int) {
-    return p.dY + (size_t)p.row_token[r] * p.H;
-  }
-  __device__ static float scale(const GemmArgs& p, int r) { return p.topk_w[p.row_slot[r]]; }
-};
-struct MNSrcX {
-  static constexpr bool SCALED = false;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int) {
-    return p.X + (size_t)p.row_token[r] * p.H;
-  }
-  __device__ static float scale(const GemmArgs&, int) { return 1.f; }
-};
-// [dg | du] rows: the bf16 values in the first pass, their bf16 remainders in the second.
-struct MNSrcDGU {
-  static constexpr bool SCALED = false;
-  __device__ static const uint16_t* row(const GemmArgs& p, const Tile&, int r, int phase) {
-    return (phase ? p.dGU_lo : p.dGU) + (size_t)r * 2 * p.I;
-  }
-  __device__ static float scale(const GemmArgs&, int) { return 1.f; }
 };
 
 // ------------------------------------------------------------------------
@@ -282,75 +247,6 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT> {
   }
 };
 
-template <class C, class SrcA, class SrcB>
-struct WgOpsBase {
-  static constexpr int PHASES = 1;
-  using Sched = WeightGrad<C::BM, C::BN, C::NT>;
-  using ALoad = MNRows<C::BM, C::NT, SrcA, GemmArgs>;
-  using BLoad = MNRows<C::BN, C::NT, SrcB, GemmArgs>;
-};
-
-// Weight-gradient tile store: out[e][m][n] for m < M (n already split by caller).
-template <class C>
-__device__ __forceinline__ void store_wg(uint16_t* out0, uint16_t* out1, int nsplit, int M, int N,
-                                         const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
-                                         int lane) {
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int m = t.m0 + Frag<C>::row(wm, fm, lane);
-    if (m >= M) continue;
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = t.n0 + Frag<C>::col(wn, fn, q, lane);
-        if (n >= N) continue;
-        uint16_t* dst = n < nsplit ? out0 + ((size_t)t.e * M + m) * nsplit + n
-                                   : out1 + ((size_t)t.e * M + m) * (N - nsplit) + (n - nsplit);
-        store_bf16x4(dst, acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                     acc[fm][fn][4 * q + 3]);
-      }
-  }
-}
-
-// dW_down[e] = sum_r h_r^T dO_r   ([I, H])
-template <class C>
-struct BwdDWDownOps : WgOpsBase<C, MNSrcH, MNSrcDO> {
-  using B = WgOpsBase<C, MNSrcH, MNSrcDO>;
-  __device__ static void init_sched(typename B::Sched& s, const GemmArgs& p, int*, int*) {
-    s.init(p.offsets, p.E, p.I, p.H);
-  }
-  __device__ static void init_loaders(typename B::ALoad& al, typename B::BLoad& bl, const GemmArgs& p,
-                                      const Tile& t) {
-    al.init(p, t, t.m0, p.I);
-    bl.init(p, t, t.n0, p.H);
-  }
-  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
-    store_wg<C>(p.dWd, p.dWd, p.H, p.I, p.H, t, acc, wm, wn, lane);
-  }
-};
-
-// [dW_gate | dW_up][e] = sum_r X_r^T [dg | du]_r   ([H, 2I] split at I)
-template <class C>
-struct BwdDWGateUpOps : WgOpsBase<C, MNSrcX, MNSrcDGU> {
-  using B = WgOpsBase<C, MNSrcX, MNSrcDGU>;
-  // dg and du enter as bf16 value + bf16 remainder: two passes over the rows
-  static constexpr int PHASES = 2;
-  __device__ static void init_sched(typename B::Sched& s, const GemmArgs& p, int*, int*) {
-    s.init(p.offsets, p.E, p.H, 2 * p.I);
-  }
-  __device__ static void init_loaders(typename B::ALoad& al, typename B::BLoad& bl, const GemmArgs& p,
-                                      const Tile& t) {
-    al.init(p, t, t.m0, p.H);
-    bl.init(p, t, t.n0, 2 * p.I);
-  }
-  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane) {
-    store_wg<C>(p.dWg, p.dWu, p.I, p.H, 2 * p.I, t, acc, wm, wn, lane);
-  }
-};
-
 // ------------------------------------------------------------------------
 // Kernels and launchers
 // ------------------------------------------------------------------------
@@ -358,18 +254,12 @@ struct BwdDWGateUpOps : WgOpsBase<C, MNSrcX, MNSrcDGU> {
   __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {          \
     rows_gemm_body<CfgRows, OPS<CfgRows>, GemmArgs>(p);                            \
   }
-#define MOE_WG_KERNEL(NAME, OPS)                                                   \
-  __global__ void __launch_bounds__(CfgMain::NT) NAME(const GemmArgs p) {          \
-    grouped_gemm_body<CfgMain, OPS<CfgMain>, GemmArgs>(p);                         \
-  }
 
 MOE_ROWS_KERNEL(k_fwd_gateup, FwdGateUpOps)
 MOE_ROWS_KERNEL(k_fwd_down, FwdDownOps)
 MOE_ROWS_KERNEL(k_bwd_p, BwdPOps)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
 MOE_ROWS_KERNEL(k_bwd_dx_rows, BwdDXOps)
-MOE_WG_KERNEL(k_bwd_dw_down, BwdDWDownOps)
-MOE_WG_KERNEL(k_bwd_dw_gateup, BwdDWGateUpOps)
 
 template <class C>
 static int row_grid(const GemmArgs& a, int N) {
@@ -380,14 +270,6 @@ static int row_grid(const GemmArgs& a, int N) {
   long g = tiles < cap ? tiles : cap;
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
-template <class C>
-static int wg_grid(const GemmArgs& a, int M, int N) {
-  long tiles = (long)a.E * ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
-  long cap = (long)num_cus();
-  long g = tiles < cap ? tiles : cap;
-  return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
-}
-
 hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_fwd_gateup, dim3(row_grid<CfgRows>(a, 2 * a.I)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
@@ -411,15 +293,6 @@ hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_bwd_dx_rows, dim3(row_grid<CfgRows>(a, a.H)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
-hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dw_down, dim3(wg_grid<CfgMain>(a, a.I, a.H)), dim3(CfgMain::NT), 0, s, a);
-  return hipGetLastError();
-}
-hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dw_gateup, dim3(wg_grid<CfgMain>(a, a.H, 2 * a.I)), dim3(CfgMain::NT), 0, s, a);
-  return hipGetLastError();
-}
-
 // dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials.
 __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, const int32_t* slot_row,
                                                           uint16_t* dX, float* dtw) {

@@ -1,0 +1,346 @@
+// Weight-gradient GEMMs of the MoE backward on gfx950 bf16 MFMA, and the row
+// gather that feeds them.  With the contraction running over the rows routed
+// to expert e (LigerCute, "Backward pass": the expert-weight gradients):
+//   dW_down[e]           = sum_r h_r^T dO_r                 [I, H]
+//   [dW_gate | dW_up][e] = sum_r x_r^T [dg | du]_r          [H, 2I]
+//
+// Both operands are "k-major": a k-tile is BK consecutive expert-major rows,
+// each contiguous along M (or N).  The rows are copied to LDS unchanged by the
+// direct global->LDS loads (one 16-byte chunk per lane), and the LDS transpose
+// read ds_read_b64_tr_b16 turns them into MFMA operands: within each 16-lane
+// group, lane i receives element i % 4 of the four-element pieces addressed by
+// lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4.  Pointing lane s of a group
+// at row kb + s / 4, columns c0 + 4 (s % 4) .. + 3 therefore gives lane i
+// column c0 + i of rows kb .. kb + 3 -- half of the eight k values a lane of
+// v_mfma_f32_32x32x16_bf16 holds.
+//
+// Rows past the end of an expert's segment in the last k-tile are loaded from
+// the segment's last row (a valid address); the B operand's copies of them are
+// then overwritten with zeros in LDS, so they add nothing.
+#include "gemm_rows.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// 256 x 256 output tiles, 8 waves (2 x 4), 64-row k-tiles, two LDS stages of 64 KB.
+using CfgWg = RowCfg<256, 256, 2, 4, 64, 2>;
+
+// Chunk position in a k-major LDS row: chunk c of row r sits at c ^ tr_swz(r).
+// The flip of chunk-index bits 1-3 by r mod 4 makes the four rows one transpose
+// read touches land in different banks, for both 16- and 32-lane LDS phases.
+__device__ __forceinline__ int tr_swz(int r) { return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0); }
+
+// Loader of one k-major operand: BK rows x COLS columns (cols [c0, c0 + COLS) of
+// the source rows).  Load instruction i of wave w fills LDS slots
+// [64 (i NW + w), + 64): rows RPI (i NW + w) + lane / CPR.
+template <class C, int COLS>
+struct KMajorLoad {
+  static constexpr int CPR = COLS / 8;                  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                  // rows per load instruction
+  static constexpr int INST = C::BK * CPR / 64;
+  static constexpr int PER = INST / C::NW;              // load instructions per wave and k-tile
+  static_assert(CPR >= 16 && 64 % CPR == 0, "row of 128..512 bf16 columns");
+  static_assert(INST % C::NW == 0 && (RPI * C::NW) % 4 == 0, "row mod 4 fixed per lane");
+  uint32_t colb;                                        // byte offset of this lane's chunk in a row
+  int rsub;
+
+  // c0: first column of the tile; ncols: columns of the source (a multiple of 8).
+  __device__ void init(int c0, int ncols) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsub = lane / CPR;
+    const int r = RPI * wave + rsub;                    // this lane's rows are r mod 4 for every i
+    const int chunk = (lane % CPR) ^ tr_swz(r);
+    colb = (uint32_t)min(c0 + chunk * 8, ncols - 8) * 2u;
+  }
+  // Load instruction i of the k-tile whose row 0 is at `rows` (ld bytes per row; rows
+  // past `last` are read from row `last`) into the operand's LDS area at `lds`.
+  __device__ void issue(const uint8_t* rows, uint32_t ld, int last, uint4* lds, int i) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (i * C::NW + wave) * 64;
+    const int r = min(S / CPR + rsub, last);
+    lds_dma16(rows, (uint32_t)r * ld + colb, lds_addr(lds + S));
+  }
+};
+
+// Byte offsets (in a stage) of this lane's transpose reads for sub-step 0, read 0;
+// sub-step kk, read j is at + (16 kk + 4 j) row strides.
+template <class C>
+struct TrFragAddr {
+  static constexpr uint32_t RA = C::BM * 2, RB = C::BN * 2;       // row strides in bytes
+  uint32_t a[C::FM], b[C::FN];
+  __device__ void init(int wm, int wn, int lane) {
+    const int s = lane & 15, g = lane >> 4;
+    const int r = 8 * (g >> 1) + (s >> 2);              // k row (lanes 32-63: k + 8)
+    const int sub = 2 * (g & 1) + ((s & 3) >> 1);       // chunk within the 32-column fragment
+    const uint32_t in = 8u * (s & 1);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int ch = (wm * C::WTM + fm * 32) / 8 + sub;
+      a[fm] = r * RA + (uint32_t)(ch ^ tr_swz(r)) * 16u + in;
+    }
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int ch = (wn * C::WTN + fn * 32) / 8 + sub;
+      b[fn] = C::A_SLOTS * 16 + r * RB + (uint32_t)(ch ^ tr_swz(r)) * 16u + in;
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* st, uint32_t off, uint32_t rs) {
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + off));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + off + 4 * rs));
+  const v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// One k-tile (BK / 16 MFMA sub-steps), operand reads of sub-step kk + 1 in flight
+// under the MFMAs of sub-step kk; the NLOAD load instructions of the next k-tile
+// are spread over the sub-steps (as in the row-grouped GEMMs).
+template <class C, bool LOADS, int NLOAD, class Issue>
+__device__ __forceinline__ void mma_ktile_tr(const lds_u8* st, const TrFragAddr<C>& fa,
+                                             f32x16 (&acc)[C::FM][C::FN], Issue issue) {
+  constexpr int KK = C::BK / 16;
+  constexpr int NR = 2 * (C::FM + C::FN), NM = C::FM * C::FN;
+  constexpr int LPS = MOE_ROWS_LPS < NLOAD ? MOE_ROWS_LPS : NLOAD;
+  static_assert(!LOADS || LPS * KK >= NLOAD, "every load of the k-tile must be issued");
+  constexpr uint32_t RA = TrFragAddr<C>::RA, RB = TrFragAddr<C>::RB;
+  bf16x8 a[2][C::FM], b[2][C::FN];
+  auto load = [&](int kk, int buf) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) a[buf][fm] = tr_frag(st, fa.a[fm] + 16u * kk * RA, RA);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) b[buf][fn] = tr_frag(st, fa.b[fn] + 16u * kk * RB, RB);
+  };
+  load(0, 0);
+  static_for<0, KK>([&](auto kkc) {
+    constexpr int kk = decltype(kkc)::value;
+    constexpr int J0 = kk * LPS, J1 = (kk + 1) * LPS < NLOAD ? (kk + 1) * LPS : NLOAD;
+    constexpr int NL = LOADS && J1 > J0 ? J1 - J0 : 0;
+    if constexpr (kk + 1 < KK) load(kk + 1, (kk + 1) & 1);
+    static_for<0, NL>([&](auto jc) { issue(J0 + decltype(jc)::value); });
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][fn], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+    constexpr int EARLY = kk + 1 < KK ? 2 : 0;
+    if constexpr (kk + 1 < KK) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR - NR / 2, 0);
+    }
+    if constexpr (NM - EARLY > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - EARLY, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Ops: M, N of dW[e]; PHASES passes over the rows (the B rows of pass 1 are the
+// bf16 remainders of those of pass 0); a_rows / b_rows: row 0 of the expert-major
+// operand arrays for a pass; lda / ldb in elements; epilogue.
+template <class C, class Ops>
+__device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
+  __shared__ uint4 smem[C::NST * C::STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  using AL = KMajorLoad<C, C::BM>;
+  using BL = KMajorLoad<C, C::BN>;
+  constexpr int PERK = AL::PER + BL::PER;
+  const int M = Ops::M(p), N = Ops::N(p);
+  const uint32_t lda = (uint32_t)Ops::lda(p) * 2u, ldb = (uint32_t)Ops::ldb(p) * 2u;
+
+  WeightGrad<C::BM, C::BN, C::NT> sched;
+  sched.init(p.offsets, p.E, M, N);
+  XcdWalk walk;
+  walk.init(sched.total);
+  if (!walk.valid()) return;
+  TrFragAddr<C> fa;
+  fa.init(wm, wn, lane);
+  const lds_u8* lds = (const lds_u8*)smem;
+  AL al;
+  BL bl;
+
+  // k-tile kt of tile t (nkp k-tiles per pass): its row-0 pointers and last valid row
+  struct KT { const uint8_t* a; const uint8_t* b; int last; };
+  auto ktile = [&](const Tile& t, int nkp, int kt) {
+    const int ph = (Ops::PHASES > 1 && kt >= nkp) ? 1 : 0;
+    const int row0 = t.k_lo + (kt - ph * nkp) * C::BK;
+    KT r;
+    r.last = min(C::BK, t.k_hi - row0) - 1;
+    r.a = reinterpret_cast<const uint8_t*>(Ops::a_rows(p, ph)) + (size_t)row0 * lda;
+    r.b = reinterpret_cast<const uint8_t*>(Ops::b_rows(p, ph)) + (size_t)row0 * ldb;
+    return r;
+  };
+  auto issue_all = [&](const KT& k, uint4* st) {
+#pragma unroll
+    for (int i = 0; i < AL::PER; ++i) al.issue(k.a, lda, k.last, st, i);
+#pragma unroll
+    for (int i = 0; i < BL::PER; ++i) bl.issue(k.b, ldb, k.last, st + C::A_SLOTS, i);
+  };
+
+  Tile tl = sched.tile(walk.t);
+  int nkp = (tl.k_hi - tl.k_lo + C::BK - 1) / C::BK;
+  int nk = Ops::PHASES * nkp;
+  al.init(tl.m0, M);
+  bl.init(tl.n0, N);
+  if (nk > 0) issue_all(ktile(tl, nkp, 0), smem);
+  while (true) {
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+    auto kstep = [&](int kt, auto loads) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      uint4* cur = smem + (kt & 1) * C::STAGE;
+      const int last = ktile(tl, nkp, kt).last;
+      if (last < C::BK - 1) {
+        // rows past the segment: zeros in the B operand
+        uint4* zb = cur + C::A_SLOTS + (last + 1) * BL::CPR;
+        const int n = (C::BK - 1 - last) * BL::CPR;
+        for (int i = threadIdx.x; i < n; i += C::NT) zb[i] = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+      }
+      KT nx = {nullptr, nullptr, 0};
+      if constexpr (decltype(loads)::value) nx = ktile(tl, nkp, kt + 1);
+      uint4* st = smem + ((kt + 1) & 1) * C::STAGE;
+      auto issue = [&](int j) {
+        if (j < AL::PER) al.issue(nx.a, lda, nx.last, st, j);
+        else bl.issue(nx.b, ldb, nx.last, st + C::A_SLOTS, j - AL::PER);
+      };
+      mma_ktile_tr<C, decltype(loads)::value, PERK>(lds + (kt & 1) * C::STAGE * 16, fa, acc, issue);
+    };
+    int kt = 0;
+    for (; kt < nk - 1; ++kt) kstep(kt, std::true_type{});
+    if (kt < nk) kstep(kt, std::false_type{});
+    __syncthreads();
+    const Tile done = tl;
+    walk.next();
+    const bool more = walk.valid();
+    if (more) {
+      tl = sched.tile(walk.t);
+      nkp = (tl.k_hi - tl.k_lo + C::BK - 1) / C::BK;
+      nk = Ops::PHASES * nkp;
+      al.init(tl.m0, M);
+      bl.init(tl.n0, N);
+      if (nk > 0) issue_all(ktile(tl, nkp, 0), smem);
+    }
+    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + C::STAGE) + wave * RowEpiLds<C>::BYTES;
+    Ops::template epilogue<C>(p, done, acc, wm, wn, lane, wave_lds);
+    if (!more) break;
+    __syncthreads();
+  }
+}
+
+// Stores the wave's 128 x 64 slab of dW[e] (rows m, columns n of a [M, ncols] matrix).
+template <class C>
+__device__ __forceinline__ void wg_store(uint8_t* wlds, uint16_t* out, int ld, int row0, int nrows, int col0,
+                                         int ncols, f32x16 (&acc)[C::FM][C::FN], int lane) {
+  stage_store_bf16<C, C::WTN, 4>(
+      wlds, out, ld, row0, nrows, col0, ncols, lane,
+      [&](int fm, int fn, int q, int j) { return acc[fm][fn][4 * q + j]; },
+      [](int fn, int q) { return fn * 32 + q * 8; });
+}
+
+// dW_down[e] = sum_r h_r^T dO_r: A = h rows [A, I], B = dO rows [A, H].
+struct WgDownOps {
+  static constexpr int PHASES = 1;
+  __device__ static int M(const GemmArgs& p) { return p.I; }
+  __device__ static int N(const GemmArgs& p) { return p.H; }
+  __device__ static int lda(const GemmArgs& p) { return p.I; }
+  __device__ static int ldb(const GemmArgs& p) { return p.H; }
+  __device__ static const uint16_t* a_rows(const GemmArgs& p, int) { return p.Hrows; }
+  __device__ static const uint16_t* b_rows(const GemmArgs& p, int) { return p.dO; }
+  template <class C>
+  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
+                                  int lane, uint8_t* wlds) {
+    wg_store<C>(wlds, p.dWd + (size_t)t.e * p.I * p.H, p.H, t.m0 + wm * C::WTM, p.I, t.n0 + wn * C::WTN, p.H, acc,
+                lane);
+  }
+};
+
+// [dW_gate | dW_up][e] = sum_r x_r^T [dg | du]_r: A = gathered x rows [A, H],
+// B = [dg | du] rows [A, 2I], as bf16 values (pass 0) and bf16 remainders (pass 1).
+struct WgGateUpOps {
+  static constexpr int PHASES = 2;
+  __device__ static int M(const GemmArgs& p) { return p.H; }
+  __device__ static int N(const GemmArgs& p) { return 2 * p.I; }
+  __device__ static int lda(const GemmArgs& p) { return p.H; }
+  __device__ static int ldb(const GemmArgs& p) { return 2 * p.I; }
+  __device__ static const uint16_t* a_rows(const GemmArgs& p, int) { return p.Xg; }
+  __device__ static const uint16_t* b_rows(const GemmArgs& p, int ph) { return ph ? p.dGU_lo : p.dGU; }
+  template <class C>
+  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
+                                  int lane, uint8_t* wlds) {
+    // I is a multiple of 64, so a wave's 64 columns are all gate or all up
+    const int col0 = t.n0 + wn * C::WTN;
+    const bool up = col0 >= p.I;
+    uint16_t* out = (up ? p.dWu : p.dWg) + (size_t)t.e * p.H * p.I;
+    wg_store<C>(wlds, out, p.I, t.m0 + wm * C::WTM, p.H, up ? col0 - p.I : col0, p.I, acc, lane);
+  }
+};
+
+__global__ void __launch_bounds__(CfgWg::NT) k_bwd_dw_down(const GemmArgs p) { wgrad_body<CfgWg, WgDownOps>(p); }
+__global__ void __launch_bounds__(CfgWg::NT) k_bwd_dw_gateup(const GemmArgs p) {
+  wgrad_body<CfgWg, WgGateUpOps>(p);
+}
+
+// Expert-major operand rows of the weight-gradient GEMMs, one wave per row r:
+// Xg[r] = X[token], dO[r] = bf16(w * dY[token]) (w = the row's top-k weight).
+__global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
+  const long A = (long)p.T * p.k;
+  const int chunks = p.H / 8;
+  const int lane = threadIdx.x & 63;
+  for (long r = blockIdx.x * 4L + (threadIdx.x >> 6); r < A; r += gridDim.x * 4L) {
+    const int tok = p.row_token[r];
+    const float w = p.topk_w[p.row_slot[r]];
+    const uint4* x = reinterpret_cast<const uint4*>(p.X + (size_t)tok * p.H);
+    const uint4* dy = reinterpret_cast<const uint4*>(p.dY + (size_t)tok * p.H);
+    uint4* xg = reinterpret_cast<uint4*>(p.Xg + (size_t)r * p.H);
+    uint4* dO = reinterpret_cast<uint4*>(p.dO + (size_t)r * p.H);
+    for (int c = lane; c < chunks; c += 64) {
+      xg[c] = x[c];
+      const uint4 v = dy[c];
+      uint4 o;
+      o.x = pack_bf16x2(w * bf16_to_f32(v.x & 0xffffu), w * bf16_to_f32(v.x >> 16));
+      o.y = pack_bf16x2(w * bf16_to_f32(v.y & 0xffffu), w * bf16_to_f32(v.y >> 16));
+      o.z = pack_bf16x2(w * bf16_to_f32(v.z & 0xffffu), w * bf16_to_f32(v.z >> 16));
+      o.w = pack_bf16x2(w * bf16_to_f32(v.w & 0xffffu), w * bf16_to_f32(v.w >> 16));
+      dO[c] = o;
+    }
+  }
+}
+
+static int wgrad_grid(const GemmArgs& a, int M, int N) {
+  long tiles = (long)a.E * ((M + CfgWg::BM - 1) / CfgWg::BM) * ((N + CfgWg::BN - 1) / CfgWg::BN);
+  long cap = (long)num_cus();            // one 128 KB-LDS block per CU
+  long g = tiles < cap ? tiles : cap;
+  return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
+}
+
+hipError_t launch_bwd_gather(const GemmArgs& a, hipStream_t s) {
+  long rows = (long)a.T * a.k;
+  long blocks = (rows + 3) / 4;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_gather, dim3((int)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_bwd_dw_down, dim3(wgrad_grid(a, a.I, a.H)), dim3(CfgWg::NT), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_bwd_dw_gateup, dim3(wgrad_grid(a, a.H, 2 * a.I)), dim3(CfgWg::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -28,6 +28,8 @@ struct GemmArgs {
   uint16_t* dGU;          // [A, 2I]  bf16(dg) | bf16(du)
   uint16_t* dGU_lo;       // [A, 2I]  bf16 of the remainders (dg - bf16(dg), du - bf16(du))
   float* dXr;             // [A, H]
+  uint16_t* Xg;           // [A, H]  X[token] per expert-major row
+  uint16_t* dO;           // [A, H]  bf16(w * dY[token]) per expert-major row
   float* dwt_part;        // [A, nparts]
   int nparts;
   uint16_t* dWg;
@@ -58,6 +60,7 @@ hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s);
+hipError_t launch_bwd_gather(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s);
 int bwd_nparts(int I);
