@@ -50,7 +50,7 @@ def recorded_traffic(workload):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha") != pt.source_hash():
+    if rec.get("source_sha") != pt.source_hash(workload):
         return None
     return int(rec["traffic_bytes"])
 

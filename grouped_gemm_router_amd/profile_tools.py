@@ -12,8 +12,8 @@ Usage (from the repository root, after the profiling runs):
       then --pmc WRITE_SIZE, --output-format csv -o run) of ``bench.py --copy-calibration``.  Each
       counter is scaled by what it reads for the calibration copy of a known number of bytes.
 
-The traffic record carries a hash of the library sources; bench.py reports it
-only while the kernels are unchanged.
+The traffic record carries a hash of the sources of the workload's expert-MLP
+kernels; bench.py reports it only while those are unchanged.
 """
 from __future__ import annotations
 
@@ -36,12 +36,22 @@ MLP_KERNELS = {                         # kernels of one moe_expert_mlp call, pe
 }
 
 
-def source_hash() -> str:
-    """sha256 over the library sources (kernels, host code, header)."""
+# library sources the kernels of one moe_expert_mlp call are built from, per workload kind
+# (the host code and shared headers for all; the backward and routing sources for none)
+_COMMON_SOURCES = ("api.cpp", "common.h", "kernels.h", "grouped_gemm.h")
+MLP_SOURCES = {
+    "bf16": _COMMON_SOURCES + ("gemm_rows.h", "gemm_bf16.hip"),
+    "decode": _COMMON_SOURCES + ("decode.hip",),
+    "mxfp8": _COMMON_SOURCES + ("gemm_rows.h", "mx_gemm.hip", "elementwise.hip"),
+}
+
+
+def source_hash(workload: str) -> str:
+    """sha256 over the sources of the workload's moe_expert_mlp kernels (and the header)."""
     h = hashlib.sha256()
-    files = [os.path.join(ROOT, "include", "moe.h")]
     csrc = os.path.join(PKG, "csrc")
-    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h", ".cpp"))]
+    files = [os.path.join(ROOT, "include", "moe.h")]
+    files += [os.path.join(csrc, f) for f in sorted(MLP_SOURCES[_kind(workload)])]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -99,7 +109,7 @@ def _kind(workload: str) -> str:
 
 def traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one moe_expert_mlp call, scaled by the copy."""
-    res = {"workload": workload, "source_sha": source_hash(), "copy_bytes": COPY_BYTES}
+    res = {"workload": workload, "source_sha": source_hash(workload), "copy_bytes": COPY_BYTES}
     for counter, src in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _per_dispatch(src, counter)
         copy = sorted(v for k, vals in per.items() if COPY_KERNEL in k for _, v in vals)
@@ -142,7 +152,7 @@ def traffic_md(t: dict, out: str, cmd_fetch: str, cmd_write: str) -> None:
         d = t[c]
         per = ", ".join(f"{k}: {v / 1e6:.1f} MB" for k, v in d["per_kernel_bytes"].items())
         lines.append(f"| {c} | {d['copy_kib_read']:.0f} | {d['factor']:.4f} | {per} | {d['call_bytes'] / 1e6:.1f} MB |")
-    lines += ["", f"Total per call: {t['traffic_bytes'] / 1e6:.1f} MB.  Library source sha256: `{t['source_sha']}`."]
+    lines += ["", f"Total per call: {t['traffic_bytes'] / 1e6:.1f} MB.  Expert-MLP source sha256: `{t['source_sha']}`."]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
