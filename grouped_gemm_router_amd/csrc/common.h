@@ -38,11 +38,4 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 __device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
 
-// 16-byte streaming load (nontemporal: data read once, keep it out of the way in the caches).
-__device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
-  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 }  // namespace moe

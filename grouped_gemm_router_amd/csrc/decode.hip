@@ -20,7 +20,15 @@
 
 namespace moe {
 
-constexpr int DEC_NT = 256;            // 4 waves
+#ifndef MOE_DEC_KSPLIT
+#define MOE_DEC_KSPLIT 4
+#endif
+#ifndef MOE_DEC_PF
+#define MOE_DEC_PF 4
+#endif
+constexpr int DEC_NT = 256;            // 4 waves (work-list build, down)
+constexpr int DEC_GU_WAVES = MOE_DEC_KSPLIT;   // gate/up: waves splitting the contraction axis
+constexpr int DEC_GU_NT = 64 * DEC_GU_WAVES;
 
 // Work list of (expert, group of 16 rows) entries for the experts that have
 // rows, in expert order: list[i] = e | (group << 16), i < count.  Returns count
@@ -74,10 +82,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 template <int PF>
 struct WaveStream {
   // rows: 16 weight rows per matrix (lane & 15), each lane owns 32 bytes of a 64-wide k step
+  // (plain cached loads: measured faster than nontemporal ones for this stream)
   static __device__ __forceinline__ void load(const uint16_t* w, int ks, uint4 (&dst)[2]) {
     const uint4* q = reinterpret_cast<const uint4*>(w + ks * 64);
-    dst[0] = ldg_nt(q);
-    dst[1] = ldg_nt(q + 1);
+    dst[0] = q[0];
+    dst[1] = q[1];
   }
   static __device__ __forceinline__ void load_x(const uint16_t* x, int ks, uint4 (&dst)[2]) {
     const uint4* q = reinterpret_cast<const uint4*>(x + ks * 64);
@@ -91,7 +100,7 @@ __device__ __forceinline__ f32x4 mfma2(const uint4 (&a)[2], const uint4 (&b)[2],
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[1]), as_bf16x8(b[1]), c, 0, 0, 0);
 }
 
-constexpr int DEC_PF = 4;
+constexpr int DEC_PF = MOE_DEC_PF;
 
 // Runs step(s) for k-steps 0..n-1 (step kk uses buffer kk % DEC_PF) with the
 // loads of step kk + DEC_PF issued right after step kk.  When n is a multiple
@@ -136,8 +145,8 @@ __device__ __forceinline__ void stream_steps(int n, Load load, Step step) {
 // gate/up + SwiGLU: one workgroup per unit (expert, row group, 16 intermediate
 // columns); its 4 waves split the contraction axis in 4 and their partial sums
 // are added through LDS in wave order before the epilogue.
-__global__ void __launch_bounds__(DEC_NT) k_decode_gateup(const GemmArgs p) {
-  __shared__ f32x4 part[DEC_NT / 64 - 1][2][64];
+__global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup(const GemmArgs p) {
+  __shared__ f32x4 part[DEC_GU_WAVES - 1][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slabs = p.I / 16;
   const int u = blockIdx.x;
@@ -148,7 +157,7 @@ __global__ void __launch_bounds__(DEC_NT) k_decode_gateup(const GemmArgs p) {
   const int r0 = p.offsets[e] + g * 16, n = min(p.offsets[e + 1] - r0, 16);
   const int ksteps = p.H / 64;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int k_lo = wave_u * ksteps / 4, nks = (wave_u + 1) * ksteps / 4 - k_lo;
+  const int k_lo = wave_u * ksteps / DEC_GU_WAVES, nks = (wave_u + 1) * ksteps / DEC_GU_WAVES - k_lo;
   const size_t wrow = ((size_t)e * p.I + i0 + (lane & 15)) * p.H + (lane >> 4) * 16 + (size_t)k_lo * 64;
   const uint16_t* wg = p.Wg_t + wrow;
   const uint16_t* wu = p.Wu_t + wrow;
@@ -175,7 +184,7 @@ __global__ void __launch_bounds__(DEC_NT) k_decode_gateup(const GemmArgs p) {
   // D layout: lane holds row (lane & 15), features 4 * (lane >> 4) + v
   if ((lane & 15) < n) {
 #pragma unroll
-    for (int w = 0; w < DEC_NT / 64 - 1; ++w) {
+    for (int w = 0; w < DEC_GU_WAVES - 1; ++w) {
       ag += part[w][0][lane];
       au += part[w][1][lane];
     }
@@ -224,7 +233,7 @@ hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s) {
   const long rows = (long)a.T * a.k;
   const long experts = rows < a.E ? rows : a.E;
   const long groups = rows / 16 + experts;
-  hipLaunchKernelGGL(k_decode_gateup, dim3((unsigned)(groups * (a.I / 16))), dim3(DEC_NT), 0, s, a);
+  hipLaunchKernelGGL(k_decode_gateup, dim3((unsigned)(groups * (a.I / 16))), dim3(DEC_GU_NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_down, dim3((unsigned)(groups * (a.H / 64))), dim3(DEC_NT), 0, s, a);

@@ -117,27 +117,24 @@ struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
 };
 
 // Plain store of the tile (bf16 or fp32) to out[r * ld + n], rows of the expert only.
-template <class C, typename T>
-__device__ __forceinline__ void store_rows(T* base, int ld, int ncols, const Tile& t,
-                                           f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
+// fp32 rows straight from the accumulators: each lane writes its 16-byte item
+// groups (32 contiguous bytes per row from the two lane halves).
+template <class C>
+__device__ __forceinline__ void store_rows_f32(float* base, int ld, int ncols, const Tile& t,
+                                               f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int r = t.m0 + Frag<C>::row(wm, fm, lane);
     if (r >= t.m_end) continue;
-    T* out = base + (size_t)r * ld;
+    float* out = base + (size_t)r * ld;
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = t.n0 + Frag<C>::col(wn, fn, q, lane);
         if (n >= ncols) continue;
-        if constexpr (sizeof(T) == 2) {
-          store_bf16x4(reinterpret_cast<uint16_t*>(out + n), acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1],
-                       acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]);
-        } else {
-          *reinterpret_cast<float4*>(out + n) =
-              make_float4(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]);
-        }
+        *reinterpret_cast<float4*>(out + n) =
+            make_float4(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]);
       }
   }
 }
@@ -167,69 +164,116 @@ struct BwdPOps : RowOpsBase<C, RSrcDY, RSrcDownWT> {
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t*) {
-    store_rows<C, float>(p.P, p.I, p.I, t, acc, wm, wn, lane);
+    store_rows_f32<C>(p.P, p.I, p.I, t, acc, wm, wn, lane);
   }
 };
 
-// v = hi + lo with hi = bf16(v), lo = bf16(v - hi): stores both (4 values).
-__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const float (&v)[4]) {
-  uint2 h, l;
-  h.x = pack_bf16x2(v[0], v[1]);
-  h.y = pack_bf16x2(v[2], v[3]);
-  l.x = pack_bf16x2(v[0] - bf16_to_f32(h.x & 0xffffu), v[1] - bf16_to_f32(h.x >> 16));
-  l.y = pack_bf16x2(v[2] - bf16_to_f32(h.y & 0xffffu), v[3] - bf16_to_f32(h.y >> 16));
-  *reinterpret_cast<uint2*>(hi) = h;
-  *reinterpret_cast<uint2*>(lo) = l;
+// v = hi + lo with hi = bf16(v), lo = bf16(v - hi), four values packed in pairs.
+__device__ __forceinline__ void split4(const float (&v)[4], uint2& hi, uint2& lo) {
+  hi.x = pack_bf16x2(v[0], v[1]);
+  hi.y = pack_bf16x2(v[2], v[3]);
+  lo.x = pack_bf16x2(v[0] - bf16_to_f32(hi.x & 0xffffu), v[1] - bf16_to_f32(hi.x >> 16));
+  lo.y = pack_bf16x2(v[2] - bf16_to_f32(hi.y & 0xffffu), v[3] - bf16_to_f32(hi.y >> 16));
 }
 
 // Recompute G, U; with P give h, the router-weight partial sums <h, P>, dg and du.
+// A wave owns 32 intermediate columns of 128 rows.  P is read one 32-row block
+// ahead of its use; the five bf16 outputs (h, dg and du with their remainders) of each
+// 32-row block go through the wave's LDS scratch and leave as whole 64-byte row
+// segments (16 bytes per lane).
 template <class C>
 struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
   __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
+  // one staged 32 x 32 bf16 block: 64-byte rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
+  static constexpr int OUT = 32 * 64;
+  static_assert(C::FN * 16 == 32, "a wave owns 32 intermediate columns");
+  static_assert(4 * OUT <= RowEpiLds<C>::BYTES, "staging area too small");
+
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
-                                  int wm, int wn, int lane, uint8_t*) {
+                                  int wm, int wn, int lane, uint8_t* wlds) {
+    const int col0 = t.nt * (C::BN / 2) + wn * 32;   // first intermediate column of the wave
+    const bool cv = col0 < p.I;                       // I is a multiple of 32: all or none valid
+    const int h = lane >> 5;
+    // P and the row weight of row block fm (rows past the segment read a valid row),
+    // one block ahead of its use
+    float4 P4[2][C::FN][2];
+    float wr[2];
+    auto load_p = [&](int fm, int buf) {
+      const int r = min(t.m0 + Frag<C>::row(wm, fm, lane), t.m_end - 1);
+      wr[buf] = p.topk_w[p.row_slot[r]];
+      const float* Prow = p.P + (size_t)r * p.I + col0 + h * 4;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          P4[buf][fn][q] = cv ? *reinterpret_cast<const float4*>(Prow + fn * 16 + q * 8) : make_float4(0, 0, 0, 0);
+    };
+    load_p(0, 0);
     // same (gate, up) pairing as the forward: items 4q + j and 4q + 8 + j of fragment fn
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
+      if (fm + 1 < C::FM) load_p(fm + 1, (fm + 1) & 1);
       const int r = t.m0 + Frag<C>::row(wm, fm, lane);
-      const bool rv = r < t.m_end;
+      const float w = wr[fm & 1];
       float dot = 0.f;
-      if (rv) {
-        const float w = p.topk_w[p.row_slot[r]];
-        const float* Prow = p.P + (size_t)r * p.I;
-        uint16_t* hrow = p.Hrows + (size_t)r * p.I;
-        uint16_t* grow = p.dGU + (size_t)r * 2 * p.I;
-        uint16_t* lrow = p.dGU_lo + (size_t)r * 2 * p.I;
+      const int rl = lane & 31;
+      // chunk (2 fn + q) of staged block o, this lane's row and half
+      auto slot = [&](int o, int fn, int q) {
+        return reinterpret_cast<uint2*>(wlds + o * OUT + rl * 64 + (((2 * fn + q) ^ ((rl >> 2) & 3)) * 16) + h * 8);
+      };
+      uint2 ul[C::FN][2];                             // staged after the first four blocks leave
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
+      for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int col = t.nt * (C::BN / 2) + (wn * C::FN + fn) * 16 + q * 8 + (lane >> 5) * 4;
-            if (col >= p.I) continue;
-            const float4 P4 = *reinterpret_cast<const float4*>(Prow + col);
-            const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
-            float hv[4], dg[4], du[4];
+        for (int q = 0; q < 2; ++q) {
+          const float4 pv = P4[fm & 1][fn][q];
+          const float Pv[4] = {pv.x, pv.y, pv.z, pv.w};
+          float hv[4], dg[4], du[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float g = acc[fm][fn][4 * q + j], u = acc[fm][fn][4 * q + 8 + j];
-              const float sg = sigmoid_f32(g);
-              hv[j] = bf16_to_f32(f32_to_bf16(g * sg * u));
-              dot += hv[j] * Pv[j];
-              const float dh = w * Pv[j];
-              du[j] = dh * (g * sg);
-              dg[j] = dh * u * (sg * (1.f + g * (1.f - sg)));
-            }
-            store_bf16x4(hrow + col, hv[0], hv[1], hv[2], hv[3]);
-            store_split4(grow + col, lrow + col, dg);
-            store_split4(grow + p.I + col, lrow + p.I + col, du);
+          for (int j = 0; j < 4; ++j) {
+            const float g = acc[fm][fn][4 * q + j], u = acc[fm][fn][4 * q + 8 + j];
+            const float sg = sigmoid_f32(g);
+            hv[j] = bf16_to_f32(f32_to_bf16(g * sg * u));
+            dot += hv[j] * Pv[j];
+            const float dh = w * Pv[j];
+            du[j] = dh * (g * sg);
+            dg[j] = dh * u * (sg * (1.f + g * (1.f - sg)));
           }
-      }
+          if (cv) {
+            uint2 hi, lo;
+            *slot(0, fn, q) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            split4(dg, hi, lo);
+            *slot(1, fn, q) = hi;
+            *slot(2, fn, q) = lo;
+            split4(du, hi, ul[fn][q]);
+            *slot(3, fn, q) = hi;
+          }
+        }
       // the other half of this row's columns sits in lane ^ 32
       dot += __shfl_xor(dot, 32, 64);
-      if (rv && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
+      if (r < t.m_end && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
+      if (!cv) continue;
+      const int row0 = t.m0 + wm * C::WTM + fm * 32;
+      auto flush = [&](int o, uint16_t* out, int ld) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int idx = i * 64 + lane, rr = idx >> 2, ch = idx & 3;
+          const uint4 v = *reinterpret_cast<const uint4*>(wlds + o * OUT + rr * 64 + ((ch ^ ((rr >> 2) & 3)) * 16));
+          if (row0 + rr < t.m_end) *reinterpret_cast<uint4*>(out + (size_t)(row0 + rr) * ld + col0 + ch * 8) = v;
+        }
+      };
+      flush(0, p.Hrows, p.I);
+      flush(1, p.dGU, 2 * p.I);
+      flush(2, p.dGU_lo, 2 * p.I);
+      flush(3, p.dGU + p.I, 2 * p.I);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) *slot(0, fn, q) = ul[fn][q];
+      flush(0, p.dGU_lo + p.I, 2 * p.I);
     }
   }
 };
@@ -243,7 +287,7 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT> {
   }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t*) {
-    store_rows<C, float>(p.dXr, p.H, p.H, t, acc, wm, wn, lane);
+    store_rows_f32<C>(p.dXr, p.H, p.H, t, acc, wm, wn, lane);
   }
 };
 
