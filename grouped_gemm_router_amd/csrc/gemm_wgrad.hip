@@ -27,8 +27,26 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// 256 x 256 output tiles, 8 waves (2 x 4), 64-row k-tiles, two LDS stages of 64 KB.
-using CfgWg = RowCfg<256, 256, 2, 4, 64, 2>;
+// Tile configuration: BM x BN output tiles, WAVES_M x WAVES_N waves, BK-row
+// k-tiles, NST LDS stages.  A stage holds the A k-tile and NB B k-tiles that
+// share it (the B rows of every pass over the same rows).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NST_, int NB_>
+struct WgCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M_ * WAVES_N_;
+  static constexpr int NT = 64 * NW;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int BK = BK_, NST = NST_, NB = NB_;
+  static constexpr int A_SLOTS = BM * BK / 8, B_SLOTS = BN * BK / 8;   // 16-byte slots per stage
+  static constexpr int STAGE = A_SLOTS + NB * B_SLOTS;
+  static_assert(BK % 16 == 0 && NST * STAGE * 16 <= 150 * 1024, "k-tile and LDS budget");
+};
+// 32-row k-tiles and three stages (two k-tiles in flight).  dW_down: 32 KB stages.
+// dW_gate/up: the x k-tile is shared by the bf16 values and the bf16 remainders
+// of [dg | du]: 48 KB stages.
+using CfgWgDown = WgCfg<256, 256, 2, 4, 32, 3, 1>;
+using CfgWgGateUp = WgCfg<256, 256, 2, 4, 32, 3, 2>;
 
 // Chunk position in a k-major LDS row: chunk c of row r sits at c ^ tr_swz(r).
 // The flip of chunk-index bits 1-3 by r mod 4 makes the four rows one transpose
@@ -68,7 +86,7 @@ struct KMajorLoad {
 };
 
 // Byte offsets (in a stage) of this lane's transpose reads for sub-step 0, read 0;
-// sub-step kk, read j is at + (16 kk + 4 j) row strides.
+// sub-step kk, read j is at + (16 kk + 4 j) row strides; B operand nb at + nb B_SLOTS.
 template <class C>
 struct TrFragAddr {
   static constexpr uint32_t RA = C::BM * 2, RB = C::BN * 2;       // row strides in bytes
@@ -99,35 +117,43 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* st, uint32_t off, uint32
 }
 
 // One k-tile (BK / 16 MFMA sub-steps), operand reads of sub-step kk + 1 in flight
-// under the MFMAs of sub-step kk; the NLOAD load instructions of the next k-tile
-// are spread over the sub-steps (as in the row-grouped GEMMs).
+// under the MFMAs of sub-step kk; the NLOAD load instructions of a later k-tile
+// are spread over the sub-steps (as in the row-grouped GEMMs).  Every B operand
+// accumulates into the same accumulators.
 template <class C, bool LOADS, int NLOAD, class Issue>
 __device__ __forceinline__ void mma_ktile_tr(const lds_u8* st, const TrFragAddr<C>& fa,
                                              f32x16 (&acc)[C::FM][C::FN], Issue issue) {
   constexpr int KK = C::BK / 16;
-  constexpr int NR = 2 * (C::FM + C::FN), NM = C::FM * C::FN;
+  constexpr int NR = 2 * (C::FM + C::NB * C::FN), NM = C::FM * C::NB * C::FN;
   constexpr int LPS = MOE_ROWS_LPS < NLOAD ? MOE_ROWS_LPS : NLOAD;
-  static_assert(!LOADS || LPS * KK >= NLOAD, "every load of the k-tile must be issued");
+  constexpr int LPS_ = LPS * KK >= NLOAD ? LPS : (NLOAD + KK - 1) / KK;
+  static_assert(!LOADS || LPS_ * KK >= NLOAD, "every load of the k-tile must be issued");
   constexpr uint32_t RA = TrFragAddr<C>::RA, RB = TrFragAddr<C>::RB;
-  bf16x8 a[2][C::FM], b[2][C::FN];
+  bf16x8 a[2][C::FM], b[2][C::NB][C::FN];
   auto load = [&](int kk, int buf) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) a[buf][fm] = tr_frag(st, fa.a[fm] + 16u * kk * RA, RA);
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) b[buf][fn] = tr_frag(st, fa.b[fn] + 16u * kk * RB, RB);
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        b[buf][nb][fn] = tr_frag(st, fa.b[fn] + nb * C::B_SLOTS * 16u + 16u * kk * RB, RB);
   };
   load(0, 0);
   static_for<0, KK>([&](auto kkc) {
     constexpr int kk = decltype(kkc)::value;
-    constexpr int J0 = kk * LPS, J1 = (kk + 1) * LPS < NLOAD ? (kk + 1) * LPS : NLOAD;
+    constexpr int J0 = kk * LPS_, J1 = (kk + 1) * LPS_ < NLOAD ? (kk + 1) * LPS_ : NLOAD;
     constexpr int NL = LOADS && J1 > J0 ? J1 - J0 : 0;
     if constexpr (kk + 1 < KK) load(kk + 1, (kk + 1) & 1);
     static_for<0, NL>([&](auto jc) { issue(J0 + decltype(jc)::value); });
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][fn], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][nb][fn], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
     constexpr int EARLY = kk + 1 < KK ? 2 : 0;
     if constexpr (kk + 1 < KK) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -140,9 +166,8 @@ __device__ __forceinline__ void mma_ktile_tr(const lds_u8* st, const TrFragAddr<
   });
 }
 
-// Ops: M, N of dW[e]; PHASES passes over the rows (the B rows of pass 1 are the
-// bf16 remainders of those of pass 0); a_rows / b_rows: row 0 of the expert-major
-// operand arrays for a pass; lda / ldb in elements; epilogue.
+// Ops: M, N of dW[e]; a_rows / b_rows(nb): row 0 of the expert-major operand
+// arrays (B operand nb of C::NB); lda / ldb in elements; epilogue.
 template <class C, class Ops>
 __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
   __shared__ uint4 smem[C::NST * C::STAGE];
@@ -150,7 +175,7 @@ __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   using AL = KMajorLoad<C, C::BM>;
   using BL = KMajorLoad<C, C::BN>;
-  constexpr int PERK = AL::PER + BL::PER;
+  constexpr int PERK = AL::PER + C::NB * BL::PER;     // load instructions per k-tile per wave
   const int M = Ops::M(p), N = Ops::N(p);
   const uint32_t lda = (uint32_t)Ops::lda(p) * 2u, ldb = (uint32_t)Ops::ldb(p) * 2u;
 
@@ -165,30 +190,40 @@ __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
   AL al;
   BL bl;
 
-  // k-tile kt of tile t (nkp k-tiles per pass): its row-0 pointers and last valid row
-  struct KT { const uint8_t* a; const uint8_t* b; int last; };
-  auto ktile = [&](const Tile& t, int nkp, int kt) {
-    const int ph = (Ops::PHASES > 1 && kt >= nkp) ? 1 : 0;
-    const int row0 = t.k_lo + (kt - ph * nkp) * C::BK;
+  // k-tile kt of tile t: its row-0 pointers and last valid row
+  struct KT { const uint8_t* a; const uint8_t* b[C::NB]; int last; };
+  auto ktile = [&](const Tile& t, int kt) {
+    const int row0 = t.k_lo + kt * C::BK;
     KT r;
     r.last = min(C::BK, t.k_hi - row0) - 1;
-    r.a = reinterpret_cast<const uint8_t*>(Ops::a_rows(p, ph)) + (size_t)row0 * lda;
-    r.b = reinterpret_cast<const uint8_t*>(Ops::b_rows(p, ph)) + (size_t)row0 * ldb;
+    r.a = reinterpret_cast<const uint8_t*>(Ops::a_rows(p)) + (size_t)row0 * lda;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) r.b[nb] = reinterpret_cast<const uint8_t*>(Ops::b_rows(p, nb)) + (size_t)row0 * ldb;
     return r;
   };
-  auto issue_all = [&](const KT& k, uint4* st) {
+  auto issue_one = [&](const KT& k, uint4* st, int j) {
+    if (j < AL::PER) {
+      al.issue(k.a, lda, k.last, st, j);
+    } else {
+      const int nb = (j - AL::PER) / BL::PER, i = (j - AL::PER) % BL::PER;
+      bl.issue(k.b[nb], ldb, k.last, st + C::A_SLOTS + nb * C::B_SLOTS, i);
+    }
+  };
+  auto prologue = [&](const Tile& t, int nk) {
 #pragma unroll
-    for (int i = 0; i < AL::PER; ++i) al.issue(k.a, lda, k.last, st, i);
+    for (int s = 0; s < C::NST - 1; ++s)
+      if (s < nk) {
+        const KT k = ktile(t, s);
 #pragma unroll
-    for (int i = 0; i < BL::PER; ++i) bl.issue(k.b, ldb, k.last, st + C::A_SLOTS, i);
+        for (int j = 0; j < PERK; ++j) issue_one(k, smem + s * C::STAGE, j);
+      }
   };
 
   Tile tl = sched.tile(walk.t);
-  int nkp = (tl.k_hi - tl.k_lo + C::BK - 1) / C::BK;
-  int nk = Ops::PHASES * nkp;
+  int nk = (tl.k_hi - tl.k_lo + C::BK - 1) / C::BK;
   al.init(tl.m0, M);
   bl.init(tl.n0, N);
-  if (nk > 0) issue_all(ktile(tl, nkp, 0), smem);
+  prologue(tl, nk);
   while (true) {
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -197,43 +232,48 @@ __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+    // k step kt: wait for k-tile kt, then compute it while (LOADS) issuing k-tile kt + NST - 1
     auto kstep = [&](int kt, auto loads) {
-      wait_vmcnt<0>();
+      const int ahead = nk - 1 - kt;                  // k-tiles issued after this one (capped)
+      // (the first step also waits for the previous tile's epilogue stores)
+      if (kt == 0) wait_vmcnt<0>();
+      else wait_ktiles<C::NST, PERK>(ahead < C::NST - 2 ? ahead : C::NST - 2);
       __syncthreads();
-      uint4* cur = smem + (kt & 1) * C::STAGE;
-      const int last = ktile(tl, nkp, kt).last;
+      uint4* cur = smem + (kt % C::NST) * C::STAGE;
+      const int last = ktile(tl, kt).last;
       if (last < C::BK - 1) {
-        // rows past the segment: zeros in the B operand
-        uint4* zb = cur + C::A_SLOTS + (last + 1) * BL::CPR;
+        // rows past the segment: zeros in every B operand
         const int n = (C::BK - 1 - last) * BL::CPR;
-        for (int i = threadIdx.x; i < n; i += C::NT) zb[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          uint4* zb = cur + C::A_SLOTS + nb * C::B_SLOTS + (last + 1) * BL::CPR;
+          for (int i = threadIdx.x; i < n; i += C::NT) zb[i] = make_uint4(0, 0, 0, 0);
+        }
         __syncthreads();
       }
-      KT nx = {nullptr, nullptr, 0};
-      if constexpr (decltype(loads)::value) nx = ktile(tl, nkp, kt + 1);
-      uint4* st = smem + ((kt + 1) & 1) * C::STAGE;
-      auto issue = [&](int j) {
-        if (j < AL::PER) al.issue(nx.a, lda, nx.last, st, j);
-        else bl.issue(nx.b, ldb, nx.last, st + C::A_SLOTS, j - AL::PER);
-      };
-      mma_ktile_tr<C, decltype(loads)::value, PERK>(lds + (kt & 1) * C::STAGE * 16, fa, acc, issue);
+      KT nx = {};
+      const int nxt = kt + C::NST - 1;
+      if constexpr (decltype(loads)::value) nx = ktile(tl, nxt);
+      uint4* st = smem + (nxt % C::NST) * C::STAGE;
+      auto issue = [&](int j) { issue_one(nx, st, j); };
+      mma_ktile_tr<C, decltype(loads)::value, PERK>(lds + (kt % C::NST) * C::STAGE * 16, fa, acc, issue);
     };
+    // the last NST - 1 k steps issue nothing: peeled, not branched
     int kt = 0;
-    for (; kt < nk - 1; ++kt) kstep(kt, std::true_type{});
-    if (kt < nk) kstep(kt, std::false_type{});
+    for (; kt < nk - (C::NST - 1); ++kt) kstep(kt, std::true_type{});
+    for (; kt < nk; ++kt) kstep(kt, std::false_type{});
     __syncthreads();
     const Tile done = tl;
     walk.next();
     const bool more = walk.valid();
     if (more) {
       tl = sched.tile(walk.t);
-      nkp = (tl.k_hi - tl.k_lo + C::BK - 1) / C::BK;
-      nk = Ops::PHASES * nkp;
+      nk = (tl.k_hi - tl.k_lo + C::BK - 1) / C::BK;
       al.init(tl.m0, M);
       bl.init(tl.n0, N);
-      if (nk > 0) issue_all(ktile(tl, nkp, 0), smem);
+      prologue(tl, nk);
     }
-    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + C::STAGE) + wave * RowEpiLds<C>::BYTES;
+    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + (C::NST - 1) * C::STAGE) + wave * RowEpiLds<C>::BYTES;
     Ops::template epilogue<C>(p, done, acc, wm, wn, lane, wave_lds);
     if (!more) break;
     __syncthreads();
@@ -252,12 +292,11 @@ __device__ __forceinline__ void wg_store(uint8_t* wlds, uint16_t* out, int ld, i
 
 // dW_down[e] = sum_r h_r^T dO_r: A = h rows [A, I], B = dO rows [A, H].
 struct WgDownOps {
-  static constexpr int PHASES = 1;
   __device__ static int M(const GemmArgs& p) { return p.I; }
   __device__ static int N(const GemmArgs& p) { return p.H; }
   __device__ static int lda(const GemmArgs& p) { return p.I; }
   __device__ static int ldb(const GemmArgs& p) { return p.H; }
-  __device__ static const uint16_t* a_rows(const GemmArgs& p, int) { return p.Hrows; }
+  __device__ static const uint16_t* a_rows(const GemmArgs& p) { return p.Hrows; }
   __device__ static const uint16_t* b_rows(const GemmArgs& p, int) { return p.dO; }
   template <class C>
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
@@ -268,15 +307,14 @@ struct WgDownOps {
 };
 
 // [dW_gate | dW_up][e] = sum_r x_r^T [dg | du]_r: A = gathered x rows [A, H],
-// B = [dg | du] rows [A, 2I], as bf16 values (pass 0) and bf16 remainders (pass 1).
+// B = [dg | du] rows [A, 2I] as bf16 values (nb = 0) and bf16 remainders (nb = 1).
 struct WgGateUpOps {
-  static constexpr int PHASES = 2;
   __device__ static int M(const GemmArgs& p) { return p.H; }
   __device__ static int N(const GemmArgs& p) { return 2 * p.I; }
   __device__ static int lda(const GemmArgs& p) { return p.H; }
   __device__ static int ldb(const GemmArgs& p) { return 2 * p.I; }
-  __device__ static const uint16_t* a_rows(const GemmArgs& p, int) { return p.Xg; }
-  __device__ static const uint16_t* b_rows(const GemmArgs& p, int ph) { return ph ? p.dGU_lo : p.dGU; }
+  __device__ static const uint16_t* a_rows(const GemmArgs& p) { return p.Xg; }
+  __device__ static const uint16_t* b_rows(const GemmArgs& p, int nb) { return nb ? p.dGU_lo : p.dGU; }
   template <class C>
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
                                   int lane, uint8_t* wlds) {
@@ -288,9 +326,11 @@ struct WgGateUpOps {
   }
 };
 
-__global__ void __launch_bounds__(CfgWg::NT) k_bwd_dw_down(const GemmArgs p) { wgrad_body<CfgWg, WgDownOps>(p); }
-__global__ void __launch_bounds__(CfgWg::NT) k_bwd_dw_gateup(const GemmArgs p) {
-  wgrad_body<CfgWg, WgGateUpOps>(p);
+__global__ void __launch_bounds__(CfgWgDown::NT) k_bwd_dw_down(const GemmArgs p) {
+  wgrad_body<CfgWgDown, WgDownOps>(p);
+}
+__global__ void __launch_bounds__(CfgWgGateUp::NT) k_bwd_dw_gateup(const GemmArgs p) {
+  wgrad_body<CfgWgGateUp, WgGateUpOps>(p);
 }
 
 // Expert-major operand rows of the weight-gradient GEMMs, one wave per row r:
@@ -319,9 +359,10 @@ __global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
   }
 }
 
+template <class C>
 static int wgrad_grid(const GemmArgs& a, int M, int N) {
-  long tiles = (long)a.E * ((M + CfgWg::BM - 1) / CfgWg::BM) * ((N + CfgWg::BN - 1) / CfgWg::BN);
-  long cap = (long)num_cus();            // one 128 KB-LDS block per CU
+  long tiles = (long)a.E * ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  long cap = (long)num_cus();            // one workgroup per CU (LDS)
   long g = tiles < cap ? tiles : cap;
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
@@ -335,11 +376,11 @@ hipError_t launch_bwd_gather(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dw_down, dim3(wgrad_grid(a, a.I, a.H)), dim3(CfgWg::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_dw_down, dim3(wgrad_grid<CfgWgDown>(a, a.I, a.H)), dim3(CfgWgDown::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dw_gateup, dim3(wgrad_grid(a, a.H, 2 * a.I)), dim3(CfgWg::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_dw_gateup, dim3(wgrad_grid<CfgWgGateUp>(a, a.H, 2 * a.I)), dim3(CfgWgGateUp::NT), 0, s, a);
   return hipGetLastError();
 }
 
