@@ -113,8 +113,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 }
 
 // ---------------------------------------------------------------------------
-// Dispatch.  The T*k slots are cut into chunks of 4096 (one block, four
-// waves of 1024 consecutive slots each).  Inside a wave, 64 slots are handled
+// Dispatch.  The T*k slots are cut into chunks of DISPATCH_CHUNK (one block,
+// four waves of DISPATCH_CHUNK / 4 consecutive slots each).  Inside a wave, 64 slots are handled
 // at a time: ten ballots over the bits of the expert id give every lane the
 // mask of lanes holding the same expert, so its rank among equal experts in
 // slot order is a popcount, and one lane per expert updates the running count.
@@ -123,8 +123,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 //   k_dispatch_scatter: offsets (scan of the totals), per-wave bases, then the
 //                       stable scatter of (row_token, row_slot, slot_row).
 // ---------------------------------------------------------------------------
-constexpr int DISPATCH_CHUNK = 4096;
-constexpr int DISPATCH_WAVE_SLOTS = 1024;
+#ifndef MOE_DISPATCH_CHUNK
+#define MOE_DISPATCH_CHUNK 2048
+#endif
+constexpr int DISPATCH_CHUNK = MOE_DISPATCH_CHUNK;
+constexpr int DISPATCH_WAVE_SLOTS = DISPATCH_CHUNK / 4;
+static_assert(DISPATCH_WAVE_SLOTS % 64 == 0, "whole groups of 64 slots per wave");
 constexpr int DISPATCH_MAX_E = 1024;
 
 size_t dispatch_ws_bytes(long A, int E) {
