@@ -92,7 +92,6 @@ struct RSrcGateUpWT {    // [W_gate | W_up] [E, H, I] read as [E, N = H, K = 2I]
 // ------------------------------------------------------------------------
 template <class C, class SrcA_, class SrcB_>
 struct RowOpsBase {
-  static constexpr int PHASES = 1;
   using SrcA = SrcA_;
   using SrcB = SrcB_;
   using Sched = RowGroups<C::BM, C::BN, C::NT>;
@@ -116,7 +115,6 @@ struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
   }
 };
 
-// Plain store of the tile (bf16 or fp32) to out[r * ld + n], rows of the expert only.
 // fp32 rows straight from the accumulators: each lane writes its 16-byte item
 // groups (32 contiguous bytes per row from the two lane halves).
 template <class C>

@@ -176,6 +176,14 @@ __device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragA
   });
 }
 
+// The lane index as a value the compiler cannot see through: addresses derived
+// from it are computed where they are used instead of being hoisted out of the
+// tile loop and held in registers (or spilled) across the k loop.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -295,7 +303,8 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
 // NQ item groups per fragment are stored.
 template <class C, int CW, int NQ, class Val, class Col>
 __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, int ld, int row0, int row_end,
-                                                 int col0, int ncols, int lane, Val val, Col col_of) {
+                                                 int col0, int ncols, int lane_, Val val, Col col_of) {
+  const int lane = opaque_lane(lane_);
   constexpr int CPRW = CW * 2 / 16;                      // 16-byte chunks per row
   // Rows padded by 16 bytes where the scratch allows it, else unpadded 128-byte
   // rows with chunk c of row r stored at c ^ ((r >> 1) & 7).
