@@ -91,20 +91,14 @@ __device__ __forceinline__ int floor_log2_f32(float a) {  // a > 0, finite
   return ex - 127;
 }
 
-// |x| already scaled into E4M3 range; returns the code (sign included).
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  float a = fabsf(x);
-  if (!(a < 448.f)) return sign | 0x7eu;                 // saturate (also catches 448 exactly)
-  if (a < 0.015625f) {                                    // subnormal range: multiples of 2^-9
-    uint32_t m = (uint32_t)__builtin_rintf(a * 512.f);   // 8 -> the smallest normal, code 0x08
-    return sign | m;
-  }
-  int e = floor_log2_f32(a);
-  uint32_t m = (uint32_t)__builtin_rintf(ldexpf(a, 3 - e));  // 8..16
-  if (m == 16) { m = 8; ++e; }
-  uint32_t code = ((uint32_t)(e + 7) << 3) | (m - 8);
-  return sign | (code > 0x7eu ? 0x7eu : code);
+// Four values already scaled by 2^-s to fp8 codes: clamped to +-448 (the
+// saturating rule), then converted by v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950,
+// round to nearest even; E4M3 subnormals are multiples of 2^-9).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  auto sat = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
 }
 
 __global__ void __launch_bounds__(256) k_mx_quantize(const uint16_t* __restrict__ x, long nblocks,
@@ -128,13 +122,9 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const uint16_t* __restrict_
       s = s < -127 ? -127 : (s > 127 ? 127 : s);
       sbyte = (uint8_t)(s + 127);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t c0 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i] & 0xffffu), -s));
-        uint32_t c1 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i] >> 16), -s));
-        uint32_t c2 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i + 1] & 0xffffu), -s));
-        uint32_t c3 = e4m3_code(ldexpf(bf16_to_f32(d[2 * i + 1] >> 16), -s));
-        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-      }
+      for (int i = 0; i < 8; ++i)
+        out[i] = e4m3x4(ldexpf(bf16_to_f32(d[2 * i] & 0xffffu), -s), ldexpf(bf16_to_f32(d[2 * i] >> 16), -s),
+                        ldexpf(bf16_to_f32(d[2 * i + 1] & 0xffffu), -s), ldexpf(bf16_to_f32(d[2 * i + 1] >> 16), -s));
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] = 0;
