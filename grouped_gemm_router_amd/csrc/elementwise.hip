@@ -9,8 +9,18 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Combine: Y[t] = bf16(sum_j w[t,j] * O[slot_row[t*k+j]]), fp32, j ascending.
-// One thread per 8 consecutive outputs (16-byte loads and stores).
+// One thread per 8 consecutive outputs (16-byte loads and stores); the rows of
+// four slots are loaded together, then added in slot order.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void combine_add(float (&acc)[8], float wj, const uint4& v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] += wj * bf16_to_f32(d[q] & 0xffffu);
+    acc[2 * q + 1] += wj * bf16_to_f32(d[q] >> 16);
+  }
+}
+
 __global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ O, const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ w, int T, int k, int H,
                                                  uint16_t* __restrict__ Y) {
@@ -18,18 +28,19 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ O,
   const long total = (long)T * chunks;
   for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
     const int t = (int)(i / chunks), c = (int)(i - (long)t * chunks);
+    const int32_t* sr = slot_row + (size_t)t * k;
+    const float* wt = w + (size_t)t * k;
+    const uint16_t* Oc = O + c * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = slot_row[t * k + j];
-      const float wj = w[t * k + j];
-      const uint4 v = *reinterpret_cast<const uint4*>(O + (size_t)r * H + c * 8);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      uint4 v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += wj * bf16_to_f32(d[q] & 0xffffu);
-        acc[2 * q + 1] += wj * bf16_to_f32(d[q] >> 16);
-      }
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(Oc + (size_t)sr[j + u] * H);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) combine_add(acc, wt[j + u], v[u]);
     }
+    for (; j < k; ++j) combine_add(acc, wt[j], *reinterpret_cast<const uint4*>(Oc + (size_t)sr[j] * H));
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
     o.y = pack_bf16x2(acc[2], acc[3]);
