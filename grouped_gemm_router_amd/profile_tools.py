@@ -12,6 +12,14 @@ Usage (from the repository root, after the profiling runs):
       then --pmc WRITE_SIZE, --output-format csv -o run) of ``bench.py --copy-calibration``.  Each
       counter is scaled by what it reads for the calibration copy of a known number of bytes.
 
+  python -m grouped_gemm_router_amd.profile_tools mfma --pmc <dir> --stats <dir> --out <out.md> --cmd-pmc "<command>" \
+      --cmd-stats "<command>" --title "<title>"
+      MFMA utilisation per kernel from one counter run (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+      SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE) and the kernel
+      durations of a trace run of the same command: busy share of the MFMA units, MFMA FLOP per
+      dispatch (MOPS x 512), the rate they give over the traced duration, and the clock the
+      active-cycle counter implies.
+
 The traffic record carries a hash of the sources of the workload's expert-MLP
 kernels; bench.py reports it only while those are unchanged.
 """
@@ -157,6 +165,71 @@ def traffic_md(t: dict, out: str, cmd_fetch: str, cmd_write: str) -> None:
         fh.write("\n".join(lines) + "\n")
 
 
+SIMD_NUM = 256 * 4                      # MI355X: 256 compute units x 4 SIMDs
+NUM_XCD = 8
+PEAK_TFLOPS = {"BF16": 2516.6, "F8": 5033.2}
+
+
+def _per_dispatch_multi(src: str):
+    """dispatch id -> (kernel short name, {counter: value}).  rocprofv3's csv holds one row per
+    dispatch and counter, summed over all instances: GRBM_GUI_ACTIVE is then the active cycles of
+    the 8 XCDs added up, so the per-XCD count (what the MfmaUtil metric's max-reduction takes) is
+    that value / 8."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(os.path.join(src, "run_counter_collection.csv"))):
+        d = int(r["Dispatch_Id"])
+        c, v = r["Counter_Name"], float(r["Counter_Value"])
+        names[d] = _short(r["Kernel_Name"])
+        vals[d][c] += v
+    for v in vals.values():
+        if "GRBM_GUI_ACTIVE" in v:
+            v["GRBM_GUI_ACTIVE"] /= NUM_XCD
+    return {d: (names[d], vals[d]) for d in vals}
+
+
+def mfma_md(pmc_dir: str, stats_dir: str, out: str, cmd_pmc: str, cmd_stats: str, title: str) -> None:
+    per = _per_dispatch_multi(pmc_dir)
+    dur = {_short(r["Name"]): float(r["AverageNs"]) for r in
+           csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv")))}
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    cnt = collections.Counter()
+    for name, v in per.values():
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + v.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+        if mops <= 0:
+            continue
+        cnt[name] += 1
+        for c, x in v.items():
+            agg[name][c] += x
+    lines = [f"# {title}", "", "Commands (repository root, one MI355X):", "", "```", cmd_pmc, cmd_stats, "```", "",
+             "Per kernel, averaged over its dispatches:", "",
+             "- MFMA busy = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (active cycles per XCD x 1024 SIMDs), the "
+             "utilisation rocprofv3's MfmaUtil metric defines (active cycles per XCD = GRBM_GUI_ACTIVE summed "
+             "over the 8 XCDs / 8);",
+             "- MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_{BF16,F8} x 512 per dispatch, over the kernel's average traced "
+             "duration (second command) = the counted MFMA rate, as a share of the dtype's dense peak;",
+             "- clock = active cycles per XCD / traced duration;",
+             "- % of clock peak = the counted rate against the dense peak scaled to that clock (nominal 2.4 GHz).", "",
+             "| kernel | dispatches | MFMA busy | MFMA GFLOP per dispatch | avg us (trace) | counted TFLOP/s | "
+             "% of peak | clock GHz | % of clock peak |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for name in sorted(agg, key=lambda n: -agg[n]["SQ_VALU_MFMA_BUSY_CYCLES"]):
+        n = cnt[name]
+        a = {c: x / n for c, x in agg[name].items()}
+        gui = a.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = 100.0 * a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * SIMD_NUM) if gui else float("nan")
+        bf, f8 = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0), a.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+        flop = (bf + f8) * 512
+        dtype = "F8" if f8 > bf else "BF16"
+        ns = dur.get(name)
+        rate = flop / ns / 1e3 if ns else float("nan")          # FLOP/ns = GFLOP/s -> TFLOP/s
+        clock = gui / ns if ns else float("nan")
+        lines.append(f"| `{name}` | {n} | {busy:.1f}% | {flop / 1e9:.2f} | {ns / 1e3 if ns else float('nan'):.1f} "
+                     f"| {rate:.0f} | {100 * rate / PEAK_TFLOPS[dtype]:.1f}% ({dtype}) | {clock:.2f} "
+                     f"| {100 * rate / (PEAK_TFLOPS[dtype] * clock / 2.4):.1f}% |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="action", required=True)
@@ -174,8 +247,17 @@ def main(argv=None) -> int:
     t.add_argument("--md")
     t.add_argument("--cmd-fetch", default="")
     t.add_argument("--cmd-write", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True)
+    m.add_argument("--stats", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--cmd-pmc", default="")
+    m.add_argument("--cmd-stats", default="")
+    m.add_argument("--title", required=True)
     a = ap.parse_args(argv)
-    if a.action == "stats":
+    if a.action == "mfma":
+        mfma_md(a.pmc, a.stats, a.out, a.cmd_pmc, a.cmd_stats, a.title)
+    elif a.action == "stats":
         stats_md(a.src, a.out, a.cmd, a.title, a.note)
     else:
         res = traffic(a.fetch, a.write, a.workload)
