@@ -5,7 +5,11 @@ One step is one pass of the layer's hot path over one batch of synthetic
 input: routing, dispatch, the grouped-GEMM expert MLP (gate/up + SwiGLU,
 down) and the weighted combine; for the training workload also the backward.
 Inputs are resident in HBM before the timed region; weight packing happens at
-load time, outside it.  Caches are not flushed between steps.
+load time, outside it.  The timed region (the reported value) does not flush
+caches between steps; its per-step times give p10 / p50 / p90.  With
+--cold-cache a second pass reads 512 MiB before every step, which evicts L2
+and the Infinity Cache (and leaves clean lines, so the step pays no write-back
+of the flush), and times each step on its own (reported under cold_cache).
 
 Prints one JSON line.  Default workload: prefill (T=4096 tokens, hidden 2048,
 intermediate 512, 256 experts, top-8, bf16).  Other workloads (--workload
@@ -25,6 +29,7 @@ METRIC = "MoE layer fwd/bwd TFLOP/s + tokens/s, % of MFMA (prefill) / HBM (decod
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+FLUSH_BYTES = 512 << 20        # read before each cold-cache step: more than L2 (8 x 4 MB) + Infinity Cache (256 MB)
 
 
 def parse():
@@ -32,6 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="also time steps after reading 512 MiB (L2 and Infinity Cache evicted), each step alone")
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
@@ -169,19 +176,38 @@ def main():
         torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]   # step boundaries
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    marks[0].record()
     for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             step(evs[i])
-    t_end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+
+    cold_ms = None
+    if args.cold_cache:
+        # 512 MiB read before each step (its lines replace everything cached), each step timed alone
+        flush = torch.full((FLUSH_BYTES // 4,), 1.0, dtype=torch.float32, device="cuda")
+        n_cold = min(args.steps, 20)
+        cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+        for i in range(n_cold):
+            torch.amax(flush)
+            cold[i][0].record()
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+            cold[i][1].record()
+        torch.cuda.synchronize()
+        cold_ms = np.array([a.elapsed_time(b) for a, b in cold])
+        del flush
 
     pl = layer.plan(cfg.T, cfg.backward)
     offsets = pl["offsets"].cpu().numpy()
@@ -212,7 +238,12 @@ def main():
         "frac_of_mfma_peak": round(tflops / peak, 4),
         "hbm_GBps_algorithmic": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed_region": round(wall, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
     }
+    if cold_ms is not None:
+        out["cold_cache"] = {"flush_bytes": FLUSH_BYTES, "steps": int(cold_ms.size),
+                             "step_ms_p10_p50_p90": [round(float(np.percentile(cold_ms, q)), 5) for q in (10, 50, 90)],
+                             "value_at_p50": round((f_fwd + f_bwd) / (float(np.median(cold_ms)) * 1e-3) / 1e12, 3)}
     if graph is None:
         mlp_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         mlp_flops = 6.0 * cfg.A * cfg.H * cfg.I
