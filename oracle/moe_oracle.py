@@ -206,6 +206,26 @@ def route(logits, k: int):
     return idx, w
 
 
+def route_backward(logits, k: int, d_topk_w):
+    """Gradient with respect to the router logits [T, E] of a loss whose gradient
+    with respect to the top-k weights of ``route(logits, k)`` is d_topk_w [T, k]
+    (LightMoE "MoE training": router gradients; the routing weights are made
+    differentiable with respect to the router output).
+
+    The chosen set is piecewise constant in the logits (its derivative is zero
+    almost everywhere), and on it the weights are the softmax of the chosen
+    logits, whose Jacobian is diag(w) - w w^T.  So for the chosen expert
+    e = topk_idx[t, j]:  d_logits[t, e] = w_j (d_j - sum_i w_i d_i);  every other
+    logit gets 0.  float64.
+    """
+    idx, w = route(logits, k)
+    dw = np.asarray(d_topk_w, dtype=np.float64)
+    g = w * (dw - (w * dw).sum(axis=1, keepdims=True))
+    out = np.zeros(np.shape(logits), dtype=np.float64)
+    np.put_along_axis(out, idx.astype(np.int64), g, axis=1)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Dispatch: expert-major order of the T*k assignments
 # ----------------------------------------------------------------------------
