@@ -3,7 +3,8 @@
 
 One step is one pass of the layer's hot path over one batch of synthetic
 input: routing, dispatch, the grouped-GEMM expert MLP (gate/up + SwiGLU,
-down) and the weighted combine; for the training workload also the backward.
+down) and the weighted combine; for the training workload also the backward
+(expert MLP and router).
 Inputs are resident in HBM before the timed region; weight packing happens at
 load time, outside it.  The timed region (the reported value) does not flush
 caches between steps; its per-step times give p10 / p50 / p90.  With
@@ -155,6 +156,7 @@ def main():
         layer.forward(logits, X, backward_plan=cfg.backward, mlp_events=ev)
         if cfg.backward:
             layer.backward(X, dY)
+            layer.route_backward(cfg.T)
 
     if args.copy_calibration:
         from grouped_gemm_router_amd.profile_tools import COPY_BYTES

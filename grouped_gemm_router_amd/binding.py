@@ -23,7 +23,7 @@ CALL_DISPATCH, CALL_EXPERT_MLP, CALL_BACKWARD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_validate_problem", "moe_workspace_size", "moe_check_device",
            "moe_route", "moe_dispatch", "moe_pack_weights", "moe_mx_quantize", "moe_expert_mlp",
-           "moe_combine", "moe_backward")
+           "moe_combine", "moe_backward", "moe_route_backward")
 
 
 class MoEError(RuntimeError):
@@ -49,6 +49,7 @@ def _load() -> ctypes.CDLL:
         "moe_workspace_size": (ctypes.c_int, [PP, ctypes.c_int, ctypes.POINTER(SZ)]),
         "moe_check_device": (ctypes.c_int, []),
         "moe_route": (ctypes.c_int, [P, I32, I32, I32, P, P, P]),
+        "moe_route_backward": (ctypes.c_int, [P, P, P, I32, I32, I32, P, P]),
         "moe_dispatch": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
         "moe_pack_weights": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "moe_mx_quantize": (ctypes.c_int, [P, I64, I32, P, P, P]),
@@ -121,6 +122,18 @@ def route(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None):
     _expect(topk_w, "topk_w", torch.float32, (T, k))
     _check("moe_route", lib.moe_route(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream()))
     return topk_idx, topk_w
+
+
+def route_backward(topk_idx: torch.Tensor, topk_w: torch.Tensor, d_topk_w: torch.Tensor, E: int, d_logits=None):
+    T, k = topk_idx.shape
+    _expect(topk_idx, "topk_idx", torch.int32)
+    _expect(topk_w, "topk_w", torch.float32, (T, k))
+    _expect(d_topk_w, "d_topk_w", torch.float32, (T, k))
+    d_logits = torch.empty(T, E, dtype=torch.float32, device=topk_idx.device) if d_logits is None else d_logits
+    _expect(d_logits, "d_logits", torch.float32, (T, E))
+    _check("moe_route_backward", lib.moe_route_backward(_ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w), T, E, k,
+                                                        _ptr(d_logits), _stream()))
+    return d_logits
 
 
 def dispatch(topk_idx: torch.Tensor, E: int, out=None, ws=None):

@@ -127,6 +127,16 @@ MOE_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t 
   return from_hip(moe::launch_route(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
 }
 
+MOE_API moe_status moe_route_backward(const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
+                                      int32_t T, int32_t E, int32_t k, float* d_logits, void* stream) {
+  moe_status s = check_route_args(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!topk_idx || !topk_w || !d_topk_w || !d_logits) return MOE_ERR_INVALID_ARG;
+  if ((s = device_ok()) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  return from_hip(moe::launch_route_backward(topk_idx, topk_w, d_topk_w, T, E, k, d_logits, (hipStream_t)stream));
+}
+
 MOE_API moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
                                 int32_t* expert_offsets, int32_t* row_token, int32_t* row_slot,
                                 int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {

@@ -42,6 +42,8 @@ int num_cus();
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         hipStream_t s);
+hipError_t launch_route_backward(const int32_t* idx, const float* w, const float* dw, int T, int E, int k,
+                                 float* dl, hipStream_t s);
 size_t dispatch_ws_bytes(long A, int E);
 // dispatch of T*k <= DISPATCH_SMALL_A slots runs in one workgroup
 constexpr int DISPATCH_SMALL_A = 4096;

@@ -113,6 +113,65 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 }
 
 // ---------------------------------------------------------------------------
+// Router backward (LightMoE "MoE training": router gradients).  On the chosen
+// logits the weights are a softmax, so for e = topk_idx[t, j]
+//   d_logits[t, e] = w_j (d_j - sum_i w_i d_i),
+// and every other logit of the token gets 0.  One wave per token: lane j < k
+// holds slot j; the sum runs over j in ascending order, the same in every lane;
+// lane l writes the logits l, l + 64, ... once each (coalesced, no ordering
+// between stores to one address needed).  Ids outside [0, E) are skipped.
+// ---------------------------------------------------------------------------
+template <int NPL>
+__device__ __forceinline__ void route_backward_token(const int32_t* idx, const float* w, const float* dw, int E,
+                                                     int k, int lane, float* out) {
+  const int my = lane < k ? idx[lane] : -1;
+  const float mw = lane < k ? w[lane] : 0.f, md = lane < k ? dw[lane] : 0.f;
+  const float prod = mw * md;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s += __shfl(prod, j, 64);
+  const float g = mw * (md - s);
+  float v[NPL];
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) v[p] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = __shfl(my, j, 64);
+    const float gj = __shfl(g, j, 64);
+    if (e >= 0 && e < E && (e & 63) == lane) {
+#pragma unroll
+      for (int p = 0; p < NPL; ++p)
+        if ((e >> 6) == p) v[p] = gj;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) {
+    const int e = p * 64 + lane;
+    if (e < E) out[e] = v[p];
+  }
+}
+
+template <int NPL>
+__global__ void __launch_bounds__(256) k_route_backward(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                        const float* __restrict__ dw, int T, int E, int k,
+                                                        float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t o = (size_t)t * k;
+  route_backward_token<NPL>(idx + o, w + o, dw + o, E, k, lane, dl + (size_t)t * E);
+}
+
+hipError_t launch_route_backward(const int32_t* idx, const float* w, const float* dw, int T, int E, int k,
+                                 float* dl, hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64) hipLaunchKernelGGL(k_route_backward<1>, grid, block, 0, s, idx, w, dw, T, E, k, dl);
+  else if (E <= 128) hipLaunchKernelGGL(k_route_backward<2>, grid, block, 0, s, idx, w, dw, T, E, k, dl);
+  else if (E <= 256) hipLaunchKernelGGL(k_route_backward<4>, grid, block, 0, s, idx, w, dw, T, E, k, dl);
+  else if (E <= 512) hipLaunchKernelGGL(k_route_backward<8>, grid, block, 0, s, idx, w, dw, T, E, k, dl);
+  else hipLaunchKernelGGL(k_route_backward<16>, grid, block, 0, s, idx, w, dw, T, E, k, dl);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch.  The T*k slots are cut into chunks of DISPATCH_CHUNK (one block,
 // four waves of DISPATCH_CHUNK / 4 consecutive slots each).  Inside a wave, 64 slots are handled
 // at a time: ten ballots over the bits of the expert id give every lane the

@@ -97,3 +97,11 @@ class MoELayer:
         return B.backward(X, dY, pl["topk_w"], pl["row_token"], pl["row_slot"], pl["slot_row"], pl["offsets"],
                           self.W_gate, self.W_up, self.W_down, self.Wg_t, self.Wu_t, out=pl["grads"],
                           ws=pl["ws_bwd"])
+
+    def route_backward(self, T: int):
+        """Gradient with respect to the router logits [T, E] fp32, from the d(top-k weights) of the
+        last backward over T tokens."""
+        pl = self.plan(T, True)
+        if "d_logits" not in pl:
+            pl["d_logits"] = torch.empty(T, self.E, dtype=torch.float32, device=self.device)
+        return B.route_backward(pl["topk_idx"], pl["topk_w"], pl["grads"][4], self.E, pl["d_logits"])

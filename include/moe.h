@@ -12,6 +12,7 @@
  *   moe_expert_mlp  grouped GEMM gate/up + SwiGLU, grouped GEMM down
  *   moe_combine     weighted sum of each token's k expert rows
  *   moe_backward    dX, dW_gate, dW_up, dW_down, d(top-k weights)
+ *   moe_route_backward  d(router logits) from d(top-k weights)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -99,6 +100,24 @@ MOE_API moe_status moe_check_device(void);
  */
 MOE_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
                              int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Router backward (LightMoE "MoE training": deterministic router-gradient
+ * kernels; the routing weights are made differentiable with respect to the
+ * router output).  Gradient with respect to the logits of a loss whose gradient
+ * with respect to the top-k weights of moe_route is d_topk_w.  On the chosen
+ * logits the weights are a softmax, and the chosen set is piecewise constant,
+ * so for e = topk_idx[t, j]:
+ *   d_logits[t, e] = topk_w[t,j] * (d_topk_w[t,j] - sum_i topk_w[t,i] * d_topk_w[t,i])
+ * (the sum in fp32 over i ascending), and every other element of row t is 0.
+ *   topk_idx [T, k] int32, topk_w [T, k] fp32: as moe_route wrote them
+ *            (ids outside [0, E) are skipped)
+ *   d_topk_w [T, k] fp32 in (e.g. the d_topk_w of moe_backward)
+ *   d_logits [T, E] fp32 out, every element written
+ */
+MOE_API moe_status moe_route_backward(const int32_t* topk_idx, const float* topk_w,
+                                      const float* d_topk_w, int32_t T, int32_t E, int32_t k,
+                                      float* d_logits, void* stream);
 
 /*
  * Expert-major dispatch (LigerCute "Forward pass": routed tokens are sorted;

@@ -103,3 +103,7 @@ def test_calls_reject_bad_arguments_before_touching_the_device():
     assert lib.moe_mx_quantize(v, 4, 48, v, v, None) == 2
     assert lib.moe_pack_weights(v, 2, 100, 64, v, None) == 2
     assert lib.moe_backward(ctypes.byref(pm), *([v] * 17), None, 0, None) == 2
+    # router backward: null pointers, k > E, E beyond the limit
+    assert lib.moe_route_backward(None, v, v, 4, 8, 2, v, None) == 1
+    assert lib.moe_route_backward(v, v, v, 4, 8, 9, v, None) == 1
+    assert lib.moe_route_backward(v, v, v, 4, 2048, 2, v, None) == 2

@@ -89,6 +89,14 @@ def test_backward_full_size_sampled():
     rdX, rdwt = orc.backward_tokens(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), tokens)
     check_close(to_f64(dX[torch.from_numpy(tokens).cuda()]), rdX, "dX[sampled tokens]")
     check_close(dtw.cpu().numpy()[tokens], rdwt, "d_topk_w[sampled tokens]")
+    # router backward on the same tokens (the layer's chain vs the oracle's)
+    dlog = layer.route_backward(cfg.T).cpu().numpy().astype(np.float64)[tokens]
+    rdl = orc.route_backward(logits[tokens], cfg.k, rdwt)
+    lim = np.zeros_like(rdl)
+    ww = w[tokens]
+    np.put_along_axis(lim, idx[tokens].astype(np.int64),
+                      ww * (2e-2 + 4e-2 * np.abs(rdwt).max(axis=1, keepdims=True)) + 1e-6, axis=1)
+    assert np.all(np.abs(dlog - rdl) <= lim), np.abs(dlog - rdl).max()
     experts = [0, int(rng.integers(1, cfg.E - 1)), cfg.E - 1]
     ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), experts=experts, want_dx=False,
                        E=cfg.E)

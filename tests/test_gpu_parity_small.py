@@ -147,6 +147,37 @@ def test_mx_quantize_bit_exact():
 
 
 # ------------------------------------------------------------------------------------------
+# router backward
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (32, 256, 8), (409, 512, 10), (40, 6, 6), (97, 1024, 32),
+                                   (5, 64, 1), (130, 100, 7)])
+def test_route_backward_vs_oracle(T, E, k):
+    """The kernel on the oracle's inputs: d_topk_w drawn here, the same array for both sides."""
+    B = _B()
+    _say("route backward", T, E, k)
+    rng = np.random.default_rng(T * 7 + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    dw = (rng.standard_normal((T, k)) * 10.0).astype(np.float32)
+    idx, w = B.route(torch.from_numpy(logits).cuda(), k)
+    dl = B.route_backward(idx, w, torch.from_numpy(dw).cuda(), E)
+    dl2 = B.route_backward(idx, w, torch.from_numpy(dw).cuda(), E)
+    torch.cuda.synchronize()
+    ref = orc.route_backward(logits, k, dw.astype(np.float64))
+    got = dl.cpu().numpy().astype(np.float64)
+    # fp32 arithmetic on fp32 inputs: a few ulps of the row's largest term
+    scale = np.abs(dw).max(axis=1, keepdims=True)
+    assert np.all(np.abs(got - ref) <= 1e-5 * scale + 1e-5 * np.abs(ref)), np.abs(got - ref).max()
+    assert np.array_equal(got == 0, ref == 0)            # unchosen logits are exactly zero
+    assert np.array_equal(dl.cpu().numpy().view(np.int32), dl2.cpu().numpy().view(np.int32))
+
+
+def route_grad_tolerance(w, dw_ref):
+    """Bound on d_logits when d_topk_w carries the layer tolerance a + r|ref| (a = 1e-2, r = 2e-2):
+    w_j (|delta d_j| + |delta s|) <= w_j (2a + 2r max_i |d_i|)."""
+    return w * (2e-2 + 4e-2 * np.abs(dw_ref).max(axis=1, keepdims=True)) + 1e-6
+
+
+# ------------------------------------------------------------------------------------------
 # forward
 # ------------------------------------------------------------------------------------------
 def _run_forward(cfg, Wg, Wu, Wd, logits, X):
@@ -248,6 +279,12 @@ def test_backward_small_vs_oracle(cfg):
     ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), E=cfg.E)
     check_close(to_f64(dX), ref["dX"], "dX")
     check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w")
+    # router backward chained on the layer's d_topk_w, against the oracle's chain
+    dlog = layer.route_backward(cfg.T).cpu().numpy().astype(np.float64)
+    rdl = orc.route_backward(logits, cfg.k, ref["d_topk_w"])
+    lim = np.zeros_like(rdl)
+    np.put_along_axis(lim, idx.astype(np.int64), route_grad_tolerance(w, ref["d_topk_w"]), axis=1)
+    assert np.all(np.abs(dlog - rdl) <= lim), np.abs(dlog - rdl).max()
     g = {"dWg": to_f64(dWg), "dWu": to_f64(dWu), "dWd": to_f64(dWd)}
     for key in ("dWg", "dWu", "dWd"):
         for e in range(cfg.E):
