@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--cold-cache", action="store_true",
                     help="also time steps after reading 512 MiB (L2 and Infinity Cache evicted), each step alone")
     ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count T (sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -133,7 +134,7 @@ def main():
     from grouped_gemm_router_amd import workloads as wl
     from grouped_gemm_router_amd.layer import MoELayer
 
-    cfg = wl.config(args.workload)
+    cfg = wl.config(args.workload) if args.tokens is None else wl.config(args.workload, T=args.tokens)
     logits_np, X_np = wl.make_logits(cfg), wl.make_x(cfg)
     dY_np = wl.make_dy(cfg) if cfg.backward else None
     full_weights = cfg.E * cfg.H * cfg.I <= 128 * 4096 * 1024

@@ -14,6 +14,9 @@ namespace moe {
 #endif
 // row-grouped GEMMs: 256 x 256 tiles, direct-to-LDS loads, 128 KB of LDS stages
 using CfgRows = RowCfg<256, 256, 2, MOE_ROWS_WAVES_N, MOE_ROWS_BK, (MOE_ROWS_BK == 32 ? 4 : 2)>;
+// remainders of at most 128 rows of an expert (forward GEMMs): 64 x 256 tiles, 8 waves
+// side by side, three 40 KB stages
+using CfgTail = RowCfg<64, 256, 1, 8, 64, 3>;
 
 // ------------------------------------------------------------------------
 // Row sources of the direct-to-LDS row-grouped GEMMs: a wave-uniform base and
@@ -90,17 +93,19 @@ struct RSrcGateUpWT {    // [W_gate | W_up] [E, H, I] read as [E, N = H, K = 2I]
 // ------------------------------------------------------------------------
 // Ops: schedule + loaders + epilogue of each GEMM
 // ------------------------------------------------------------------------
-template <class C, class SrcA_, class SrcB_>
+// PART: which rows of each expert the schedule covers (all, or the full / tail
+// split of 256-row blocks).
+template <class C, class SrcA_, class SrcB_, int PART = ROWS_ALL>
 struct RowOpsBase {
   using SrcA = SrcA_;
   using SrcB = SrcB_;
-  using Sched = RowGroups<C::BM, C::BN, C::NT>;
+  using Sched = RowGroups<C::BM, C::BN, C::NT, PART, (PART == ROWS_ALL ? C::BM : 256)>;
 };
 
 // h = bf16(silu(X Wg) * (X Wu))
-template <class C>
-struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>>::Sched& s,
+template <class C, int PART = ROWS_ALL>
+struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
@@ -138,9 +143,9 @@ __device__ __forceinline__ void store_rows_f32(float* base, int ld, int ncols, c
 }
 
 // O = bf16(h Wd)
-template <class C>
-struct FwdDownOps : RowOpsBase<C, RSrcH, RSrcDownW> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcH, RSrcDownW>::Sched& s,
+template <class C, int PART = ROWS_ALL>
+struct FwdDownOps : RowOpsBase<C, RSrcH, RSrcDownW, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcH, RSrcDownW, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, p.I, pre, red);
   }
@@ -297,8 +302,13 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT> {
     rows_gemm_body<CfgRows, OPS<CfgRows>, GemmArgs>(p);                            \
   }
 
-MOE_ROWS_KERNEL(k_fwd_gateup, FwdGateUpOps)
-MOE_ROWS_KERNEL(k_fwd_down, FwdDownOps)
+#define MOE_ROWS_SPLIT_KERNEL(NAME, OPS)                                                              \
+  __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {                             \
+    rows_gemm_split_body<CfgRows, CfgTail, OPS<CfgRows, ROWS_FULL>, OPS<CfgTail, ROWS_TAIL>, GemmArgs>(p); \
+  }
+
+MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps)
 MOE_ROWS_KERNEL(k_bwd_p, BwdPOps)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
 MOE_ROWS_KERNEL(k_bwd_dx_rows, BwdDXOps)

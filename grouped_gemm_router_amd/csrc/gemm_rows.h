@@ -211,10 +211,15 @@ struct RowEpiLds {
   static constexpr int BYTES = C::STAGE * 16 / C::NW;
 };
 
+// LDS of the schedule: prefix of per-expert tile counts (up to 1024 experts) and the
+// block scan's partial sums.
+constexpr int SCHED_LDS_INTS = 1024 + 1 + 16 + 1;
+
+// Every tile of Ops' schedule, with the stages at smem (C::NST * C::STAGE uint4) and the
+// schedule's scratch at sched_lds.
 template <class C, class Ops, class P>
-__device__ __forceinline__ void rows_gemm_body(const P& p) {
-  __shared__ uint4 smem[C::NST * C::STAGE];
-  __shared__ int sched_lds[1024 + 1 + C::NT / 64 + 1];
+__device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sched_lds) {
+  static_assert(C::NT / 64 <= 16, "schedule scratch");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   using AL = DirectRows<C, C::BM, typename Ops::SrcA, P>;
@@ -293,6 +298,27 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
     // the scratch stage is the next tile's last stage: all waves must be done with it
     __syncthreads();
   }
+}
+
+template <class C, class Ops, class P>
+__device__ __forceinline__ void rows_gemm_body(const P& p) {
+  __shared__ uint4 smem[C::NST * C::STAGE];
+  __shared__ int sched_lds[SCHED_LDS_INTS];
+  rows_gemm_tiles<C, Ops, P>(p, smem, sched_lds);
+}
+
+// Two passes over the experts' rows in one kernel: the full 256-row tiles (and
+// remainders above 128 rows) with configuration CF, then the remainders of at
+// most 128 rows in CT's shorter tiles, with the same LDS.  A workgroup that is
+// done with its full tiles goes on to its share of the short ones.
+template <class CF, class CT, class OpsF, class OpsT, class P>
+__device__ __forceinline__ void rows_gemm_split_body(const P& p) {
+  static_assert(CT::NST * CT::STAGE <= CF::NST * CF::STAGE && CT::NT == CF::NT, "shared LDS and block");
+  __shared__ uint4 smem[CF::NST * CF::STAGE];
+  __shared__ int sched_lds[SCHED_LDS_INTS];
+  rows_gemm_tiles<CF, OpsF, P>(p, smem, sched_lds);
+  __syncthreads();
+  rows_gemm_tiles<CT, OpsT, P>(p, smem, sched_lds);
 }
 
 // Stages this wave's bf16 output, one 32-row fragment row-block at a time,

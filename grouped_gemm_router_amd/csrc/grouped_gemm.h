@@ -60,9 +60,27 @@ __device__ int block_exclusive_scan(int v, int* red /* NT/64 + 1 ints */) {
 // ---------------------------------------------------------------------------
 // Schedules
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NT>
+// Which rows of each expert a RowGroups schedule covers (n rows = q * BMF + r, r < BMF):
+//   ROWS_ALL:  all n rows in tiles of BM;
+//   ROWS_FULL: the q full blocks of BMF = BM rows, plus the remainder when r > BMF / 2 (one
+//              partly filled tile);
+//   ROWS_TAIL: the remainder r when 0 < r <= BMF / 2, in tiles of BM (< BMF) rows.
+// A FULL and a TAIL schedule with the same BMF cover every row exactly once.
+enum RowPart { ROWS_ALL = 0, ROWS_FULL = 1, ROWS_TAIL = 2 };
+
+template <int BM, int BN, int NT, int PART = ROWS_ALL, int BMF = BM>
 struct RowGroups {
+  static_assert(PART != ROWS_FULL || BMF == BM, "full tiles are BMF rows");
+  static_assert(PART != ROWS_TAIL || (BM < BMF && (BMF / 2) % BM == 0), "tail tiles split half a full tile");
   static constexpr int MAX_E = 1024;
+  // tiles of expert e with n rows, and the first of its rows they cover
+  __device__ static int count(int n) {
+    if constexpr (PART == ROWS_ALL) return (n + BM - 1) / BM;
+    const int q = n / BMF, r = n - q * BMF;
+    if constexpr (PART == ROWS_FULL) return q + (r > BMF / 2 ? 1 : 0);
+    return r > BMF / 2 ? 0 : (r + BM - 1) / BM;
+  }
+  __device__ static int first_row(int n) { return PART == ROWS_TAIL ? n / BMF * BMF : 0; }
   int* prefix;   // LDS [E+1]: exclusive prefix of per-expert m-tile counts
   int E, ntiles_n, total, K;
   const int32_t* offsets;
@@ -79,7 +97,7 @@ struct RowGroups {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int e = threadIdx.x * 4 + i;
-      cnt[i] = (e < E) ? (offs[e + 1] - offs[e] + BM - 1) / BM : 0;
+      cnt[i] = (e < E) ? count(offs[e + 1] - offs[e]) : 0;
       sum += cnt[i];
     }
     int ex = block_exclusive_scan<NT>(sum, red);
@@ -105,7 +123,8 @@ struct RowGroups {
     // every lane computes the same tile: keep its fields in scalar registers
     Tile tl;
     tl.e = __builtin_amdgcn_readfirstlane(lo);
-    tl.m0 = __builtin_amdgcn_readfirstlane(offsets[lo] + (mt - prefix[lo]) * BM);
+    tl.m0 = __builtin_amdgcn_readfirstlane(offsets[lo] + first_row(offsets[lo + 1] - offsets[lo]) +
+                                           (mt - prefix[lo]) * BM);
     tl.m_end = __builtin_amdgcn_readfirstlane(offsets[lo + 1]);
     tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
     tl.nt = __builtin_amdgcn_readfirstlane(nt);
