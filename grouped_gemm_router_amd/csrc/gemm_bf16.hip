@@ -159,9 +159,9 @@ struct FwdDownOps : RowOpsBase<C, RSrcH, RSrcDownW, PART> {
 };
 
 // P = dY[token] W_down^T (fp32)
-template <class C>
-struct BwdPOps : RowOpsBase<C, RSrcDY, RSrcDownWT> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcDY, RSrcDownWT>::Sched& s,
+template <class C, int PART = ROWS_ALL>
+struct BwdPOps : RowOpsBase<C, RSrcDY, RSrcDownWT, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDY, RSrcDownWT, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.I, p.H, pre, red);
   }
@@ -180,20 +180,21 @@ __device__ __forceinline__ void split4(const float (&v)[4], uint2& hi, uint2& lo
 }
 
 // Recompute G, U; with P give h, the router-weight partial sums <h, P>, dg and du.
-// A wave owns 32 intermediate columns of 128 rows.  P is read one 32-row block
-// ahead of its use; the five bf16 outputs (h, dg and du with their remainders) of each
-// 32-row block go through the wave's LDS scratch and leave as whole 64-byte row
-// segments (16 bytes per lane).
-template <class C>
-struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>>::Sched& s,
+// A wave owns 32 intermediate columns of WTM rows.  P is read one 32-row block
+// ahead of its use; the five bf16 outputs (h, dg and du with their remainders) of
+// each 32-row block go through the wave's LDS scratch (NSLOT staged blocks at a
+// time) and leave as whole 64-byte row segments (16 bytes per lane).
+template <class C, int PART = ROWS_ALL>
+struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
   // one staged 32 x 32 bf16 block: 64-byte rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
   static constexpr int OUT = 32 * 64;
+  static constexpr int NSLOT = RowEpiLds<C>::BYTES / OUT < 4 ? RowEpiLds<C>::BYTES / OUT : 4;
   static_assert(C::FN * 16 == 32, "a wave owns 32 intermediate columns");
-  static_assert(4 * OUT <= RowEpiLds<C>::BYTES, "staging area too small");
+  static_assert(NSLOT >= 1, "staging area too small");
 
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t* wlds) {
@@ -227,7 +228,18 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
       auto slot = [&](int o, int fn, int q) {
         return reinterpret_cast<uint2*>(wlds + o * OUT + rl * 64 + (((2 * fn + q) ^ ((rl >> 2) & 3)) * 16) + h * 8);
       };
-      uint2 ul[C::FN][2];                             // staged after the first four blocks leave
+      // outputs 0..4: h, dg, dg remainder, du, du remainder; with four slots the first four
+      // are staged as they are computed and the last waits in registers, with fewer all wait
+      constexpr int HELD = NSLOT >= 4 ? 1 : 5;
+      uint2 held[HELD][C::FN][2];
+      auto emit = [&](int o, int fn, int q, uint2 v) {
+        if constexpr (NSLOT >= 4) {
+          if (o < 4) *slot(o, fn, q) = v;
+          else held[0][fn][q] = v;
+        } else {
+          held[o][fn][q] = v;
+        }
+      };
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
@@ -247,12 +259,13 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
           }
           if (cv) {
             uint2 hi, lo;
-            *slot(0, fn, q) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            emit(0, fn, q, make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])));
             split4(dg, hi, lo);
-            *slot(1, fn, q) = hi;
-            *slot(2, fn, q) = lo;
-            split4(du, hi, ul[fn][q]);
-            *slot(3, fn, q) = hi;
+            emit(1, fn, q, hi);
+            emit(2, fn, q, lo);
+            split4(du, hi, lo);
+            emit(3, fn, q, hi);
+            emit(4, fn, q, lo);
           }
         }
       // the other half of this row's columns sits in lane ^ 32
@@ -260,31 +273,44 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>> {
       if (r < t.m_end && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
       if (!cv) continue;
       const int row0 = t.m0 + wm * C::WTM + fm * 32;
-      auto flush = [&](int o, uint16_t* out, int ld) {
+      auto flush = [&](int s, int o) {
+        uint16_t* out = (o == 0 ? p.Hrows : (o == 1 || o == 3) ? p.dGU : p.dGU_lo) + (o >= 3 ? p.I : 0);
+        const int ld = o == 0 ? p.I : 2 * p.I;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int idx = i * 64 + lane, rr = idx >> 2, ch = idx & 3;
-          const uint4 v = *reinterpret_cast<const uint4*>(wlds + o * OUT + rr * 64 + ((ch ^ ((rr >> 2) & 3)) * 16));
+          const uint4 v = *reinterpret_cast<const uint4*>(wlds + s * OUT + rr * 64 + ((ch ^ ((rr >> 2) & 3)) * 16));
           if (row0 + rr < t.m_end) *reinterpret_cast<uint4*>(out + (size_t)(row0 + rr) * ld + col0 + ch * 8) = v;
         }
       };
-      flush(0, p.Hrows, p.I);
-      flush(1, p.dGU, 2 * p.I);
-      flush(2, p.dGU_lo, 2 * p.I);
-      flush(3, p.dGU + p.I, 2 * p.I);
+      auto put = [&](int s, const uint2 (&v)[C::FN][2]) {
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
+        for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) *slot(0, fn, q) = ul[fn][q];
-      flush(0, p.dGU_lo + p.I, 2 * p.I);
+          for (int q = 0; q < 2; ++q) *slot(s, fn, q) = v[fn][q];
+      };
+      if constexpr (NSLOT >= 4) {
+#pragma unroll
+        for (int o = 0; o < 4; ++o) flush(o, o);
+        put(0, held[0]);
+        flush(0, 4);
+      } else {
+#pragma unroll
+        for (int o0 = 0; o0 < 5; o0 += NSLOT) {
+#pragma unroll
+          for (int o = o0; o < o0 + NSLOT && o < 5; ++o) put(o - o0, held[o]);
+#pragma unroll
+          for (int o = o0; o < o0 + NSLOT && o < 5; ++o) flush(o - o0, o);
+        }
+      }
     }
   }
 };
 
 // dXr = [dg | du] [W_gate | W_up]^T (fp32 rows)
-template <class C>
-struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcDGU, RSrcGateUpWT>::Sched& s,
+template <class C, int PART = ROWS_ALL>
+struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, 2 * p.I, pre, red);
   }
@@ -302,16 +328,16 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT> {
     rows_gemm_body<CfgRows, OPS<CfgRows>, GemmArgs>(p);                            \
   }
 
-#define MOE_ROWS_SPLIT_KERNEL(NAME, OPS)                                                              \
+#define MOE_ROWS_SPLIT_KERNEL(NAME, OPS, CT)                                                         \
   __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {                             \
-    rows_gemm_split_body<CfgRows, CfgTail, OPS<CfgRows, ROWS_FULL>, OPS<CfgTail, ROWS_TAIL>, GemmArgs>(p); \
+    rows_gemm_split_body<CfgRows, CT, OPS<CfgRows, ROWS_FULL>, OPS<CT, ROWS_TAIL>, GemmArgs>(p);      \
   }
 
-MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps)
-MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps)
-MOE_ROWS_KERNEL(k_bwd_p, BwdPOps)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps, CfgTail)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps, CfgTail)
+MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps, CfgTail)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
-MOE_ROWS_KERNEL(k_bwd_dx_rows, BwdDXOps)
+MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps, CfgTail)
 
 template <class C>
 static int row_grid(const GemmArgs& a, int N) {
