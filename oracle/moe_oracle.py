@@ -42,6 +42,8 @@ design notes of the repository):
   the lowest expert index; weights are the softmax restricted to the k chosen
   logits, which equals softmax over all E renormalised over the k.
 * SwiGLU: h = silu(G) * U with silu(x) = x * sigmoid(x); W_gate feeds silu.
+  The other gated activations (bounded SwiGLU, SwiGLU-OAI, GeGLU, ReGLU) are
+  read from their public definitions (see ``activation``).
 * Rounding points: h, the expert outputs O and the layer output Y are rounded
   to bf16 (round-to-nearest-even); accumulation is exact (float64 here).
 * Combine adds the k weighted expert rows of a token in slot order
@@ -274,10 +276,81 @@ def _expert_getter(W):
     return lambda e: _as_f64(W[e])
 
 
-def expert_forward_rows(x_rows, wg, wu, wd, mxfp8: bool = False, exact: bool = False):
+# ----------------------------------------------------------------------------
+# Gated activations h = f(G, U) (LightMoE "Highlights": SwiGLU-OAI, bounded
+# SwiGLU, GeGLU and ReGLU epilogues; "MoE inference": an activation clamp of 10
+# for one model family).  The pages name the variants but print no formulas;
+# these are the public definitions of the model families that use them:
+#   swiglu        silu(G) U
+#   swiglu_clamp  silu(min(G, c)) clamp(U, -c, c)                 (bounded SwiGLU)
+#   swiglu_oai    g sigmoid(1.702 g) (u + 1), g = min(G, c), u = clamp(U, -c, c)
+#   geglu         gelu(G) U, gelu(x) = x Phi(x) with the normal CDF Phi (erf form)
+#   reglu         max(G, 0) U
+# ----------------------------------------------------------------------------
+ACTIVATIONS = ("swiglu", "swiglu_clamp", "swiglu_oai", "geglu", "reglu")
+OAI_ALPHA = 1.702
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _clamps(G, U, act, limit):
+    if act in ("swiglu_clamp", "swiglu_oai"):
+        if not (limit and limit > 0):
+            raise ValueError(f"{act} needs a positive limit")
+        return np.minimum(G, limit), np.clip(U, -limit, limit)
+    return G, U
+
+
+def activation(G, U, act: str = "swiglu", limit=None):
+    """h = f(G, U) elementwise, float64."""
+    G = np.asarray(G, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    g, u = _clamps(G, U, act, limit)
+    if act in ("swiglu", "swiglu_clamp"):
+        return silu(g) * u
+    if act == "swiglu_oai":
+        return g * _sigmoid(OAI_ALPHA * g) * (u + 1.0)
+    if act == "geglu":
+        from scipy.special import ndtr
+        return G * ndtr(G) * U
+    if act == "reglu":
+        return np.maximum(G, 0.0) * U
+    raise ValueError(act)
+
+
+def activation_grads(G, U, act: str = "swiglu", limit=None):
+    """(df/dG, df/dU) elementwise, float64 (a clamp passes the gradient where its
+    argument lies inside the bounds, the bounds included)."""
+    G = np.asarray(G, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    g, u = _clamps(G, U, act, limit)
+    if act in ("swiglu_clamp", "swiglu_oai"):
+        pg = (G <= limit).astype(np.float64)
+        pu = ((U >= -limit) & (U <= limit)).astype(np.float64)
+    else:
+        pg = pu = 1.0
+    if act in ("swiglu", "swiglu_clamp"):
+        return u * dsilu(g) * pg, silu(g) * pu
+    if act == "swiglu_oai":
+        s = _sigmoid(OAI_ALPHA * g)
+        return (s + OAI_ALPHA * g * s * (1.0 - s)) * (u + 1.0) * pg, g * s * pu
+    if act == "geglu":
+        from scipy.special import ndtr
+        phi = np.exp(-0.5 * G * G) / np.sqrt(2.0 * np.pi)
+        return (ndtr(G) + G * phi) * U, G * ndtr(G)
+    if act == "reglu":
+        return (G > 0).astype(np.float64) * U, np.maximum(G, 0.0)
+    raise ValueError(act)
+
+
+def expert_forward_rows(x_rows, wg, wu, wd, mxfp8: bool = False, exact: bool = False,
+                        act: str = "swiglu", limit=None):
     """One expert's MLP on rows x_rows [n, H] (float64 values).
 
-    G = x Wg, U = x Wu, h = bf16(silu(G) * U), O = bf16(h Wd).  With
+    G = x Wg, U = x Wu, h = bf16(f(G, U)), O = bf16(h Wd), f = ``activation(.., act, limit)``
+    (SwiGLU by default).  With
     ``mxfp8`` the GEMM operands x, W and h are the values their MXFP8 (32-long
     blocks along the contraction axis) representation holds.  ``exact``
     skips every rounding (used to check derivatives).
@@ -290,7 +363,7 @@ def expert_forward_rows(x_rows, wg, wu, wd, mxfp8: bool = False, exact: bool = F
         wd = mx_fake_quant(wd.T).T
     G = x_rows @ wg
     U = x_rows @ wu
-    h = silu(G) * U
+    h = activation(G, U, act, limit)
     if not exact:
         h = bf16_round(h)
     hq = mx_fake_quant(h) if mxfp8 else h
@@ -301,7 +374,7 @@ def expert_forward_rows(x_rows, wg, wu, wd, mxfp8: bool = False, exact: bool = F
 
 
 def expert_mlp(X, row_token, offsets, W_gate, W_up, W_down, mxfp8: bool = False,
-               experts=None, exact: bool = False):
+               experts=None, exact: bool = False, act: str = "swiglu", limit=None):
     """Expert-major expert MLP over all routed rows.
 
     X: [T, H] (bf16 bits or values); row_token / offsets from ``dispatch``;
@@ -324,7 +397,8 @@ def expert_mlp(X, row_token, offsets, W_gate, W_up, W_down, mxfp8: bool = False,
         if hi == lo:
             continue
         rows = Xv[np.asarray(row_token[lo:hi], dtype=np.int64)]
-        _, _, he, Oe = expert_forward_rows(rows, gg(e), gu(e), gd(e), mxfp8=mxfp8, exact=exact)
+        _, _, he, Oe = expert_forward_rows(rows, gg(e), gu(e), gd(e), mxfp8=mxfp8, exact=exact, act=act,
+                                           limit=limit)
         h[lo:hi] = he
         O[lo:hi] = Oe
     return h, O
@@ -342,7 +416,7 @@ def combine(O, slot_row, topk_w, exact: bool = False):
 
 
 def layer_forward_tokens(X, topk_idx, topk_w, W_gate, W_up, W_down, tokens,
-                         mxfp8: bool = False, exact: bool = False):
+                         mxfp8: bool = False, exact: bool = False, act: str = "swiglu", limit=None):
     """The layer output Y for the listed tokens only, straight from the
     per-token definition (no dispatch): Y[t] = bf16(sum_j w[t,j] * MLP_e(x_t))."""
     Xv = _as_f64(X)
@@ -358,7 +432,8 @@ def layer_forward_tokens(X, topk_idx, topk_w, W_gate, W_up, W_down, tokens,
     contrib = {}
     for e, items in by_expert.items():
         rows = Xv[[t for _, t, _ in items]]
-        _, _, _, Oe = expert_forward_rows(rows, gg(e), gu(e), gd(e), mxfp8=mxfp8, exact=exact)
+        _, _, _, Oe = expert_forward_rows(rows, gg(e), gu(e), gd(e), mxfp8=mxfp8, exact=exact, act=act,
+                                          limit=limit)
         for (n, t, j), o in zip(items, Oe):
             contrib[(n, j)] = w[t, j] * o
     for n in range(len(tokens)):
@@ -381,34 +456,37 @@ def dsilu(x):
     return s * (1.0 + x * (1.0 - s))
 
 
-def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = False):
+def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = False, act: str = "swiglu",
+                         limit=None):
     """Backward of one expert for its rows.
 
     x_rows, dy_rows: [n, H] token inputs and output gradients of the rows;
     w_rows: [n] routing weights.  G, U, h are recomputed as in the forward.
-    P = dY W_down^T; dwt = <h, P>; dh = w P; du = dh * silu(G);
-    dg = dh * U * silu'(G); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
+    P = dY W_down^T; dwt = <h, P>; dh = w P; dg = dh * df/dG, du = dh * df/dU
+    (SwiGLU: du = dh * silu(G), dg = dh * U * silu'(G)); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
     dWg = x^T dg, dWu = x^T du, dWd = h^T dO (not yet rounded).
     Returns dict of float64 arrays.
     """
     rnd = (lambda a: a) if exact else bf16_round
     G = x_rows @ wg
     U = x_rows @ wu
-    h = silu(G) * U
+    h = activation(G, U, act, limit)
     if not exact:
         h = bf16_round(h)
     P = dy_rows @ wd.T
     dwt = np.sum(h * P, axis=1)
     dh = w_rows[:, None] * P
-    du = dh * silu(G)
-    dg = dh * U * dsilu(G)
+    fg, fu = activation_grads(G, U, act, limit)
+    du = dh * fu
+    dg = dh * fg
     dO = rnd(w_rows[:, None] * dy_rows)
     dXr = dg @ wg.T + du @ wu.T
     return {"dwt": dwt, "dXr": dXr, "dWg": x_rows.T @ dg, "dWu": x_rows.T @ du,
             "dWd": h.T @ dO, "dg": dg, "du": du, "h": h}
 
 
-def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact: bool = False,
+def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact: bool = False, act: str = "swiglu",
+             limit=None,
              want_dx: bool = True, E: int | None = None):
     """Gradients of the layer.
 
@@ -440,7 +518,7 @@ def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact:
             dW["dWu"][e] = np.zeros((H, I))
             dW["dWd"][e] = np.zeros((I, H))
             continue
-        r = expert_backward_rows(Xv[tt], dYv[tt], w[tt, jj], gg(e), gu(e), gd(e), exact=exact)
+        r = expert_backward_rows(Xv[tt], dYv[tt], w[tt, jj], gg(e), gu(e), gd(e), exact=exact, act=act, limit=limit)
         dW["dWg"][e] = rnd(r["dWg"])
         dW["dWu"][e] = rnd(r["dWu"])
         dW["dWd"][e] = rnd(r["dWd"])
@@ -456,7 +534,8 @@ def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact:
     return out
 
 
-def backward_tokens(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, tokens, exact: bool = False):
+def backward_tokens(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, tokens, exact: bool = False,
+                    act: str = "swiglu", limit=None):
     """dX and d_topk_w of the listed tokens only, straight from the per-row
     definition (same formulas as ``backward``).  Returns (dX [n, H], dwt [n, k])."""
     rnd = (lambda a: a) if exact else bf16_round
@@ -472,7 +551,8 @@ def backward_tokens(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, tokens, exact
         acc = np.zeros(Xv.shape[1])
         for j in range(k):
             e = int(idx[t, j])
-            r = expert_backward_rows(Xv[t:t + 1], dYv[t:t + 1], w[t, j:j + 1], gg(e), gu(e), gd(e), exact=exact)
+            r = expert_backward_rows(Xv[t:t + 1], dYv[t:t + 1], w[t, j:j + 1], gg(e), gu(e), gd(e), exact=exact,
+                                     act=act, limit=limit)
             acc = acc + r["dXr"][0]
             dwt[n, j] = r["dwt"][0]
         dX[n] = acc
@@ -502,9 +582,9 @@ def mx_requant_delta(h_exact, rel_eps: float = 2.0 ** -14):
     return base, np.maximum(np.abs(up - base), np.abs(dn - base))
 
 
-def mx_down_ambiguity(G, U, wd):
-    """For O = MXFP8(h) W_down with h = bf16(silu(G) U): per element of O, the
+def mx_down_ambiguity(G, U, wd, act: str = "swiglu", limit=None):
+    """For O = MXFP8(h) W_down with h = bf16(f(G, U)): per element of O, the
     largest change another valid rounding of the requantised h can cause
     (|delta| @ |W_down as MXFP8|, delta from ``mx_requant_delta``)."""
-    _, delta = mx_requant_delta(silu(G) * np.asarray(U, dtype=np.float64))
+    _, delta = mx_requant_delta(activation(G, U, act, limit))
     return delta @ np.abs(mx_fake_quant(np.asarray(wd, dtype=np.float64).T).T)
