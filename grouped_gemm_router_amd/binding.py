@@ -19,6 +19,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE", 3: "MOE_ERR_WORKSPACE",
           4: "MOE_ERR_UNSUPPORTED_DEVICE", 5: "MOE_ERR_HIP"}
 DTYPE = {"bf16": 0, "mxfp8": 1}
+ACT = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_oai": 2, "geglu": 3, "reglu": 4}
 CALL_DISPATCH, CALL_EXPERT_MLP, CALL_BACKWARD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_validate_problem", "moe_workspace_size", "moe_check_device",
@@ -34,7 +35,8 @@ class MoEError(RuntimeError):
 
 class moe_problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
-                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("act_limit", ctypes.c_float)]
 
 
 def _load() -> ctypes.CDLL:
@@ -90,8 +92,8 @@ def _expect(t, name, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def problem(T, H, I, E, k, dtype="bf16") -> moe_problem:
-    return moe_problem(T, H, I, E, k, DTYPE[dtype])
+def problem(T, H, I, E, k, dtype="bf16", activation="swiglu", act_limit=0.0) -> moe_problem:
+    return moe_problem(T, H, I, E, k, DTYPE[dtype], ACT[activation], float(act_limit or 0.0))
 
 
 def validate_problem(p: moe_problem) -> int:
@@ -174,7 +176,8 @@ def mx_quantize(x: torch.Tensor):
     return q, s
 
 
-def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=None, O_rows=None, ws=None):
+def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=None, O_rows=None, ws=None,
+               activation="swiglu", act_limit=0.0):
     """Expert MLP over the dispatched rows.  bf16 weights [E, I, H] / [E, H, I]
     (pack_weights), or MXFP8 codes with ``scales = (Sg, Su, Sd)``."""
     T, H = X.shape
@@ -199,7 +202,7 @@ def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=N
     O_rows = torch.empty(T * k, H, dtype=torch.bfloat16, device=dev) if O_rows is None else O_rows
     _expect(H_rows, "H_rows", torch.bfloat16, (T * k, I))
     _expect(O_rows, "O_rows", torch.bfloat16, (T * k, H))
-    p = problem(T, H, I, E, k, "mxfp8" if mx else "bf16")
+    p = problem(T, H, I, E, k, "mxfp8" if mx else "bf16", activation, act_limit)
     if ws is None:
         ws, n = _workspace(p, CALL_EXPERT_MLP, dev)
     else:
@@ -224,7 +227,7 @@ def combine(O_rows, slot_row, topk_w, Y=None):
 
 
 def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, W_gate, W_up, W_down, Wg_t, Wu_t,
-             out=None, ws=None):
+             out=None, ws=None, activation="swiglu", act_limit=0.0):
     """Returns (dX, dW_gate, dW_up, dW_down, d_topk_w)."""
     T, H = X.shape
     E, _, I = W_gate.shape
@@ -245,7 +248,7 @@ def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, W_gate, W_up
                torch.empty(E, I, H, dtype=torch.bfloat16, device=dev),
                torch.empty(T, k, dtype=torch.float32, device=dev))
     dX, dWg, dWu, dWd, dtw = out
-    p = problem(T, H, I, E, k)
+    p = problem(T, H, I, E, k, "bf16", activation, act_limit)
     if ws is None:
         ws, n = _workspace(p, CALL_BACKWARD, dev)
     else:

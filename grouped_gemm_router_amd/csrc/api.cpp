@@ -33,6 +33,10 @@ moe_status check_problem(const moe_problem* p) {
   if (s != MOE_OK) return s;
   if (p->H < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (p->activation < MOE_ACT_SWIGLU || p->activation > MOE_ACT_REGLU) return MOE_ERR_INVALID_ARG;
+  if ((p->activation == MOE_ACT_SWIGLU_CLAMP || p->activation == MOE_ACT_SWIGLU_OAI) &&
+      !(p->act_limit > 0.f && p->act_limit < 3.0e38f))
+    return MOE_ERR_INVALID_ARG;
   const int align = p->dtype == MOE_DTYPE_MXFP8 ? 128 : 64;
   if (p->H % align || p->I % align) return MOE_ERR_UNSUPPORTED_SHAPE;
   // element offsets of the largest tensors must fit the kernels' index math
@@ -189,6 +193,7 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
   if (!mx) {
     moe::GemmArgs a = {};
     a.T = p->T; a.H = p->H; a.I = p->I; a.E = p->E; a.k = p->k;
+    a.act = p->activation; a.act_limit = p->act_limit;
     a.offsets = expert_offsets;
     a.row_token = row_token;
     a.X = (const uint16_t*)X;
@@ -211,6 +216,7 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
   uint8_t* Hs = Hq + align_up(A * I);
   moe::MxArgs m = {};
   m.T = p->T; m.H = p->H; m.I = p->I; m.E = p->E; m.k = p->k;
+  m.act = p->activation; m.act_limit = p->act_limit;
   m.offsets = expert_offsets;
   m.row_token = row_token;
   m.Xq = Xq; m.Xs = Xs;
@@ -259,6 +265,7 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   uint8_t* w8 = (uint8_t*)ws;
   moe::GemmArgs a = {};
   a.T = p->T; a.H = p->H; a.I = p->I; a.E = p->E; a.k = p->k;
+  a.act = p->activation; a.act_limit = p->act_limit;
   a.offsets = expert_offsets;
   a.row_token = row_token;
   a.row_slot = row_slot;

@@ -38,4 +38,71 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 __device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
 
+// Gated activations h = f(g, u) (the moe_activation codes) and their partial
+// derivatives, in fp32.  Clamps pass the gradient where their argument lies
+// inside the bounds, the bounds included.
+enum : int { ACT_SWIGLU = 0, ACT_SWIGLU_CLAMP = 1, ACT_SWIGLU_OAI = 2, ACT_GEGLU = 3, ACT_REGLU = 4 };
+// Kernels take the activation as a template constant ACTK: ACT_SWIGLU for the
+// default path (nothing else compiled in), ACT_ANY to switch on the run-time code.
+constexpr int ACT_ANY = -1;
+__device__ __forceinline__ int act_code(int actk, int runtime) { return actk == ACT_ANY ? runtime : actk; }
+constexpr float OAI_ALPHA = 1.702f;
+constexpr float INV_SQRT2 = 0.70710678118654752f;
+constexpr float INV_SQRT_2PI = 0.39894228040143268f;
+
+__device__ __forceinline__ float gated_act(float g, float u, int act, float lim) {
+  switch (act) {
+    case ACT_SWIGLU_CLAMP: return silu_f32(fminf(g, lim)) * fminf(fmaxf(u, -lim), lim);
+    case ACT_SWIGLU_OAI: {
+      const float gc = fminf(g, lim);
+      return gc * sigmoid_f32(OAI_ALPHA * gc) * (fminf(fmaxf(u, -lim), lim) + 1.f);
+    }
+    case ACT_GEGLU: return 0.5f * g * (1.f + erff(g * INV_SQRT2)) * u;
+    case ACT_REGLU: return fmaxf(g, 0.f) * u;
+    default: return silu_f32(g) * u;
+  }
+}
+
+// h = f(g, u), fg = df/dg, fu = df/du.
+__device__ __forceinline__ void gated_act_grad(float g, float u, int act, float lim, float& h, float& fg,
+                                               float& fu) {
+  switch (act) {
+    case ACT_SWIGLU_CLAMP:
+    case ACT_SWIGLU_OAI: {
+      const float gc = fminf(g, lim), uc = fminf(fmaxf(u, -lim), lim);
+      const float pg = g <= lim ? 1.f : 0.f, pu = (u >= -lim && u <= lim) ? 1.f : 0.f;
+      if (act == ACT_SWIGLU_CLAMP) {
+        const float s = sigmoid_f32(gc);
+        h = gc * s * uc;
+        fg = uc * (s * (1.f + gc * (1.f - s))) * pg;
+        fu = gc * s * pu;
+      } else {
+        const float s = sigmoid_f32(OAI_ALPHA * gc);
+        h = gc * s * (uc + 1.f);
+        fg = (s + OAI_ALPHA * gc * s * (1.f - s)) * (uc + 1.f) * pg;
+        fu = gc * s * pu;
+      }
+      return;
+    }
+    case ACT_GEGLU: {
+      const float Phi = 0.5f * (1.f + erff(g * INV_SQRT2));
+      h = g * Phi * u;
+      fg = (Phi + g * INV_SQRT_2PI * __expf(-0.5f * g * g)) * u;
+      fu = g * Phi;
+      return;
+    }
+    case ACT_REGLU:
+      h = fmaxf(g, 0.f) * u;
+      fg = g > 0.f ? u : 0.f;
+      fu = fmaxf(g, 0.f);
+      return;
+    default: {
+      const float s = sigmoid_f32(g);
+      h = g * s * u;
+      fg = u * (s * (1.f + g * (1.f - s)));
+      fu = g * s;
+    }
+  }
+}
+
 }  // namespace moe

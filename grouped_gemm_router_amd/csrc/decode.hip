@@ -142,10 +142,11 @@ __device__ __forceinline__ void stream_steps(int n, Load load, Step step) {
 // and their output columns are not stored, so no load is predicated and the
 // weight prefetch is never drained by a divergent branch.
 
-// gate/up + SwiGLU: one workgroup per unit (expert, row group, 16 intermediate
+// gate/up + gated activation: one workgroup per unit (expert, row group, 16 intermediate
 // columns); its 4 waves split the contraction axis in 4 and their partial sums
 // are added through LDS in wave order before the epilogue.
-__global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup(const GemmArgs p) {
+template <int ACTK>
+__device__ __forceinline__ void decode_gateup(const GemmArgs& p) {
   __shared__ f32x4 part[DEC_GU_WAVES - 1][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slabs = p.I / 16;
@@ -190,10 +191,14 @@ __global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup(const GemmArgs p) {
     }
     float h[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) h[v] = silu_f32(ag[v]) * au[v];
+    for (int v = 0; v < 4; ++v) h[v] = gated_act(ag[v], au[v], act_code(ACTK, p.act), p.act_limit);
     store_bf16x4(p.Hrows + (size_t)(r0 + (lane & 15)) * p.I + i0 + 4 * (lane >> 4), h[0], h[1], h[2], h[3]);
   }
 }
+
+__global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup(const GemmArgs p) { decode_gateup<ACT_SWIGLU>(p); }
+// any other gated activation (run-time code)
+__global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup_act(const GemmArgs p) { decode_gateup<ACT_ANY>(p); }
 
 // down: one workgroup per (expert, row group, 64 hidden columns), one wave per
 // 16 columns over the whole intermediate axis.
@@ -233,7 +238,8 @@ hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s) {
   const long rows = (long)a.T * a.k;
   const long experts = rows < a.E ? rows : a.E;
   const long groups = rows / 16 + experts;
-  hipLaunchKernelGGL(k_decode_gateup, dim3((unsigned)(groups * (a.I / 16))), dim3(DEC_GU_NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_decode_gateup : k_decode_gateup_act, dim3((unsigned)(groups * (a.I / 16))),
+                     dim3(DEC_GU_NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_down, dim3((unsigned)(groups * (a.H / 64))), dim3(DEC_NT), 0, s, a);

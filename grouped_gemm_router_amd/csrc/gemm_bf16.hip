@@ -1,4 +1,4 @@
-// bf16 grouped GEMMs of the MoE layer: forward gate/up + SwiGLU, forward down,
+// bf16 grouped GEMMs of the MoE layer: forward gate/up + gated activation, forward down,
 // and the three row-grouped GEMMs of the backward (direct-to-LDS rows, gemm_rows.h).
 #include "gemm_rows.h"
 #include "grouped_gemm.h"
@@ -102,8 +102,8 @@ struct RowOpsBase {
   using Sched = RowGroups<C::BM, C::BN, C::NT, PART, (PART == ROWS_ALL ? C::BM : 256)>;
 };
 
-// h = bf16(silu(X Wg) * (X Wu))
-template <class C, int PART = ROWS_ALL>
+// h = bf16(f(X Wg, X Wu)), f the problem's gated activation (SwiGLU by default)
+template <class C, int PART = ROWS_ALL, int ACTK = ACT_SWIGLU>
 struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
   __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
@@ -115,7 +115,9 @@ struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
     // are gate and 4q + 8 + j the up values of column 8q + 4 * (lane / 32) + j
     stage_store_bf16<C, C::FN * 16, 2>(
         wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.nt * (C::BN / 2) + wn * C::FN * 16, p.I, lane,
-        [&](int fm, int fn, int q, int j) { return silu_f32(acc[fm][fn][4 * q + j]) * acc[fm][fn][4 * q + 8 + j]; },
+        [&](int fm, int fn, int q, int j) {
+          return gated_act(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit);
+        },
         [](int fn, int q) { return fn * 16 + q * 8; });
   }
 };
@@ -184,7 +186,7 @@ __device__ __forceinline__ void split4(const float (&v)[4], uint2& hi, uint2& lo
 // ahead of its use; the five bf16 outputs (h, dg and du with their remainders) of
 // each 32-row block go through the wave's LDS scratch (NSLOT staged blocks at a
 // time) and leave as whole 64-byte row segments (16 bytes per lane).
-template <class C, int PART = ROWS_ALL>
+template <class C, int PART = ROWS_ALL, int ACTK = ACT_SWIGLU>
 struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
   __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
@@ -249,13 +251,14 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
           float hv[4], dg[4], du[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float g = acc[fm][fn][4 * q + j], u = acc[fm][fn][4 * q + 8 + j];
-            const float sg = sigmoid_f32(g);
-            hv[j] = bf16_to_f32(f32_to_bf16(g * sg * u));
+            float hf, fg, fu;
+            gated_act_grad(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit,
+                           hf, fg, fu);
+            hv[j] = bf16_to_f32(f32_to_bf16(hf));
             dot += hv[j] * Pv[j];
             const float dh = w * Pv[j];
-            du[j] = dh * (g * sg);
-            dg[j] = dh * u * (sg * (1.f + g * (1.f - sg)));
+            du[j] = dh * fu;
+            dg[j] = dh * fg;
           }
           if (cv) {
             uint2 hi, lo;
@@ -333,10 +336,18 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART> {
     rows_gemm_split_body<CfgRows, CT, OPS<CfgRows, ROWS_FULL>, OPS<CT, ROWS_TAIL>, GemmArgs>(p);      \
   }
 
+// the gated activation as a run-time code (every activation but the default SwiGLU)
+template <class C, int PART>
+using FwdGateUpOpsAny = FwdGateUpOps<C, PART, ACT_ANY>;
+template <class C>
+using BwdRecomputeOpsAny = BwdRecomputeOps<C, ROWS_ALL, ACT_ANY>;
+
 MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps, CfgTail)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny, CfgTail)
 MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps, CfgTail)
 MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps, CfgTail)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
+MOE_ROWS_KERNEL(k_bwd_recompute_act, BwdRecomputeOpsAny)
 MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps, CfgTail)
 
 template <class C>
@@ -349,7 +360,8 @@ static int row_grid(const GemmArgs& a, int N) {
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
 hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_fwd_gateup, dim3(row_grid<CfgRows>(a, 2 * a.I)), dim3(CfgRows::NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_fwd_gateup : k_fwd_gateup_act, dim3(row_grid<CfgRows>(a, 2 * a.I)),
+                     dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s) {
@@ -364,7 +376,8 @@ int bwd_nparts(int I) {
   return ((2 * I + CfgRows::BN - 1) / CfgRows::BN) * CfgRows::WAVES_N;
 }
 hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_recompute, dim3(row_grid<CfgRows>(a, 2 * a.I)), dim3(CfgRows::NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_bwd_recompute : k_bwd_recompute_act, dim3(row_grid<CfgRows>(a, 2 * a.I)),
+                     dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {

@@ -10,6 +10,8 @@ namespace moe {
 // Arguments of every grouped GEMM of the layer (unused fields stay null).
 struct GemmArgs {
   int T, H, I, E, k;
+  int act;                // gated activation (moe_activation)
+  float act_limit;        // its clamp, where it has one
   const int32_t* offsets;
   const int32_t* row_token;
   const int32_t* row_slot;
@@ -78,6 +80,8 @@ hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s);
 // MXFP8 expert GEMMs
 struct MxArgs {
   int T, H, I, E, k;
+  int act;
+  float act_limit;
   const int32_t* offsets;
   const int32_t* row_token;
   const uint8_t* Xq;  const uint8_t* Xs;    // [T, H], [T, H/32]

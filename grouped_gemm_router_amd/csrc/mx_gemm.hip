@@ -1,4 +1,4 @@
-// MXFP8 grouped GEMMs (gate/up + SwiGLU, down) on gfx950's block-scaled MFMA
+// MXFP8 grouped GEMMs (gate/up + gated activation, down) on gfx950's block-scaled MFMA
 // v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and one E8M0 scale per
 // 32 contraction elements of every row (OCP Microscaling v1.0).
 //
@@ -246,13 +246,15 @@ __device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
   }
 }
 
-template <class C>
-struct MxSwiGLUEpi {  // h = bf16(silu(G) * U) -> Hrows (columns as in the bf16 gate/up GEMM)
+template <class C, int ACTK = ACT_SWIGLU>
+struct MxSwiGLUEpi {  // h = bf16(f(G, U)) -> Hrows (columns as in the bf16 gate/up GEMM)
   __device__ static void apply(const MxArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
                                int lane, uint8_t* wlds) {
     stage_store_bf16<C, C::FN * 16, 2>(
         wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.nt * (C::BN / 2) + wn * C::FN * 16, p.I, lane,
-        [&](int fm, int fn, int q, int j) { return silu_f32(acc[fm][fn][4 * q + j]) * acc[fm][fn][4 * q + 8 + j]; },
+        [&](int fm, int fn, int q, int j) {
+          return gated_act(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit);
+        },
         [](int fn, int q) { return fn * 16 + q * 8; });
   }
 };
@@ -271,6 +273,10 @@ struct MxStoreOEpi {  // O = bf16(acc) -> Orows
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_gateup(const MxArgs p) {
   mx_rows_body<CfgMx, MxSrcX, MxSrcGateUpW<CfgMx>, MxSwiGLUEpi<CfgMx>>(p, 2 * p.I, p.H);
 }
+// any other gated activation (run-time code)
+__global__ void __launch_bounds__(CfgMx::NT) k_mx_gateup_act(const MxArgs p) {
+  mx_rows_body<CfgMx, MxSrcX, MxSrcGateUpW<CfgMx>, MxSwiGLUEpi<CfgMx, ACT_ANY>>(p, 2 * p.I, p.H);
+}
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_down(const MxArgs p) {
   mx_rows_body<CfgMx, MxSrcH, MxSrcDownW, MxStoreOEpi<CfgMx>>(p, p.H, p.I);
 }
@@ -285,7 +291,8 @@ static int mx_grid(const MxArgs& a, int N) {
 }
 
 hipError_t launch_mx_gateup(const MxArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_mx_gateup, dim3(mx_grid(a, 2 * a.I)), dim3(CfgMx::NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_mx_gateup : k_mx_gateup_act, dim3(mx_grid(a, 2 * a.I)), dim3(CfgMx::NT),
+                     0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_mx_down(const MxArgs& a, hipStream_t s) {

@@ -15,8 +15,12 @@ from . import binding as B
 
 
 class MoELayer:
-    def __init__(self, H: int, I: int, E: int, k: int, dtype: str = "bf16", device="cuda"):
+    def __init__(self, H: int, I: int, E: int, k: int, dtype: str = "bf16", device="cuda",
+                 activation: str = "swiglu", act_limit: float = 0.0):
+        """``activation``: swiglu (default), swiglu_clamp, swiglu_oai, geglu or reglu (include/moe.h,
+        moe_activation); ``act_limit``: the clamp of the two clamped ones."""
         self.H, self.I, self.E, self.k, self.dtype = H, I, E, k, dtype
+        self.activation, self.act_limit = activation, act_limit
         self.device = torch.device(device)
         self.W_gate = self.W_up = self.W_down = None
         self._plans = {}
@@ -45,7 +49,7 @@ class MoELayer:
             return self._plans[key]
         H, I, E, k, dev = self.H, self.I, self.E, self.k, self.device
         A = T * k
-        p = B.problem(T, H, I, E, k, self.dtype)
+        p = B.problem(T, H, I, E, k, self.dtype, self.activation, self.act_limit)
         pl = {
             "topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev),
             "topk_w": torch.empty(T, k, dtype=torch.float32, device=dev),
@@ -82,7 +86,8 @@ class MoELayer:
         if mlp_events is not None:
             mlp_events[0].record()
         B.expert_mlp(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
-                     scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"])
+                     scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"],
+                     activation=self.activation, act_limit=self.act_limit)
         if mlp_events is not None:
             mlp_events[1].record()
         B.combine(pl["O_rows"], pl["slot_row"], pl["topk_w"], pl["Y"])
@@ -96,7 +101,7 @@ class MoELayer:
         pl = self.plan(T, True)
         return B.backward(X, dY, pl["topk_w"], pl["row_token"], pl["row_slot"], pl["slot_row"], pl["offsets"],
                           self.W_gate, self.W_up, self.W_down, self.Wg_t, self.Wu_t, out=pl["grads"],
-                          ws=pl["ws_bwd"])
+                          ws=pl["ws_bwd"], activation=self.activation, act_limit=self.act_limit)
 
     def route_backward(self, T: int):
         """Gradient with respect to the router logits [T, E] fp32, from the d(top-k weights) of the

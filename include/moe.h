@@ -63,11 +63,28 @@ typedef enum {
                            per 32 elements along the contraction axis */
 } moe_dtype;
 
+/*
+ * Gated activation h = f(G, U) of the expert MLP (G = x W_gate, U = x W_up).
+ * LightMoE "Highlights" names SwiGLU-OAI, bounded SwiGLU, GeGLU and ReGLU
+ * epilogues and "MoE inference" an activation clamp of 10; the formulas are
+ * the public definitions of the model families that use them:
+ */
+typedef enum {
+  MOE_ACT_SWIGLU = 0,       /* silu(G) * U (the default) */
+  MOE_ACT_SWIGLU_CLAMP = 1, /* silu(min(G, c)) * clamp(U, -c, c), c = act_limit (bounded SwiGLU) */
+  MOE_ACT_SWIGLU_OAI = 2,   /* g * sigmoid(1.702 g) * (u + 1), g = min(G, c), u = clamp(U, -c, c) */
+  MOE_ACT_GEGLU = 3,        /* gelu(G) * U, gelu(x) = x * Phi(x), Phi the normal CDF (erf form) */
+  MOE_ACT_REGLU = 4         /* max(G, 0) * U */
+} moe_activation;
+
 /* Problem shape.  T tokens, hidden size H, expert intermediate size I,
- * E experts, k experts per token. */
+ * E experts, k experts per token; the activation (a zeroed field is SwiGLU)
+ * and the clamp c of the clamped ones (> 0, finite; ignored by the others). */
 typedef struct {
   int32_t T, H, I, E, k;
-  int32_t dtype; /* moe_dtype */
+  int32_t dtype;      /* moe_dtype */
+  int32_t activation; /* moe_activation */
+  float act_limit;    /* c of MOE_ACT_SWIGLU_CLAMP and MOE_ACT_SWIGLU_OAI */
 } moe_problem;
 
 /* Which call a workspace is sized for (moe_workspace_size). */

@@ -582,6 +582,26 @@ def mx_requant_delta(h_exact, rel_eps: float = 2.0 ** -14):
     return base, np.maximum(np.abs(up - base), np.abs(dn - base))
 
 
+def bf16_round_delta(x_exact, rel_eps: float = 2.0 ** -14):
+    """Rounding decisions of x to bf16 that another correct implementation may take
+    the other way: x is known to an fp32 implementation only to within a few fp32
+    ulps, so this perturbs it by +-rel_eps * |x| (far more than fp32 error) and
+    returns, per element, the largest change of its bf16 value (0 away from a
+    rounding midpoint, one bf16 step next to one)."""
+    x = np.asarray(x_exact, dtype=np.float64)
+    slack = rel_eps * np.abs(x)
+    base = bf16_round(x)
+    return np.maximum(np.abs(bf16_round(x + slack) - base), np.abs(bf16_round(x - slack) - base))
+
+
+def h_ambiguity_rows(x_rows, wg, wu, act: str = "swiglu", limit=None):
+    """Per element of h = bf16(f(x Wg, x Wu)) for one expert's rows: the change another
+    valid bf16 rounding of h can make (``bf16_round_delta`` of the exact value)."""
+    G = x_rows @ wg
+    U = x_rows @ wu
+    return bf16_round_delta(activation(G, U, act, limit))
+
+
 def mx_down_ambiguity(G, U, wd, act: str = "swiglu", limit=None):
     """For O = MXFP8(h) W_down with h = bf16(f(G, U)): per element of O, the
     largest change another valid rounding of the requantised h can cause

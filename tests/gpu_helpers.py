@@ -68,3 +68,27 @@ def device_weights(cfg, name, experts=None, fill=float("nan")):
 def host_weight_fn(cfg, name):
     """Per-expert weight getter for the oracle (regenerates the seeded draw)."""
     return lambda e: wl.make_expert_weight(cfg, name, e)
+
+
+def backward_h_ambiguity(cfg, X, dY, idx, w, fn, act="swiglu", limit=None, experts=None):
+    """What other valid bf16 roundings of h = bf16(f(G, U)) and dO = bf16(w dY) can change
+    (``bf16_round_delta``; both are rounding decisions on values the GPU knows to fp32):
+    per expert |delta h|^T |dO| + |h|^T |delta dO| (dW_down), per slot
+    sum_i |delta h_i| |P_i| (d_topk_w)."""
+    off, row_token, row_slot, _ = orc.dispatch(idx, cfg.E)
+    Xv, dYv = orc.bf16_decode(X), orc.bf16_decode(dY)
+    amb_dwd = {}
+    amb_dtw = np.zeros(idx.shape)
+    for e in (range(cfg.E) if experts is None else experts):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        tok, sl = row_token[lo:hi], row_slot[lo:hi]
+        wg, wu, wd = (orc.bf16_decode(fn(n)(e)) for n in ("gate", "up", "down"))
+        dh = orc.h_ambiguity_rows(Xv[tok], wg, wu, act, limit)
+        _, _, h, _ = orc.expert_forward_rows(Xv[tok], wg, wu, wd, act=act, limit=limit)
+        dO_exact = w.reshape(-1)[sl][:, None] * dYv[tok]
+        dO = orc.bf16_round(dO_exact)
+        amb_dwd[e] = dh.T @ np.abs(dO) + np.abs(h).T @ orc.bf16_round_delta(dO_exact)
+        amb_dtw.reshape(-1)[sl] = (dh * np.abs(dYv[tok] @ wd.T)).sum(axis=1)
+    return amb_dwd, amb_dtw

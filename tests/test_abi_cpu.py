@@ -66,6 +66,20 @@ def test_validate_problem(args, expect):
     assert B.validate_problem(B.problem(*args)) == expect
 
 
+def test_validate_problem_activation():
+    from grouped_gemm_router_amd import binding as B
+    assert B.validate_problem(B.problem(64, 256, 128, 8, 2)) == 0
+    for act in ("swiglu", "geglu", "reglu"):
+        assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act)) == 0
+    for act in ("swiglu_clamp", "swiglu_oai"):
+        assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act, act_limit=7.0)) == 0
+        assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act, act_limit=0.0)) == 1
+        assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act, act_limit=float("nan"))) == 1
+    p = B.problem(64, 256, 128, 8, 2)
+    p.activation = 5
+    assert B.validate_problem(p) == 1
+
+
 def test_workspace_sizes():
     from grouped_gemm_router_amd import binding as B
     p = B.problem(4096, 2048, 512, 256, 8)

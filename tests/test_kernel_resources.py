@@ -3,8 +3,9 @@
 The pipelined k loops wait for their global->LDS loads with counted waits
 (`s_waitcnt vmcnt(N)`: "at most N load instructions still outstanding"), which
 is only right when nothing else touches vector memory inside the loop.  A
-register spill would put scratch loads and stores there, so every GEMM kernel
-must compile without spills or scratch memory.  The check compiles the sources
+VGPR spill would put scratch loads and stores there, so every GEMM kernel must
+compile without VGPR spills and without scratch memory (SGPRs the compiler
+parks in VGPR lanes touch no memory and are allowed).  The check compiles the sources
 for gfx950 with the build's own flags and reads the compiler's resource
 remarks.
 
@@ -54,5 +55,4 @@ def test_gemm_kernels_do_not_spill(src, tmp_path):
     assert kernels, "no kernel resource remarks"
     for name, res in kernels.items():
         assert res.get("VGPRs Spill", 0) == 0, (name, res)
-        assert res.get("SGPRs Spill", 0) == 0, (name, res)
         assert res.get("ScratchSize [bytes/lane]", 0) == 0, (name, res)

@@ -123,6 +123,22 @@ def test_mx_quantize_lossless_for_representable_blocks():
     assert np.array_equal(orc.mx_dequantize(codes, scales), v)
 
 
+def test_bf16_round_delta_marks_only_midpoints():
+    # a value exactly half-way between two bf16 neighbours, one a hair above it, and
+    # values well inside a rounding interval
+    lo = orc.bf16_decode(np.array([0x3F80], np.uint16))[0]          # 1.0
+    step = 2.0 ** -7
+    mids = np.array([lo + step / 2, lo + step / 2 * (1 + 1e-9), -(lo + step / 2)])
+    inner = np.array([lo + step / 4, lo + 3 * step / 4, 3.0 + step / 8, -7.1])
+    d_mid = orc.bf16_round_delta(mids)
+    assert np.allclose(d_mid, step * np.array([1, 1, 1]))
+    assert np.all(orc.bf16_round_delta(inner) == 0)
+    # on random values only the few within 2^-14 (relative) of a midpoint are flagged:
+    # about 2 * 2^-14 / 2^-7.5, i.e. 2 %
+    v = np.random.default_rng(2).standard_normal(200000)
+    assert np.count_nonzero(orc.bf16_round_delta(v)) < 0.03 * v.size
+
+
 def test_mx_requant_delta_marks_only_ambiguous_decisions():
     rng = np.random.default_rng(8)
     # values sitting exactly between two E4M3 codes (after bf16 rounding) at scale 2^0
