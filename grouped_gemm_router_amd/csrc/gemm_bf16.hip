@@ -14,9 +14,15 @@ namespace moe {
 #endif
 // row-grouped GEMMs: 256 x 256 tiles, direct-to-LDS loads, 128 KB of LDS stages
 using CfgRows = RowCfg<256, 256, 2, MOE_ROWS_WAVES_N, MOE_ROWS_BK, (MOE_ROWS_BK == 32 ? 4 : 2)>;
-// remainders of at most 128 rows of an expert (forward GEMMs): 64 x 256 tiles, 8 waves
-// side by side, three 40 KB stages
-using CfgTail = RowCfg<64, 256, 1, 8, 64, 3>;
+// Remainder tiles (the rows of an expert past its last full 256-row block), one per expert
+// and GEMM column tile, of the smallest height of 64, 128 or 192 rows that holds them: an
+// expert with a few hundred rows streams each weight tile once, with at most 63 rows of
+// padding in its MFMAs.
+//   192 x 256: two 56 KB stages;  128 x 256: three 48 KB stages;
+//   64 x 256:  8 waves side by side, three 40 KB stages.
+using CfgRem192 = RowCfg<192, 256, 2, 4, 64, 2>;
+using CfgRem128 = RowCfg<128, 256, 2, 4, 64, 3>;
+using CfgRem64 = RowCfg<64, 256, 1, 8, 64, 3>;
 
 // ------------------------------------------------------------------------
 // Row sources of the direct-to-LDS row-grouped GEMMs: a wave-uniform base and
@@ -331,9 +337,11 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART> {
     rows_gemm_body<CfgRows, OPS<CfgRows>, GemmArgs>(p);                            \
   }
 
-#define MOE_ROWS_SPLIT_KERNEL(NAME, OPS, CT)                                                         \
-  __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {                             \
-    rows_gemm_split_body<CfgRows, CT, OPS<CfgRows, ROWS_FULL>, OPS<CT, ROWS_TAIL>, GemmArgs>(p);      \
+#define MOE_ROWS_SPLIT_KERNEL(NAME, OPS)                                                            \
+  __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {                            \
+    rows_gemm_split_body<CfgRows, CfgRem192, CfgRem128, CfgRem64, OPS<CfgRows, ROWS_FULL>,           \
+                         OPS<CfgRem192, ROWS_REM_Q3>, OPS<CfgRem128, ROWS_REM_Q2>,                   \
+                         OPS<CfgRem64, ROWS_REM_Q1>, GemmArgs>(p);                                    \
   }
 
 // the gated activation as a run-time code (every activation but the default SwiGLU)
@@ -342,20 +350,20 @@ using FwdGateUpOpsAny = FwdGateUpOps<C, PART, ACT_ANY>;
 template <class C>
 using BwdRecomputeOpsAny = BwdRecomputeOps<C, ROWS_ALL, ACT_ANY>;
 
-MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps, CfgTail)
-MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny, CfgTail)
-MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps, CfgTail)
-MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps, CfgTail)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny)
+MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps)
+MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
 MOE_ROWS_KERNEL(k_bwd_recompute_act, BwdRecomputeOpsAny)
-MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps, CfgTail)
+MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps)
 
 template <class C>
 static int row_grid(const GemmArgs& a, int N) {
   long A = (long)a.T * a.k;
   long mt = A / C::BM + (a.E < A ? a.E : A) + 1;
   long tiles = mt * ((N + C::BN - 1) / C::BN);
-  long cap = (long)num_cus();            // one 132 KB-LDS block per CU
+  long cap = (long)num_cus();            // one block per CU (its LDS stages fill most of the 160 KB)
   long g = tiles < cap ? tiles : cap;
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }

@@ -216,9 +216,10 @@ struct RowEpiLds {
 constexpr int SCHED_LDS_INTS = 1024 + 1 + 16 + 1;
 
 // Every tile of Ops' schedule, with the stages at smem (C::NST * C::STAGE uint4) and the
-// schedule's scratch at sched_lds.
+// schedule's scratch at sched_lds.  `carry` is XcdWalk's deal position, updated for a
+// schedule that follows on the same grid.
 template <class C, class Ops, class P>
-__device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sched_lds) {
+__device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sched_lds, int& carry) {
   static_assert(C::NT / 64 <= 16, "schedule scratch");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -229,7 +230,7 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
   typename Ops::Sched sched;
   Ops::init_sched(sched, p, sched_lds, sched_lds + 1025);
   XcdWalk walk;
-  walk.init(sched.total);
+  carry = walk.init(sched.total, carry);
   if (!walk.valid()) return;
   Tile tl = sched.tile(walk.t);
   FragAddr<C> fa;
@@ -304,21 +305,32 @@ template <class C, class Ops, class P>
 __device__ __forceinline__ void rows_gemm_body(const P& p) {
   __shared__ uint4 smem[C::NST * C::STAGE];
   __shared__ int sched_lds[SCHED_LDS_INTS];
-  rows_gemm_tiles<C, Ops, P>(p, smem, sched_lds);
+  int carry = 0;
+  rows_gemm_tiles<C, Ops, P>(p, smem, sched_lds, carry);
 }
 
-// Two passes over the experts' rows in one kernel: the full 256-row tiles (and
-// remainders above 128 rows) with configuration CF, then the remainders of at
-// most 128 rows in CT's shorter tiles, with the same LDS.  A workgroup that is
-// done with its full tiles goes on to its share of the short ones.
-template <class CF, class CT, class OpsF, class OpsT, class P>
+// Four passes over the experts' rows in one kernel, sharing one LDS allocation:
+// the full 256-row tiles (and remainders above 192 rows) with configuration CF,
+// then each remainder of at most 192, 128 and 64 rows in one C3, C2 or C1 tile.
+// A workgroup that is done with its share of one pass goes on to its share of
+// the next.
+template <int A, int B>
+constexpr int cmax() { return A > B ? A : B; }
+template <class CF, class C3, class C2, class C1, class OpsF, class Ops3, class Ops2, class Ops1, class P>
 __device__ __forceinline__ void rows_gemm_split_body(const P& p) {
-  static_assert(CT::NST * CT::STAGE <= CF::NST * CF::STAGE && CT::NT == CF::NT, "shared LDS and block");
-  __shared__ uint4 smem[CF::NST * CF::STAGE];
+  static_assert(C3::NT == CF::NT && C2::NT == CF::NT && C1::NT == CF::NT, "one block shape");
+  constexpr int SMAX = cmax<cmax<CF::NST * CF::STAGE, C3::NST * C3::STAGE>(),
+                           cmax<C2::NST * C2::STAGE, C1::NST * C1::STAGE>()>();
+  __shared__ uint4 smem[SMAX];
   __shared__ int sched_lds[SCHED_LDS_INTS];
-  rows_gemm_tiles<CF, OpsF, P>(p, smem, sched_lds);
+  int carry = 0;
+  rows_gemm_tiles<CF, OpsF, P>(p, smem, sched_lds, carry);
   __syncthreads();
-  rows_gemm_tiles<CT, OpsT, P>(p, smem, sched_lds);
+  rows_gemm_tiles<C3, Ops3, P>(p, smem, sched_lds, carry);
+  __syncthreads();
+  rows_gemm_tiles<C2, Ops2, P>(p, smem, sched_lds, carry);
+  __syncthreads();
+  rows_gemm_tiles<C1, Ops1, P>(p, smem, sched_lds, carry);
 }
 
 // Stages this wave's bf16 output, one 32-row fragment row-block at a time,

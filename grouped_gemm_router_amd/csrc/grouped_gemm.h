@@ -61,26 +61,30 @@ __device__ int block_exclusive_scan(int v, int* red /* NT/64 + 1 ints */) {
 // Schedules
 // ---------------------------------------------------------------------------
 // Which rows of each expert a RowGroups schedule covers (n rows = q * BMF + r, r < BMF):
-//   ROWS_ALL:  all n rows in tiles of BM;
-//   ROWS_FULL: the q full blocks of BMF = BM rows, plus the remainder when r > BMF / 2 (one
-//              partly filled tile);
-//   ROWS_TAIL: the remainder r when 0 < r <= BMF / 2, in tiles of BM (< BMF) rows.
-// A FULL and a TAIL schedule with the same BMF cover every row exactly once.
-enum RowPart { ROWS_ALL = 0, ROWS_FULL = 1, ROWS_TAIL = 2 };
+//   ROWS_ALL:    all n rows in tiles of BM;
+//   ROWS_FULL:   the q full blocks of BMF = BM rows, plus the remainder when r > 3 BMF / 4 (one
+//                partly filled tile);
+//   ROWS_REM_Q3: the remainder when BMF / 2 < r <= 3 BMF / 4, in one tile of BM = 3 BMF / 4 rows;
+//   ROWS_REM_Q2: the remainder when BMF / 4 < r <= BMF / 2, in one tile of BM = BMF / 2 rows;
+//   ROWS_REM_Q1: the remainder when 0 < r <= BMF / 4, in one tile of BM = BMF / 4 rows.
+// FULL and the three REM schedules with the same BMF cover every row exactly once, and
+// every expert's remainder is one tile at most BMF / 4 - 1 rows taller than it.
+enum RowPart { ROWS_ALL = 0, ROWS_FULL = 1, ROWS_REM_Q1 = 2, ROWS_REM_Q2 = 3, ROWS_REM_Q3 = 4 };
 
 template <int BM, int BN, int NT, int PART = ROWS_ALL, int BMF = BM>
 struct RowGroups {
+  static constexpr int QUARTER = PART >= ROWS_REM_Q1 ? PART - ROWS_REM_Q1 + 1 : 0;
   static_assert(PART != ROWS_FULL || BMF == BM, "full tiles are BMF rows");
-  static_assert(PART != ROWS_TAIL || (BM < BMF && (BMF / 2) % BM == 0), "tail tiles split half a full tile");
+  static_assert(QUARTER == 0 || (BMF % 4 == 0 && BM * 4 == QUARTER * BMF), "one remainder tile per class");
   static constexpr int MAX_E = 1024;
   // tiles of expert e with n rows, and the first of its rows they cover
   __device__ static int count(int n) {
     if constexpr (PART == ROWS_ALL) return (n + BM - 1) / BM;
     const int q = n / BMF, r = n - q * BMF;
-    if constexpr (PART == ROWS_FULL) return q + (r > BMF / 2 ? 1 : 0);
-    return r > BMF / 2 ? 0 : (r + BM - 1) / BM;
+    if constexpr (PART == ROWS_FULL) return q + (r > 3 * BMF / 4 ? 1 : 0);
+    return (r > (QUARTER - 1) * BMF / 4 && r <= QUARTER * BMF / 4) ? 1 : 0;
   }
-  __device__ static int first_row(int n) { return PART == ROWS_TAIL ? n / BMF * BMF : 0; }
+  __device__ static int first_row(int n) { return QUARTER ? n / BMF * BMF : 0; }
   int* prefix;   // LDS [E+1]: exclusive prefix of per-expert m-tile counts
   int E, ntiles_n, total, K;
   const int32_t* offsets;
@@ -165,18 +169,26 @@ struct WeightGrad {
   }
 };
 
-// XCD-aware persistent walk: XCD x owns tiles [x*tpx, (x+1)*tpx).
+// XCD-aware persistent walk: XCD x owns tiles [x*tpx, (x+1)*tpx), dealt round-robin to its
+// bpx workgroups.  For several schedules run one after another by the same grid, `carry`
+// continues the deal where the previous schedule stopped on this XCD, so that the
+// workgroups that took one tile more in one schedule are not also first in the next; init
+// returns the carry for the following schedule (0 starts a fresh deal).
 struct XcdWalk {
   int t, step, end;
-  __device__ void init(int total) {
+  __device__ int init(int total, int carry = 0) {
     const int G = gridDim.x;            // a multiple of NUM_XCD
     const int xcd = blockIdx.x % NUM_XCD;
     const int local = blockIdx.x / NUM_XCD;
     const int bpx = G / NUM_XCD;
     const int tpx = (total + NUM_XCD - 1) / NUM_XCD;
-    t = xcd * tpx + local;
+    int first = local - carry;
+    if (first < 0) first += bpx;
+    t = xcd * tpx + first;
     step = bpx;
     end = min(total, (xcd + 1) * tpx);
+    const int here = max(0, end - xcd * tpx);
+    return (carry + here) % bpx;
   }
   __device__ bool valid() const { return t < end; }
   __device__ void next() { t += step; }

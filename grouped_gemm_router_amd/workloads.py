@@ -49,6 +49,8 @@ class MoEConfig:
     logits: str     # "normal", "zipf" (N(0,1) + 0.5*Zipf(1.1) per expert) or "rankzipf"
     seed: int
     backward: bool = False
+    activation: str = "swiglu"   # gated activation (swiglu, swiglu_clamp, swiglu_oai, geglu, reglu)
+    act_limit: float = 0.0       # clamp of swiglu_clamp / swiglu_oai
 
     @property
     def A(self) -> int:
@@ -64,6 +66,14 @@ CONFIGS = {
     "train": MoEConfig("train", 8192, 4096, 1024, 128, 8, "bf16", "normal", 4, backward=True),
     # Diagnostic: prefill shapes with a milder per-rank bias, every expert active.
     "prefill_rankzipf": MoEConfig("prefill_rankzipf", 4096, 2048, 512, 256, 8, "bf16", "rankzipf", 1),
+    # Diagnostic: the larger expert shapes of the LightMoE compatibility table (hidden / intermediate,
+    # experts / top-k, activation), 4096 tokens, balanced routing.  The clamp of the bounded SwiGLU is
+    # the value the pages give; SwiGLU-OAI's 7 is its public definition's (the pages give none).
+    "h4096_i2048_e256_k6_clamp": MoEConfig("h4096_i2048_e256_k6_clamp", 4096, 4096, 2048, 256, 6, "bf16",
+                                           "normal", 5, activation="swiglu_clamp", act_limit=10.0),
+    "h6144_i2048_e256_k8": MoEConfig("h6144_i2048_e256_k8", 4096, 6144, 2048, 256, 8, "bf16", "normal", 6),
+    "h6144_i3072_e128_k4_oai": MoEConfig("h6144_i3072_e128_k4_oai", 4096, 6144, 3072, 128, 4, "bf16",
+                                         "normal", 7, activation="swiglu_oai", act_limit=7.0),
 }
 
 

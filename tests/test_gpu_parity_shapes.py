@@ -1,0 +1,67 @@
+"""GPU parity of the whole forward layer at the larger expert shapes of the
+LightMoE compatibility table (4096 tokens; hidden / intermediate, experts /
+top-k and activation of each row), in the launch configuration the benchmark
+times.  Routing and dispatch are compared whole and bit for bit; the layer
+output on sampled tokens and the h and O rows of sampled rows, one by one
+against the oracle.  Only the experts the sampled tokens use get weights; the
+others hold NaN, so a read of a wrong expert shows up in the sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+from grouped_gemm_router_amd import workloads as wl
+
+from gpu_helpers import check_close, device_weights, host_weight_fn, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = ["h4096_i2048_e256_k6_clamp", "h6144_i2048_e256_k8", "h6144_i3072_e128_k4_oai"]
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.mark.parametrize("name", SHAPES)
+def test_forward_model_shape_sampled(name):
+    from grouped_gemm_router_amd.layer import MoELayer
+    cfg = wl.config(name)
+    act, limit = cfg.activation, (cfg.act_limit or None)
+    logits, X = wl.make_logits(cfg), wl.make_x(cfg)
+    idx, w = orc.route(logits, cfg.k)
+    rng = np.random.default_rng(321)
+    tokens = np.sort(rng.choice(cfg.T, 8, replace=False))
+    tokens[0], tokens[-1] = 0, cfg.T - 1
+    drawn = np.unique(idx[tokens])
+    _say(name, "experts with weights", len(drawn))
+    W = {n: device_weights(cfg, n, experts=drawn) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=act,
+                     act_limit=cfg.act_limit).load_weights(W["gate"], W["up"], W["down"], keep_math=False)
+    layer.forward(torch.from_numpy(logits).cuda(), to_dev(X))
+    torch.cuda.synchronize()
+    pl = layer.plan(cfg.T)
+    off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
+    assert np.array_equal(pl["topk_idx"].cpu().numpy(), idx)
+    for g, r in zip((pl["offsets"], pl["row_token"], pl["row_slot"], pl["slot_row"]),
+                    (off, row_token, row_slot, slot_row)):
+        assert np.array_equal(g.cpu().numpy(), r)
+    fn = lambda n: host_weight_fn(cfg, n)
+    Yref = orc.layer_forward_tokens(X, idx, w, fn("gate"), fn("up"), fn("down"), tokens, act=act, limit=limit)
+    check_close(to_f64(pl["Y"][torch.from_numpy(tokens).cuda()]), Yref, f"{name} Y[sampled tokens]")
+    # h and O rows: the sampled tokens' rows plus each drawn expert's first and last row
+    rows = np.concatenate([slot_row.reshape(cfg.T, cfg.k)[tokens].reshape(-1),
+                           off[drawn], off[drawn + 1] - 1])
+    rows = np.unique(rows)
+    Hg = to_f64(pl["H_rows"][torch.from_numpy(rows).cuda()])
+    Og = to_f64(pl["O_rows"][torch.from_numpy(rows).cuda()])
+    owner = np.searchsorted(off, rows, side="right") - 1
+    assert np.isin(owner, drawn).all()
+    Xv = orc.bf16_decode(X)
+    for e in np.unique(owner):
+        sel = np.nonzero(owner == e)[0]
+        _, _, h, O = orc.expert_forward_rows(Xv[row_token[rows[sel]]], orc.bf16_decode(fn("gate")(e)),
+                                             orc.bf16_decode(fn("up")(e)), orc.bf16_decode(fn("down")(e)),
+                                             act=act, limit=limit)
+        check_close(Hg[sel], h, f"{name} h[rows of expert {e}]")
+        check_close(Og[sel], O, f"{name} O[rows of expert {e}]")

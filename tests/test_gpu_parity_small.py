@@ -236,6 +236,54 @@ def test_forward_small_vs_oracle(cfg):
     check_close(to_f64(pl["Y"]), Y, "Y", ambiguity=amb_Y)
 
 
+# expert sizes that land in every row class of the row-grouped GEMMs (n = q * 256 + r: full
+# 256-row tiles and remainders above 192 rows, and one 192-, 128- or 64-row tile for the
+# remainders up to 192, 128 and 64 rows), including each class boundary
+REMAINDER_COUNTS = [0, 1, 63, 64, 65, 100, 127, 128, 129, 192, 193, 200, 255, 256, 257, 300, 320, 321, 384, 385,
+                    448, 449, 513]
+
+
+def remainder_logits(counts, E, seed):
+    """k = 1 logits that send exactly counts[e] tokens to expert e (tokens in a shuffled order)."""
+    rng = np.random.default_rng(seed)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    logits = 0.1 * rng.standard_normal((owner.size, E)).astype(np.float32)
+    logits[np.arange(owner.size), owner] = 4.0
+    return np.ascontiguousarray(logits)
+
+
+def test_forward_backward_every_row_class():
+    _say("row classes", REMAINDER_COUNTS)
+    from grouped_gemm_router_amd.layer import MoELayer
+    E = len(REMAINDER_COUNTS)
+    logits = remainder_logits(REMAINDER_COUNTS, E, 61)
+    cfg = wl.config("tiny", name="row_classes", T=logits.shape[0], H=192, I=128, E=E, k=1, seed=61, backward=True)
+    X, dY = wl.make_x(cfg), wl.make_dy(cfg)
+    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k).load_weights(W["gate"], W["up"], W["down"])
+    layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=True)
+    pl = layer.plan(cfg.T, True)
+    torch.cuda.synchronize()
+    fn = lambda n: host_weight_fn(cfg, n)
+    idx, w, off, h, O, Y, _, _ = _oracle_forward(cfg, logits, X, fn)
+    assert np.array_equal(np.diff(off), REMAINDER_COUNTS)
+    assert np.array_equal(pl["offsets"].cpu().numpy(), off)
+    check_close(to_f64(pl["H_rows"]), h, "h")
+    check_close(to_f64(pl["O_rows"]), O, "O")
+    check_close(to_f64(pl["Y"]), Y, "Y")
+    dX, dWg, dWu, dWd, dtw = layer.backward(to_dev(X), to_dev(dY))
+    torch.cuda.synchronize()
+    ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), E=cfg.E)
+    amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn)
+    check_close(to_f64(dX), ref["dX"], "dX")
+    check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w", ambiguity=amb_dtw)
+    g = {"dWg": to_f64(dWg), "dWu": to_f64(dWu), "dWd": to_f64(dWd)}
+    for key in ("dWg", "dWu", "dWd"):
+        for e in range(cfg.E):
+            check_close(g[key][e], ref["dW"][key][e], f"{key}[{e}] ({REMAINDER_COUNTS[e]} rows)",
+                        ambiguity=amb_dwd.get(e) if key == "dWd" else None)
+
+
 ACTS = [("swiglu", 0.0), ("swiglu_clamp", 1.0), ("swiglu_oai", 1.0), ("swiglu_oai", 7.0), ("geglu", 0.0),
         ("reglu", 0.0)]
 ACT_CFGS = [wl.config("tiny", name="act_rows", T=300, H=320, I=192, E=5, k=3, seed=51),
