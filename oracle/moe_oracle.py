@@ -270,7 +270,10 @@ def _as_f64(w) -> np.ndarray:
 
 
 def _expert_getter(W):
-    """W: array [E, K, N] (bits or values) or a callable e -> [K, N]."""
+    """W: array [E, K, N] (bits or values) or a callable e -> [K, N]; None (the gate of an
+    ungated expert) gives None for every expert."""
+    if W is None:
+        return lambda e: None
     if callable(W):
         return lambda e: _as_f64(W(e))
     return lambda e: _as_f64(W[e])
@@ -286,8 +289,17 @@ def _expert_getter(W):
 #   swiglu_oai    g sigmoid(1.702 g) (u + 1), g = min(G, c), u = clamp(U, -c, c)
 #   geglu         gelu(G) U, gelu(x) = x Phi(x) with the normal CDF Phi (erf form)
 #   reglu         max(G, 0) U
+# and one ungated activation (LightMoE "MoE inference": its experts load only an up and a
+# down weight), whose h depends on U alone:
+#   relu2         max(U, 0)^2
 # ----------------------------------------------------------------------------
-ACTIVATIONS = ("swiglu", "swiglu_clamp", "swiglu_oai", "geglu", "reglu")
+ACTIVATIONS = ("swiglu", "swiglu_clamp", "swiglu_oai", "geglu", "reglu", "relu2")
+UNGATED = ("relu2",)
+
+
+def is_gated(act: str) -> bool:
+    """Whether the expert has a gate projection (every activation but ReLU^2)."""
+    return act not in UNGATED
 OAI_ALPHA = 1.702
 
 
@@ -304,9 +316,11 @@ def _clamps(G, U, act, limit):
 
 
 def activation(G, U, act: str = "swiglu", limit=None):
-    """h = f(G, U) elementwise, float64."""
-    G = np.asarray(G, dtype=np.float64)
+    """h = f(G, U) elementwise, float64 (G is ignored, and may be None, for ReLU^2)."""
     U = np.asarray(U, dtype=np.float64)
+    if act == "relu2":
+        return np.maximum(U, 0.0) ** 2
+    G = np.asarray(G, dtype=np.float64)
     g, u = _clamps(G, U, act, limit)
     if act in ("swiglu", "swiglu_clamp"):
         return silu(g) * u
@@ -322,9 +336,12 @@ def activation(G, U, act: str = "swiglu", limit=None):
 
 def activation_grads(G, U, act: str = "swiglu", limit=None):
     """(df/dG, df/dU) elementwise, float64 (a clamp passes the gradient where its
-    argument lies inside the bounds, the bounds included)."""
-    G = np.asarray(G, dtype=np.float64)
+    argument lies inside the bounds, the bounds included).  ReLU^2 has no gate: its
+    df/dG is None."""
     U = np.asarray(U, dtype=np.float64)
+    if act == "relu2":
+        return None, 2.0 * np.maximum(U, 0.0)
+    G = np.asarray(G, dtype=np.float64)
     g, u = _clamps(G, U, act, limit)
     if act in ("swiglu_clamp", "swiglu_oai"):
         pg = (G <= limit).astype(np.float64)
@@ -350,18 +367,19 @@ def expert_forward_rows(x_rows, wg, wu, wd, mxfp8: bool = False, exact: bool = F
     """One expert's MLP on rows x_rows [n, H] (float64 values).
 
     G = x Wg, U = x Wu, h = bf16(f(G, U)), O = bf16(h Wd), f = ``activation(.., act, limit)``
-    (SwiGLU by default).  With
+    (SwiGLU by default; ReLU^2 has no gate: wg is not used and G is None).  With
     ``mxfp8`` the GEMM operands x, W and h are the values their MXFP8 (32-long
     blocks along the contraction axis) representation holds.  ``exact``
     skips every rounding (used to check derivatives).
     Returns (G, U, h, O) as float64.
     """
+    gated = is_gated(act)
     if mxfp8:
         x_rows = mx_fake_quant(x_rows)
-        wg = mx_fake_quant(wg.T).T
+        wg = mx_fake_quant(wg.T).T if gated else None
         wu = mx_fake_quant(wu.T).T
         wd = mx_fake_quant(wd.T).T
-    G = x_rows @ wg
+    G = x_rows @ wg if gated else None
     U = x_rows @ wu
     h = activation(G, U, act, limit)
     if not exact:
@@ -378,8 +396,8 @@ def expert_mlp(X, row_token, offsets, W_gate, W_up, W_down, mxfp8: bool = False,
     """Expert-major expert MLP over all routed rows.
 
     X: [T, H] (bf16 bits or values); row_token / offsets from ``dispatch``;
-    W_gate, W_up: [E, H, I]; W_down: [E, I, H] (or callables e -> matrix).
-    Returns (h [A, I], O [A, H]) as float64 (bf16 values).  Rows of experts
+    W_gate, W_up: [E, H, I]; W_down: [E, I, H] (or callables e -> matrix; W_gate None for
+    ReLU^2).  Returns (h [A, I], O [A, H]) as float64 (bf16 values).  Rows of experts
     not in ``experts`` (when given) are left NaN.
     """
     Xv = _as_f64(X)
@@ -387,7 +405,7 @@ def expert_mlp(X, row_token, offsets, W_gate, W_up, W_down, mxfp8: bool = False,
     E = offsets.shape[0] - 1
     A = int(offsets[-1])
     gg, gu, gd = _expert_getter(W_gate), _expert_getter(W_up), _expert_getter(W_down)
-    I = gg(0).shape[1] if E else 0
+    I = gu(0).shape[1] if E else 0
     H = Xv.shape[1]
     h = np.full((A, I), np.nan)
     O = np.full((A, H), np.nan)
@@ -464,11 +482,13 @@ def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = Fals
     w_rows: [n] routing weights.  G, U, h are recomputed as in the forward.
     P = dY W_down^T; dwt = <h, P>; dh = w P; dg = dh * df/dG, du = dh * df/dU
     (SwiGLU: du = dh * silu(G), dg = dh * U * silu'(G)); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
-    dWg = x^T dg, dWu = x^T du, dWd = h^T dO (not yet rounded).
+    dWg = x^T dg, dWu = x^T du, dWd = h^T dO (not yet rounded).  ReLU^2 has no gate:
+    du = dh * 2 max(U, 0), dXr = du Wu^T, and dg, dWg are None.
     Returns dict of float64 arrays.
     """
     rnd = (lambda a: a) if exact else bf16_round
-    G = x_rows @ wg
+    gated = is_gated(act)
+    G = x_rows @ wg if gated else None
     U = x_rows @ wu
     h = activation(G, U, act, limit)
     if not exact:
@@ -478,10 +498,10 @@ def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = Fals
     dh = w_rows[:, None] * P
     fg, fu = activation_grads(G, U, act, limit)
     du = dh * fu
-    dg = dh * fg
+    dg = dh * fg if gated else None
     dO = rnd(w_rows[:, None] * dy_rows)
-    dXr = dg @ wg.T + du @ wu.T
-    return {"dwt": dwt, "dXr": dXr, "dWg": x_rows.T @ dg, "dWu": x_rows.T @ du,
+    dXr = dg @ wg.T + du @ wu.T if gated else du @ wu.T
+    return {"dwt": dwt, "dXr": dXr, "dWg": x_rows.T @ dg if gated else None, "dWu": x_rows.T @ du,
             "dWd": h.T @ dO, "dg": dg, "du": du, "h": h}
 
 
@@ -492,7 +512,7 @@ def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact:
 
     Returns dict with dX [T, H], dW_gate / dW_up [E, H, I], dW_down [E, I, H]
     (bf16 values after exact accumulation; only for ``experts`` when given, the
-    rest NaN; experts with no rows get exact zeros) and d_topk_w [T, k]
+    rest NaN; experts with no rows get exact zeros; dW_gate None for ReLU^2) and d_topk_w [T, k]
     (float64).  dX sums a token's k row contributions in slot order and is
     only complete when every expert is processed.  ``E`` is needed when the
     weights are given as callables.
@@ -505,8 +525,9 @@ def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact:
     H = Xv.shape[1]
     gg, gu, gd = _expert_getter(W_gate), _expert_getter(W_up), _expert_getter(W_down)
     if E is None:
-        E = W_gate.shape[0]
-    I = gg(int(idx[0, 0])).shape[1]
+        E = W_up.shape[0]
+    I = gu(int(idx[0, 0])).shape[1]
+    gated = is_gated(act)
     todo = range(E) if experts is None else sorted(set(experts))
     dW = {n: {} for n in ("dWg", "dWu", "dWd")}
     dxr = np.zeros((T, k, H)) if want_dx else None
@@ -514,12 +535,12 @@ def backward(X, dY, topk_idx, topk_w, W_gate, W_up, W_down, experts=None, exact:
     for e in todo:
         tt, jj = np.nonzero(idx == e)            # (t, j) in slot order
         if len(tt) == 0:
-            dW["dWg"][e] = np.zeros((H, I))
+            dW["dWg"][e] = np.zeros((H, I)) if gated else None
             dW["dWu"][e] = np.zeros((H, I))
             dW["dWd"][e] = np.zeros((I, H))
             continue
         r = expert_backward_rows(Xv[tt], dYv[tt], w[tt, jj], gg(e), gu(e), gd(e), exact=exact, act=act, limit=limit)
-        dW["dWg"][e] = rnd(r["dWg"])
+        dW["dWg"][e] = rnd(r["dWg"]) if gated else None
         dW["dWu"][e] = rnd(r["dWu"])
         dW["dWd"][e] = rnd(r["dWd"])
         dwt[tt, jj] = r["dwt"]
@@ -597,7 +618,7 @@ def bf16_round_delta(x_exact, rel_eps: float = 2.0 ** -14):
 def h_ambiguity_rows(x_rows, wg, wu, act: str = "swiglu", limit=None):
     """Per element of h = bf16(f(x Wg, x Wu)) for one expert's rows: the change another
     valid bf16 rounding of h can make (``bf16_round_delta`` of the exact value)."""
-    G = x_rows @ wg
+    G = x_rows @ wg if is_gated(act) else None
     U = x_rows @ wu
     return bf16_round_delta(activation(G, U, act, limit))
 

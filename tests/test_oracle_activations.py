@@ -1,7 +1,7 @@
-"""Pins of the oracle's gated activations h = f(G, U) and their derivatives:
-textbook values (sigmoid(1), the normal CDF at 1), GELU's odd-part identity,
-the clamps' limit cases, and the derivatives against float64 autograd of the
-forward functions and against central differences."""
+"""Pins of the oracle's activations h = f(G, U) (and the ungated ReLU^2, h = f(U))
+and their derivatives: textbook values (sigmoid(1), the normal CDF at 1, squares),
+GELU's odd-part identity, the clamps' limit cases, and the derivatives against
+float64 autograd of the forward functions and against central differences."""
 import math
 
 import numpy as np
@@ -29,6 +29,12 @@ def test_textbook_values():
     # SwiGLU-OAI: g sigmoid(1.702 g) (u + 1)
     assert orc.activation(2.0, 0.0, "swiglu_oai", 7.0) == pytest.approx(2.0 / (1.0 + math.exp(-3.404)), rel=1e-15)
     assert orc.activation(2.0, -1.0, "swiglu_oai", 7.0) == 0.0
+    # ReLU^2: max(U, 0)^2, no gate
+    assert orc.activation(None, 3.0, "relu2") == 9.0
+    assert orc.activation(-5.0, 1.5, "relu2") == 2.25
+    assert orc.activation(5.0, -2.0, "relu2") == 0.0
+    assert orc.activation_grads(None, np.array([3.0, -2.0, 0.0]), "relu2")[1].tolist() == [6.0, 0.0, 0.0]
+    assert orc.activation_grads(None, 3.0, "relu2")[0] is None
 
 
 def test_gelu_odd_part_and_limits():
@@ -66,6 +72,8 @@ def _torch_forward(g, u, act, lim):
         return gc * torch.sigmoid(1.702 * gc) * (torch.clamp(u, -lim, lim) + 1)
     if act == "geglu":
         return torch.nn.functional.gelu(g) * u
+    if act == "relu2":
+        return torch.relu(u) ** 2
     return torch.relu(g) * u
 
 
@@ -80,7 +88,10 @@ def test_grads_match_autograd(act):
     u = torch.tensor(U, requires_grad=True)
     _torch_forward(g, u, act, lim).sum().backward()
     fg, fu = orc.activation_grads(G, U, act, lim)
-    assert np.allclose(fg, g.grad.numpy(), rtol=1e-12, atol=1e-13)
+    if orc.is_gated(act):
+        assert np.allclose(fg, g.grad.numpy(), rtol=1e-12, atol=1e-13)
+    else:
+        assert fg is None and g.grad is None
     assert np.allclose(fu, u.grad.numpy(), rtol=1e-12, atol=1e-13)
     assert np.allclose(orc.activation(G, U, act, lim), _torch_forward(g, u, act, lim).detach().numpy(),
                        rtol=1e-13, atol=1e-14)
@@ -99,7 +110,10 @@ def test_grads_match_central_differences(act):
     fg, fu = orc.activation_grads(G, U, act, lim)
     dg = (orc.activation(G + eps, U, act, lim) - orc.activation(G - eps, U, act, lim)) / (2 * eps)
     du = (orc.activation(G, U + eps, act, lim) - orc.activation(G, U - eps, act, lim)) / (2 * eps)
-    assert np.allclose(fg, dg, rtol=1e-6, atol=1e-7)
+    if orc.is_gated(act):
+        assert np.allclose(fg, dg, rtol=1e-6, atol=1e-7)
+    else:
+        assert fg is None and np.all(dg == 0)
     assert np.allclose(fu, du, rtol=1e-6, atol=1e-7)
 
 
@@ -113,12 +127,16 @@ def test_layer_backward_with_activation_matches_autograd():
     wg, wu, wd = (rng.standard_normal(s) / 3 for s in ((H, I), (H, I), (I, H)))
     for act in orc.ACTIVATIONS:
         lim = LIMIT.get(act)
-        r = orc.expert_backward_rows(x, dy, w, wg, wu, wd, exact=True, act=act, limit=lim)
+        gated = orc.is_gated(act)
+        r = orc.expert_backward_rows(x, dy, w, wg if gated else None, wu, wd, exact=True, act=act, limit=lim)
         tx, twg, twu, twd = (torch.tensor(a, requires_grad=True) for a in (x, wg, wu, wd))
         h = _torch_forward(tx @ twg, tx @ twu, act, lim)
         o = h @ twd
         (torch.tensor(w)[:, None] * o * torch.tensor(dy)).sum().backward()
-        assert np.allclose(r["dWg"], twg.grad.numpy(), rtol=1e-10, atol=1e-12), act
+        if gated:
+            assert np.allclose(r["dWg"], twg.grad.numpy(), rtol=1e-10, atol=1e-12), act
+        else:
+            assert r["dWg"] is None and r["dg"] is None
         assert np.allclose(r["dWu"], twu.grad.numpy(), rtol=1e-10, atol=1e-12), act
         assert np.allclose(r["dXr"], tx.grad.numpy(), rtol=1e-10, atol=1e-12), act
         assert np.allclose(r["dWd"], twd.grad.numpy(), rtol=1e-10, atol=1e-12), act
