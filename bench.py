@@ -88,9 +88,11 @@ def device_weights(cfg, name, experts=None):
 
 
 def step_flops(cfg, active_rows):
-    A, H, I = active_rows, cfg.H, cfg.I
-    fwd = 6.0 * A * H * I
-    bwd = 12.0 * A * H * I if cfg.backward else 0.0
+    """Algorithmic FLOP of the expert MLP (2 H I per weight matrix and row) and of its backward
+    (dX, the weight gradients and P: 4 H I per matrix and row; the recompute is not counted)."""
+    A, H, I, m = active_rows, cfg.H, cfg.I, len(cfg.mats)
+    fwd = 2.0 * m * A * H * I
+    bwd = 4.0 * m * A * H * I if cfg.backward else 0.0
     return fwd, bwd
 
 
@@ -109,8 +111,8 @@ def cpu_baseline(cfg, logits, X, dY, min_s=10.0, max_reps=20):
     toks = np.sort(np.random.default_rng(0).choice(cfg.T, ntok, replace=False))
     idx, w = orc.route(logits, cfg.k)
     cache = {(n, int(e)): wl.make_expert_weight(cfg, n, int(e))
-             for n in ("gate", "up", "down") for e in np.unique(idx[toks])}
-    fn = lambda n: (lambda e: cache[(n, int(e))])
+             for n in cfg.mats for e in np.unique(idx[toks])}
+    fn = lambda n: (lambda e: cache[(n, int(e))]) if n in cfg.mats else None
     reps, t_route, t_mlp = 0, 0.0, 0.0
     while reps < max_reps and (t_route + t_mlp) < min_s:
         t0 = time.perf_counter()
@@ -157,12 +159,12 @@ def main():
         from grouped_gemm_router_amd import binding as B
         idx, _ = B.route(torch.from_numpy(logits_np).cuda(), cfg.k)
         experts = torch.unique(idx).cpu().numpy()
-    W = {n: device_weights(cfg, n, experts) for n in ("gate", "up", "down")}
+    W = {n: device_weights(cfg, n, experts) for n in cfg.mats}
     logits = torch.from_numpy(logits_np).cuda()
     X = torch.from_numpy(X_np.view(np.int16)).cuda().view(torch.bfloat16)
     dY = torch.from_numpy(dY_np.view(np.int16)).cuda().view(torch.bfloat16) if cfg.backward else None
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation,
-                     act_limit=cfg.act_limit).load_weights(W["gate"], W["up"], W["down"], keep_math=cfg.backward)
+                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"], keep_math=cfg.backward)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -231,7 +233,7 @@ def main():
     tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if cfg.dtype == "mxfp8" else PEAK_BF16_TFLOPS
     wbytes = 1 if cfg.dtype == "mxfp8" else 2
-    weight_bytes = n_active * 3 * cfg.H * cfg.I * wbytes
+    weight_bytes = n_active * len(cfg.mats) * cfg.H * cfg.I * wbytes
     act_bytes = cfg.T * cfg.E * 4 + cfg.T * cfg.H * 2 * 2
     out = {
         "metric": METRIC,
@@ -262,7 +264,7 @@ def main():
                              "value_at_p50": round((f_fwd + f_bwd) / (float(np.median(cold_ms)) * 1e-3) / 1e12, 3)}
     if graph is None:
         mlp_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        mlp_flops = 6.0 * cfg.A * cfg.H * cfg.I
+        mlp_flops = step_flops(cfg, cfg.A)[0]
         # algorithmic bytes of one call: the active experts' weights once, X rows in and h rows
         # out (gate/up), h rows in and O rows out (down)
         mlp_bytes = weight_bytes + cfg.A * (cfg.H + cfg.I) * 2 * 2

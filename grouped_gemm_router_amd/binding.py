@@ -19,7 +19,9 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE", 3: "MOE_ERR_WORKSPACE",
           4: "MOE_ERR_UNSUPPORTED_DEVICE", 5: "MOE_ERR_HIP"}
 DTYPE = {"bf16": 0, "mxfp8": 1}
-ACT = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_oai": 2, "geglu": 3, "reglu": 4}
+ACT = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_oai": 2, "geglu": 3, "reglu": 4, "relu2": 5}
+# ReLU^2 experts have no gate weight: every gate argument is None (NULL) for it
+UNGATED = ("relu2",)
 CALL_DISPATCH, CALL_EXPERT_MLP, CALL_BACKWARD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_validate_problem", "moe_workspace_size", "moe_check_device",
@@ -179,20 +181,24 @@ def mx_quantize(x: torch.Tensor):
 def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=None, O_rows=None, ws=None,
                activation="swiglu", act_limit=0.0):
     """Expert MLP over the dispatched rows.  bf16 weights [E, I, H] / [E, H, I]
-    (pack_weights), or MXFP8 codes with ``scales = (Sg, Su, Sd)``."""
+    (pack_weights), or MXFP8 codes with ``scales = (Sg, Su, Sd)``.  For ReLU^2 the
+    gate weight (and Sg) is None."""
     T, H = X.shape
-    E, I, _ = Wg_t.shape
+    E, I, _ = Wu_t.shape
     mx = scales is not None
+    gated = activation not in UNGATED
     _expect(X, "X", torch.bfloat16, (T, H))
     wdt = torch.uint8 if mx else torch.bfloat16
-    _expect(Wg_t, "Wg_t", wdt, (E, I, H))
+    if gated:
+        _expect(Wg_t, "Wg_t", wdt, (E, I, H))
     _expect(Wu_t, "Wu_t", wdt, (E, I, H))
     _expect(Wd_t, "Wd_t", wdt, (E, H, I))
     _expect(offsets, "expert_offsets", torch.int32, (E + 1,))
     _expect(row_token, "row_token", torch.int32, (T * k,))
     if mx:
         Sg, Su, Sd = scales
-        _expect(Sg, "Sg", torch.uint8, (E, I, H // 32))
+        if gated:
+            _expect(Sg, "Sg", torch.uint8, (E, I, H // 32))
         _expect(Su, "Su", torch.uint8, (E, I, H // 32))
         _expect(Sd, "Sd", torch.uint8, (E, H, I // 32))
     else:
@@ -228,14 +234,17 @@ def combine(O_rows, slot_row, topk_w, Y=None):
 
 def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, W_gate, W_up, W_down, Wg_t, Wu_t,
              out=None, ws=None, activation="swiglu", act_limit=0.0):
-    """Returns (dX, dW_gate, dW_up, dW_down, d_topk_w)."""
+    """Returns (dX, dW_gate, dW_up, dW_down, d_topk_w); for ReLU^2 W_gate and Wg_t are None
+    and so is dW_gate."""
     T, H = X.shape
-    E, _, I = W_gate.shape
+    E, _, I = W_up.shape
     k = topk_w.shape[1]
+    gated = activation not in UNGATED
     for name, t, shape in (("X", X, (T, H)), ("dY", dY, (T, H)), ("W_gate", W_gate, (E, H, I)),
                            ("W_up", W_up, (E, H, I)), ("W_down", W_down, (E, I, H)),
                            ("Wg_t", Wg_t, (E, I, H)), ("Wu_t", Wu_t, (E, I, H))):
-        _expect(t, name, torch.bfloat16, shape)
+        if gated or name not in ("W_gate", "Wg_t"):
+            _expect(t, name, torch.bfloat16, shape)
     _expect(topk_w, "topk_w", torch.float32, (T, k))
     for name, t in (("row_token", row_token), ("row_slot", row_slot), ("slot_row", slot_row)):
         _expect(t, name, torch.int32, (T * k,))
@@ -243,7 +252,7 @@ def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, W_gate, W_up
     dev = X.device
     if out is None:
         out = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
-               torch.empty(E, H, I, dtype=torch.bfloat16, device=dev),
+               torch.empty(E, H, I, dtype=torch.bfloat16, device=dev) if gated else None,
                torch.empty(E, H, I, dtype=torch.bfloat16, device=dev),
                torch.empty(E, I, H, dtype=torch.bfloat16, device=dev),
                torch.empty(T, k, dtype=torch.float32, device=dev))

@@ -33,7 +33,7 @@ moe_status check_problem(const moe_problem* p) {
   if (s != MOE_OK) return s;
   if (p->H < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_MXFP8) return MOE_ERR_INVALID_ARG;
-  if (p->activation < MOE_ACT_SWIGLU || p->activation > MOE_ACT_REGLU) return MOE_ERR_INVALID_ARG;
+  if (p->activation < MOE_ACT_SWIGLU || p->activation > MOE_ACT_RELU2) return MOE_ERR_INVALID_ARG;
   if ((p->activation == MOE_ACT_SWIGLU_CLAMP || p->activation == MOE_ACT_SWIGLU_OAI) &&
       !(p->act_limit > 0.f && p->act_limit < 3.0e38f))
     return MOE_ERR_INVALID_ARG;
@@ -52,7 +52,7 @@ size_t mlp_ws(const moe_problem* p) {
 
 size_t bwd_ws(const moe_problem* p) {
   const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
-  const size_t nparts = moe::bwd_nparts(p->I);
+  const size_t nparts = moe::bwd_nparts(p->I, p->activation);
   return align_up(A * I * 4) + 2 * align_up(A * 2 * I * 2) + align_up(A * I * 2) + align_up(A * H * 4) +
          align_up(A * nparts * 4);
 }
@@ -180,10 +180,11 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
                                   void* H_rows, void* O_rows, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
-  if (!X || !expert_offsets || !Wg_t || !Wu_t || !Wd_t || !H_rows || !O_rows) return MOE_ERR_INVALID_ARG;
+  const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
+  if (!X || !expert_offsets || (gated && !Wg_t) || !Wu_t || !Wd_t || !H_rows || !O_rows) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && !row_token) return MOE_ERR_INVALID_ARG;
   const bool mx = p->dtype == MOE_DTYPE_MXFP8;
-  if (mx != (Sg && Su && Sd)) return MOE_ERR_INVALID_ARG;
+  if (mx != ((Sg || !gated) && Su && Sd)) return MOE_ERR_INVALID_ARG;
   if (!mx && (Sg || Su || Sd)) return MOE_ERR_INVALID_ARG;
   const size_t need = mlp_ws(p);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
@@ -255,8 +256,10 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
   if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
-  if (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !expert_offsets || !W_gate || !W_up ||
-      !W_down || !Wg_t || !Wu_t || !dX || !dW_gate || !dW_up || !dW_down || !d_topk_w)
+  const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
+  if (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !expert_offsets || (gated && !W_gate) ||
+      !W_up || !W_down || (gated && !Wg_t) || !Wu_t || !dX || (gated && !dW_gate) || !dW_up || !dW_down ||
+      !d_topk_w)
     return MOE_ERR_INVALID_ARG;
   const size_t need = bwd_ws(p);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -277,7 +280,7 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   a.Wg = (const uint16_t*)W_gate;
   a.Wu = (const uint16_t*)W_up;
   a.Wd = (const uint16_t*)W_down;
-  a.nparts = moe::bwd_nparts(p->I);
+  a.nparts = moe::bwd_nparts(p->I, p->activation);
   a.P = (float*)w8;
   w8 += align_up(A * I * 4);
   a.dGU = (uint16_t*)w8;

@@ -38,10 +38,17 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 __device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu_f32(float x) { return x * sigmoid_f32(x); }
 
-// Gated activations h = f(g, u) (the moe_activation codes) and their partial
+// Activations h = f(g, u) (the moe_activation codes) and their partial
 // derivatives, in fp32.  Clamps pass the gradient where their argument lies
-// inside the bounds, the bounds included.
-enum : int { ACT_SWIGLU = 0, ACT_SWIGLU_CLAMP = 1, ACT_SWIGLU_OAI = 2, ACT_GEGLU = 3, ACT_REGLU = 4 };
+// inside the bounds, the bounds included.  ReLU^2 is ungated (h = f(u)): its
+// kernels have no gate operand and call relu2 / relu2_grad.
+enum : int { ACT_SWIGLU = 0, ACT_SWIGLU_CLAMP = 1, ACT_SWIGLU_OAI = 2, ACT_GEGLU = 3, ACT_REGLU = 4, ACT_RELU2 = 5 };
+__host__ __device__ constexpr bool act_gated(int act) { return act != ACT_RELU2; }
+__device__ __forceinline__ float relu2(float u) {
+  const float r = fmaxf(u, 0.f);
+  return r * r;
+}
+__device__ __forceinline__ float relu2_grad(float u) { return 2.f * fmaxf(u, 0.f); }
 // Kernels take the activation as a template constant ACTK: ACT_SWIGLU for the
 // default path (nothing else compiled in), ACT_ANY to switch on the run-time code.
 constexpr int ACT_ANY = -1;

@@ -160,24 +160,25 @@ __device__ __forceinline__ void decode_gateup(const GemmArgs& p) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int k_lo = wave_u * ksteps / DEC_GU_WAVES, nks = (wave_u + 1) * ksteps / DEC_GU_WAVES - k_lo;
   const size_t wrow = ((size_t)e * p.I + i0 + (lane & 15)) * p.H + (lane >> 4) * 16 + (size_t)k_lo * 64;
-  const uint16_t* wg = p.Wg_t + wrow;
+  constexpr bool GATED = act_gated(ACTK);            // ReLU^2 streams W_up only
+  const uint16_t* wg = GATED ? p.Wg_t + wrow : nullptr;
   const uint16_t* wu = p.Wu_t + wrow;
   const int t = min(lane & 15, n - 1);
   const uint16_t* xr = p.X + (size_t)p.row_token[r0 + t] * p.H + (lane >> 4) * 16 + (size_t)k_lo * 64;
   f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
   uint4 bg[DEC_PF][2], bu[DEC_PF][2], bx[DEC_PF][2];
   auto load = [&](int kk, int s) {
-    WaveStream<DEC_PF>::load(wg, kk, bg[s]);
+    if constexpr (GATED) WaveStream<DEC_PF>::load(wg, kk, bg[s]);
     WaveStream<DEC_PF>::load(wu, kk, bu[s]);
     WaveStream<DEC_PF>::load_x(xr, kk, bx[s]);
   };
   auto step = [&](int s) {
-    ag = mfma2(bg[s], bx[s], ag);
+    if constexpr (GATED) ag = mfma2(bg[s], bx[s], ag);
     au = mfma2(bu[s], bx[s], au);
   };
   stream_steps(nks, load, step);
   if (wave > 0) {
-    part[wave - 1][0][lane] = ag;
+    if constexpr (GATED) part[wave - 1][0][lane] = ag;
     part[wave - 1][1][lane] = au;
   }
   __syncthreads();
@@ -186,12 +187,13 @@ __device__ __forceinline__ void decode_gateup(const GemmArgs& p) {
   if ((lane & 15) < n) {
 #pragma unroll
     for (int w = 0; w < DEC_GU_WAVES - 1; ++w) {
-      ag += part[w][0][lane];
+      if constexpr (GATED) ag += part[w][0][lane];
       au += part[w][1][lane];
     }
     float h[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) h[v] = gated_act(ag[v], au[v], act_code(ACTK, p.act), p.act_limit);
+    for (int v = 0; v < 4; ++v)
+      h[v] = GATED ? gated_act(ag[v], au[v], act_code(ACTK, p.act), p.act_limit) : relu2(au[v]);
     store_bf16x4(p.Hrows + (size_t)(r0 + (lane & 15)) * p.I + i0 + 4 * (lane >> 4), h[0], h[1], h[2], h[3]);
   }
 }
@@ -199,6 +201,8 @@ __device__ __forceinline__ void decode_gateup(const GemmArgs& p) {
 __global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup(const GemmArgs p) { decode_gateup<ACT_SWIGLU>(p); }
 // any other gated activation (run-time code)
 __global__ void __launch_bounds__(DEC_GU_NT) k_decode_gateup_act(const GemmArgs p) { decode_gateup<ACT_ANY>(p); }
+// the ungated ReLU^2 expert (W_up only)
+__global__ void __launch_bounds__(DEC_GU_NT) k_decode_up(const GemmArgs p) { decode_gateup<ACT_RELU2>(p); }
 
 // down: one workgroup per (expert, row group, 64 hidden columns), one wave per
 // 16 columns over the whole intermediate axis.
@@ -238,8 +242,8 @@ hipError_t launch_decode_mlp(const GemmArgs& a, hipStream_t s) {
   const long rows = (long)a.T * a.k;
   const long experts = rows < a.E ? rows : a.E;
   const long groups = rows / 16 + experts;
-  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_decode_gateup : k_decode_gateup_act, dim3((unsigned)(groups * (a.I / 16))),
-                     dim3(DEC_GU_NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_decode_gateup : a.act == ACT_RELU2 ? k_decode_up : k_decode_gateup_act,
+                     dim3((unsigned)(groups * (a.I / 16))), dim3(DEC_GU_NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_down, dim3((unsigned)(groups * (a.H / 64))), dim3(DEC_NT), 0, s, a);

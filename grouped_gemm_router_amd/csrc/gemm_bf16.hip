@@ -23,6 +23,9 @@ using CfgRows = RowCfg<256, 256, 2, MOE_ROWS_WAVES_N, MOE_ROWS_BK, (MOE_ROWS_BK 
 using CfgRem192 = RowCfg<192, 256, 2, 4, 64, 2>;
 using CfgRem128 = RowCfg<128, 256, 2, 4, 64, 3>;
 using CfgRem64 = RowCfg<64, 256, 1, 8, 64, 3>;
+// the ungated (ReLU^2) recompute: 128 x 256 tiles, three 48 KB stages (its epilogue, with
+// 256-row tiles, would spill)
+using CfgRecUp = RowCfg<128, 256, 2, 4, 64, 3>;
 
 // ------------------------------------------------------------------------
 // Row sources of the direct-to-LDS row-grouped GEMMs: a wave-uniform base and
@@ -68,6 +71,32 @@ struct RSrcGateUpW {
   __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
     const int col = t.nt * (C::BN / 2) + (row / 32) * 16 + (row % 16);
     return (uint32_t)min(col, p.I - 1) * (uint32_t)p.H;
+  }
+};
+struct RSrcUpW {         // packed W_up [E, I, H]: the B rows of the ungated (ReLU^2) up GEMM
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
+    return p.Wu_t + (size_t)t.e * p.I * p.H + k0;
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.I - 1) * (uint32_t)p.H;
+  }
+};
+// du rows of the ungated backward as [T*k, K = 2I]: the bf16 values [T*k, I] then their bf16
+// remainders [T*k, I]
+struct RSrcDU2 {
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile&, int, int k0) {
+    return k0 < p.I ? p.dGU + k0 : p.dGU_lo + (k0 - p.I);
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)clamp_row(t, row) * (uint32_t)p.I;
+  }
+};
+struct RSrcUpWT2 {       // W_up [E, H, I] read twice along K, as [E, N = H, K = 2I]
+  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
+    return p.Wu + (size_t)t.e * p.H * p.I + (k0 < p.I ? k0 : k0 - p.I);
+  }
+  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
   }
 };
 struct RSrcDownW {       // packed [E, H, I]
@@ -125,6 +154,22 @@ struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
           return gated_act(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit);
         },
         [](int fn, int q) { return fn * 16 + q * 8; });
+  }
+};
+
+// h = bf16(max(X Wu, 0)^2): the ungated (ReLU^2) expert, one GEMM over the I columns
+template <class C, int PART = ROWS_ALL>
+struct FwdUpOps : RowOpsBase<C, RSrcX, RSrcUpW, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcUpW, PART>::Sched& s, const GemmArgs& p,
+                                    int* pre, int* red) {
+    s.init(p.offsets, p.E, p.I, p.H, pre, red);
+  }
+  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
+                                  int wm, int wn, int lane, uint8_t* wlds) {
+    stage_store_bf16<C, C::WTN, 4>(
+        wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.I, lane,
+        [&](int fm, int fn, int q, int j) { return relu2(acc[fm][fn][4 * q + j]); },
+        [](int fn, int q) { return fn * 32 + q * 8; });
   }
 };
 
@@ -316,6 +361,84 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
   }
 };
 
+// The ungated (ReLU^2) recompute: U again; with P give h = bf16(max(U, 0)^2), the
+// router-weight partial sums <h, P> and du = w P 2 max(U, 0) as a bf16 value and a bf16
+// remainder.  A wave owns 64 columns.  The three bf16 outputs are staged through the wave's
+// LDS scratch one after another, each computed from U and P as it goes (P is read once per
+// output: holding it across them would spill).
+template <class C, int PART = ROWS_ALL>
+struct BwdRecomputeUpOps : RowOpsBase<C, RSrcX, RSrcUpW, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcUpW, PART>::Sched& s, const GemmArgs& p,
+                                    int* pre, int* red) {
+    s.init(p.offsets, p.E, p.I, p.H, pre, red);
+  }
+
+  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
+                                  int wm, int wn, int lane, uint8_t* wlds) {
+    const int col0 = t.n0 + wn * C::WTN;            // first intermediate column of the wave
+    const bool cv = col0 < p.I;                      // I is a multiple of 64: all or none valid
+    const int hc = (lane >> 5) * 4;
+    auto row_of = [&](int fm) { return min(t.m0 + Frag<C>::row(wm, fm, lane), t.m_end - 1); };
+    // P of item group q of fragment (fm, fn) (zeros for columns past I)
+    auto p4 = [&](int rc, int fn, int q) {
+      return cv ? *reinterpret_cast<const float4*>(p.P + (size_t)rc * p.I + col0 + fn * 32 + q * 8 + hc)
+                : make_float4(0, 0, 0, 0);
+    };
+    // router-weight partial sums: <bf16(h), P> over the wave's columns of each row
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int rc = row_of(fm);
+      float dot = 0.f;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 pv = p4(rc, fn, q);
+          const float Pv[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dot += bf16_to_f32(f32_to_bf16(relu2(acc[fm][fn][4 * q + j]))) * Pv[j];
+        }
+      dot += __shfl_xor(dot, 32, 64);                // the other half of the row's columns
+      const int r = t.m0 + Frag<C>::row(wm, fm, lane);
+      if (r < t.m_end && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
+    }
+    if (!cv) return;
+    const int row0 = t.m0 + wm * C::WTM;
+    auto col_of = [](int fn, int q) { return fn * 32 + q * 8; };
+    stage_store_bf16<C, C::WTN, 4>(wlds, p.Hrows, p.I, row0, t.m_end, col0, p.I, lane,
+                                   [&](int fm, int fn, int q, int j) { return relu2(acc[fm][fn][4 * q + j]); }, col_of);
+    // du for item j of group q: w P 2 max(U, 0)
+    auto du = [&](int fm, int fn, int q, int j) {
+      const int rc = row_of(fm);
+      const float Pj = p.P[(size_t)rc * p.I + col0 + fn * 32 + q * 8 + hc + j];
+      return p.topk_w[p.row_slot[rc]] * Pj * relu2_grad(acc[fm][fn][4 * q + j]);
+    };
+    stage_store_bf16<C, C::WTN, 4>(wlds, p.dGU, p.I, row0, t.m_end, col0, p.I, lane, du, col_of);
+    stage_store_bf16<C, C::WTN, 4>(
+        wlds, p.dGU_lo, p.I, row0, t.m_end, col0, p.I, lane,
+        [&](int fm, int fn, int q, int j) {
+          const float v = du(fm, fn, q, j);
+          return v - bf16_to_f32(f32_to_bf16(v));
+        },
+        col_of);
+  }
+};
+
+// dXr = du W_up^T (fp32 rows) of the ungated expert, with du as its bf16 value plus its bf16
+// remainder (two passes over I): ReLU^2's du = w P 2 max(U, 0) reaches several units, and
+// its bf16 value alone leaves dX short of the exact-du result near cancellations
+template <class C, int PART = ROWS_ALL>
+struct BwdDXUpOps : RowOpsBase<C, RSrcDU2, RSrcUpWT2, PART> {
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDU2, RSrcUpWT2, PART>::Sched& s,
+                                    const GemmArgs& p, int* pre, int* red) {
+    s.init(p.offsets, p.E, p.H, 2 * p.I, pre, red);
+  }
+  __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
+                                  int wm, int wn, int lane, uint8_t*) {
+    store_rows_f32<C>(p.dXr, p.H, p.H, t, acc, wm, wn, lane);
+  }
+};
+
 // dXr = [dg | du] [W_gate | W_up]^T (fp32 rows)
 template <class C, int PART = ROWS_ALL>
 struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART> {
@@ -357,6 +480,12 @@ MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
 MOE_ROWS_KERNEL(k_bwd_recompute_act, BwdRecomputeOpsAny)
 MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps)
+// the ungated (ReLU^2) expert
+MOE_ROWS_SPLIT_KERNEL(k_fwd_up, FwdUpOps)
+__global__ void __launch_bounds__(CfgRecUp::NT) k_bwd_recompute_up(const GemmArgs p) {
+  rows_gemm_body<CfgRecUp, BwdRecomputeUpOps<CfgRecUp>, GemmArgs>(p);
+}
+MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows_up, BwdDXUpOps)
 
 template <class C>
 static int row_grid(const GemmArgs& a, int N) {
@@ -368,6 +497,10 @@ static int row_grid(const GemmArgs& a, int N) {
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
 hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s) {
+  if (a.act == ACT_RELU2) {
+    hipLaunchKernelGGL(k_fwd_up, dim3(row_grid<CfgRows>(a, a.I)), dim3(CfgRows::NT), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_fwd_gateup : k_fwd_gateup_act, dim3(row_grid<CfgRows>(a, 2 * a.I)),
                      dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
@@ -380,16 +513,22 @@ hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_bwd_p, dim3(row_grid<CfgRows>(a, a.I)), dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
-int bwd_nparts(int I) {
-  return ((2 * I + CfgRows::BN - 1) / CfgRows::BN) * CfgRows::WAVES_N;
+int bwd_nparts(int I, int act) {
+  const int N = act_gated(act) ? 2 * I : I;        // columns of the recompute GEMM
+  return ((N + CfgRows::BN - 1) / CfgRows::BN) * CfgRows::WAVES_N;
 }
 hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s) {
+  if (a.act == ACT_RELU2) {
+    hipLaunchKernelGGL(k_bwd_recompute_up, dim3(row_grid<CfgRecUp>(a, a.I)), dim3(CfgRecUp::NT), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_bwd_recompute : k_bwd_recompute_act, dim3(row_grid<CfgRows>(a, 2 * a.I)),
                      dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dx_rows, dim3(row_grid<CfgRows>(a, a.H)), dim3(CfgRows::NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_RELU2 ? k_bwd_dx_rows_up : k_bwd_dx_rows, dim3(row_grid<CfgRows>(a, a.H)),
+                     dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
 // dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials.

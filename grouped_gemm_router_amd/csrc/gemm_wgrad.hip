@@ -308,11 +308,12 @@ struct WgDownOps {
 
 // [dW_gate | dW_up][e] = sum_r x_r^T [dg | du]_r: A = gathered x rows [A, H],
 // B = [dg | du] rows [A, 2I] as bf16 values (nb = 0) and bf16 remainders (nb = 1).
+// The ungated (ReLU^2) expert has du rows [A, I] only and gets dW_up alone.
 struct WgGateUpOps {
   __device__ static int M(const GemmArgs& p) { return p.H; }
-  __device__ static int N(const GemmArgs& p) { return 2 * p.I; }
+  __device__ static int N(const GemmArgs& p) { return act_gated(p.act) ? 2 * p.I : p.I; }
   __device__ static int lda(const GemmArgs& p) { return p.H; }
-  __device__ static int ldb(const GemmArgs& p) { return 2 * p.I; }
+  __device__ static int ldb(const GemmArgs& p) { return N(p); }
   __device__ static const uint16_t* a_rows(const GemmArgs& p) { return p.Xg; }
   __device__ static const uint16_t* b_rows(const GemmArgs& p, int nb) { return nb ? p.dGU_lo : p.dGU; }
   template <class C>
@@ -320,9 +321,11 @@ struct WgGateUpOps {
                                   int lane, uint8_t* wlds) {
     // I is a multiple of 64, so a wave's 64 columns are all gate or all up
     const int col0 = t.n0 + wn * C::WTN;
-    const bool up = col0 >= p.I;
+    // (ungated: every column is an up column, and columns past I are not stored)
+    const bool gated = act_gated(p.act);
+    const bool up = !gated || col0 >= p.I;
     uint16_t* out = (up ? p.dWu : p.dWg) + (size_t)t.e * p.H * p.I;
-    wg_store<C>(wlds, out, p.I, t.m0 + wm * C::WTM, p.H, up ? col0 - p.I : col0, p.I, acc, lane);
+    wg_store<C>(wlds, out, p.I, t.m0 + wm * C::WTM, p.H, gated && up ? col0 - p.I : col0, p.I, acc, lane);
   }
 };
 
@@ -380,7 +383,8 @@ hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dw_gateup, dim3(wgrad_grid<CfgWgGateUp>(a, a.H, 2 * a.I)), dim3(CfgWgGateUp::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_dw_gateup, dim3(wgrad_grid<CfgWgGateUp>(a, a.H, act_gated(a.act) ? 2 * a.I : a.I)),
+                     dim3(CfgWgGateUp::NT), 0, s, a);
   return hipGetLastError();
 }
 

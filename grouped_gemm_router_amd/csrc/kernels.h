@@ -67,7 +67,8 @@ hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_gather(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s);
-int bwd_nparts(int I);
+// router-weight partial sums per row of the recompute (its column tiles times waves across)
+int bwd_nparts(int I, int act);
 hipError_t launch_bwd_token_reduce(const GemmArgs& a, const int32_t* slot_row, uint16_t* dX,
                                    float* d_topk_w, hipStream_t s);
 

@@ -58,6 +58,17 @@ struct MxSrcGateUpW {
     return (up ? p.Su : p.Sg) + ((size_t)t.e * p.I + col(p, t, row)) * (p.H / 32);
   }
 };
+struct MxSrcUpW {      // packed up codes [E, I, H]: the B rows of the ungated (ReLU^2) up GEMM
+  __device__ static const uint16_t* base(const MxArgs& p, const Tile& t, int, int k0) {
+    return reinterpret_cast<const uint16_t*>(p.Wu) + (size_t)t.e * p.I * (p.H / 2) + k0;
+  }
+  __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.I - 1) * (uint32_t)(p.H / 2);
+  }
+  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
+    return p.Su + ((size_t)t.e * p.I + min(t.n0 + row, p.I - 1)) * (p.H / 32);
+  }
+};
 struct MxSrcH {        // expert-major quantised h rows
   __device__ static const uint16_t* base(const MxArgs& p, const Tile&, int, int k0) {
     return reinterpret_cast<const uint16_t*>(p.Hq) + k0;
@@ -260,6 +271,17 @@ struct MxSwiGLUEpi {  // h = bf16(f(G, U)) -> Hrows (columns as in the bf16 gate
 };
 
 template <class C>
+struct MxRelu2Epi {  // h = bf16(max(U, 0)^2) -> Hrows (the ungated expert)
+  __device__ static void apply(const MxArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
+                               int lane, uint8_t* wlds) {
+    stage_store_bf16<C, C::WTN, 4>(
+        wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.I, lane,
+        [&](int fm, int fn, int q, int j) { return relu2(acc[fm][fn][4 * q + j]); },
+        [](int fn, int q) { return fn * 32 + q * 8; });
+  }
+};
+
+template <class C>
 struct MxStoreOEpi {  // O = bf16(acc) -> Orows
   __device__ static void apply(const MxArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
                                int lane, uint8_t* wlds) {
@@ -277,6 +299,10 @@ __global__ void __launch_bounds__(CfgMx::NT) k_mx_gateup(const MxArgs p) {
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_gateup_act(const MxArgs p) {
   mx_rows_body<CfgMx, MxSrcX, MxSrcGateUpW<CfgMx>, MxSwiGLUEpi<CfgMx, ACT_ANY>>(p, 2 * p.I, p.H);
 }
+// the ungated ReLU^2 expert (W_up only)
+__global__ void __launch_bounds__(CfgMx::NT) k_mx_up(const MxArgs p) {
+  mx_rows_body<CfgMx, MxSrcX, MxSrcUpW, MxRelu2Epi<CfgMx>>(p, p.I, p.H);
+}
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_down(const MxArgs p) {
   mx_rows_body<CfgMx, MxSrcH, MxSrcDownW, MxStoreOEpi<CfgMx>>(p, p.H, p.I);
 }
@@ -291,6 +317,10 @@ static int mx_grid(const MxArgs& a, int N) {
 }
 
 hipError_t launch_mx_gateup(const MxArgs& a, hipStream_t s) {
+  if (a.act == ACT_RELU2) {
+    hipLaunchKernelGGL(k_mx_up, dim3(mx_grid(a, a.I)), dim3(CfgMx::NT), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_mx_gateup : k_mx_gateup_act, dim3(mx_grid(a, 2 * a.I)), dim3(CfgMx::NT),
                      0, s, a);
   return hipGetLastError();

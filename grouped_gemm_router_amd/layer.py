@@ -17,8 +17,9 @@ from . import binding as B
 class MoELayer:
     def __init__(self, H: int, I: int, E: int, k: int, dtype: str = "bf16", device="cuda",
                  activation: str = "swiglu", act_limit: float = 0.0):
-        """``activation``: swiglu (default), swiglu_clamp, swiglu_oai, geglu or reglu (include/moe.h,
-        moe_activation); ``act_limit``: the clamp of the two clamped ones."""
+        """``activation``: swiglu (default), swiglu_clamp, swiglu_oai, geglu, reglu or relu2
+        (include/moe.h, moe_activation; relu2 experts have no gate weight); ``act_limit``: the
+        clamp of the two clamped ones."""
         self.H, self.I, self.E, self.k, self.dtype = H, I, E, k, dtype
         self.activation, self.act_limit = activation, act_limit
         self.device = torch.device(device)
@@ -26,16 +27,19 @@ class MoELayer:
         self._plans = {}
 
     # -- weights (once, outside any timed region) ---------------------------------
-    def load_weights(self, W_gate: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor, keep_math=True):
-        """W_gate, W_up [E, H, I] and W_down [E, I, H] bf16 on the device."""
-        self.Wg_t = B.pack_weights(W_gate)
+    def load_weights(self, W_gate, W_up: torch.Tensor, W_down: torch.Tensor, keep_math=True):
+        """W_gate, W_up [E, H, I] and W_down [E, I, H] bf16 on the device (W_gate None for the
+        two-weight ReLU^2 expert)."""
+        if (W_gate is None) != (self.activation in B.UNGATED):
+            raise ValueError("ReLU^2 experts take no gate weight; every other activation needs one")
+        self.Wg_t = B.pack_weights(W_gate) if W_gate is not None else None
         self.Wu_t = B.pack_weights(W_up)
         self.Wd_t = B.pack_weights(W_down)
         if keep_math:
             self.W_gate, self.W_up, self.W_down = W_gate, W_up, W_down
         self.scales = None
         if self.dtype == "mxfp8":
-            qg, sg = B.mx_quantize(self.Wg_t)
+            qg, sg = B.mx_quantize(self.Wg_t) if self.Wg_t is not None else (None, None)
             qu, su = B.mx_quantize(self.Wu_t)
             qd, sd = B.mx_quantize(self.Wd_t)
             self.Wg_t, self.Wu_t, self.Wd_t = qg, qu, qd
@@ -66,7 +70,8 @@ class MoELayer:
         if backward:
             pl["ws_bwd"] = torch.empty(B.workspace_size(p, B.CALL_BACKWARD), dtype=torch.uint8, device=dev)
             pl["grads"] = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
-                           torch.empty(E, H, I, dtype=torch.bfloat16, device=dev),
+                           torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
+                           if self.activation not in B.UNGATED else None,
                            torch.empty(E, H, I, dtype=torch.bfloat16, device=dev),
                            torch.empty(E, I, H, dtype=torch.bfloat16, device=dev),
                            torch.empty(T, k, dtype=torch.float32, device=dev))
@@ -95,7 +100,7 @@ class MoELayer:
 
     def backward(self, X: torch.Tensor, dY: torch.Tensor):
         """Gradients of the last forward with the same X (needs backward_plan=True)."""
-        if self.dtype != "bf16" or self.W_gate is None:
+        if self.dtype != "bf16" or self.W_up is None:
             raise ValueError("backward needs bf16 weights kept in the math layout")
         T = X.shape[0]
         pl = self.plan(T, True)

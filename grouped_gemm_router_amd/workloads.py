@@ -57,6 +57,16 @@ class MoEConfig:
         """Routed rows (token-expert assignments), T*k."""
         return self.T * self.k
 
+    @property
+    def gated(self) -> bool:
+        """Whether the experts have a gate weight (every activation but relu2)."""
+        return self.activation != "relu2"
+
+    @property
+    def mats(self) -> tuple:
+        """Names of the expert weight matrices."""
+        return ("gate", "up", "down") if self.gated else ("up", "down")
+
 
 CONFIGS = {
     "tiny": MoEConfig("tiny", 64, 256, 128, 8, 2, "bf16", "normal", 0),
@@ -74,6 +84,9 @@ CONFIGS = {
     "h6144_i2048_e256_k8": MoEConfig("h6144_i2048_e256_k8", 4096, 6144, 2048, 256, 8, "bf16", "normal", 6),
     "h6144_i3072_e128_k4_oai": MoEConfig("h6144_i3072_e128_k4_oai", 4096, 6144, 3072, 128, 4, "bf16",
                                          "normal", 7, activation="swiglu_oai", act_limit=7.0),
+    # the two-weight ReLU^2 expert shape of the same table
+    "h2688_i1856_e128_k6_relu2": MoEConfig("h2688_i1856_e128_k6_relu2", 4096, 2688, 1856, 128, 6, "bf16",
+                                           "normal", 8, activation="relu2"),
 }
 
 

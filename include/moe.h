@@ -64,17 +64,21 @@ typedef enum {
 } moe_dtype;
 
 /*
- * Gated activation h = f(G, U) of the expert MLP (G = x W_gate, U = x W_up).
- * LightMoE "Highlights" names SwiGLU-OAI, bounded SwiGLU, GeGLU and ReGLU
- * epilogues and "MoE inference" an activation clamp of 10; the formulas are
- * the public definitions of the model families that use them:
+ * Activation h = f(G, U) of the expert MLP (G = x W_gate, U = x W_up).
+ * LightMoE "Highlights" names SwiGLU-OAI, bounded SwiGLU, GeGLU, ReGLU and
+ * ReLU^2 epilogues and "MoE inference" an activation clamp of 10 and ReLU^2
+ * experts that load only an up and a down weight; the formulas are the public
+ * definitions of the model families that use them.  ReLU^2 is ungated: the
+ * expert has no W_gate, every gate pointer of a call may be NULL and is not
+ * read, and dW_gate is not written.
  */
 typedef enum {
   MOE_ACT_SWIGLU = 0,       /* silu(G) * U (the default) */
   MOE_ACT_SWIGLU_CLAMP = 1, /* silu(min(G, c)) * clamp(U, -c, c), c = act_limit (bounded SwiGLU) */
   MOE_ACT_SWIGLU_OAI = 2,   /* g * sigmoid(1.702 g) * (u + 1), g = min(G, c), u = clamp(U, -c, c) */
   MOE_ACT_GEGLU = 3,        /* gelu(G) * U, gelu(x) = x * Phi(x), Phi the normal CDF (erf form) */
-  MOE_ACT_REGLU = 4         /* max(G, 0) * U */
+  MOE_ACT_REGLU = 4,        /* max(G, 0) * U */
+  MOE_ACT_RELU2 = 5         /* max(U, 0)^2 (no gate) */
 } moe_activation;
 
 /* Problem shape.  T tokens, hidden size H, expert intermediate size I,
@@ -185,14 +189,14 @@ MOE_API moe_status moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8
  * Expert MLP over the expert-major rows (LightMoE "MoE inference": gate/up
  * projection, gated activation, requantisation, down projection):
  *   G = X[row_token[r]] W_gate[e], U = X[row_token[r]] W_up[e]   (fp32 accumulation)
- *   h[r] = bf16(silu(G) * U),  O[r] = bf16(h[r] W_down[e])
+ *   h[r] = bf16(f(G, U)) (f = p->activation, silu(G) * U by default),  O[r] = bf16(h[r] W_down[e])
  * for every row r of every expert e with rows.  Experts without rows are
  * never read.
  *   p              problem (dtype selects bf16 or MXFP8 operands)
  *   X              [T, H] bf16
  *   row_token, expert_offsets   from moe_dispatch
  *   bf16:  Wg_t, Wu_t [E, I, H] bf16 and Wd_t [E, H, I] bf16 (moe_pack_weights);
- *          Sg, Su, Sd must be NULL
+ *          Sg, Su, Sd must be NULL.  For MOE_ACT_RELU2, Wg_t (and Sg) may be NULL
  *   MXFP8: Wg_t, Wu_t [E, I, H] and Wd_t [E, H, I] E4M3 codes with
  *          Sg, Su [E, I, H/32] and Sd [E, H, I/32] E8M0 scales (moe_mx_quantize
  *          of the packed bf16 weights); X is quantised here, and h is
@@ -226,7 +230,8 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
  * Per row r (token t, slot s, expert e, weight w = topk_w[s]):
  *   G, U, h recomputed as in moe_expert_mlp;  P = dY[t] W_down[e]^T (fp32)
  *   d_topk_w[s] = <h, P>;  dh = w P
- *   du = dh * silu(G),  dg = dh * U * silu'(G),  dO = bf16(w dY[t])
+ *   du = dh * df/dU,  dg = dh * df/dG  (SwiGLU: du = dh * silu(G), dg = dh * U * silu'(G)),
+ *   dO = bf16(w dY[t])
  *   dX[t]      = bf16( sum_j (dg W_gate[e]^T + du W_up[e]^T) ), j ascending
  *   dW_gate[e] = bf16( sum_r X[t]^T dg ),  dW_up[e] = bf16( sum_r X[t]^T du )
  *   dW_down[e] = bf16( sum_r h^T dO )      (all sums in fp32, fixed order;
@@ -237,6 +242,8 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
  *   dX [T, H], dW_gate, dW_up [E, H, I], dW_down [E, I, H] bf16 out;
  *   d_topk_w [T, k] fp32 out
  *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_BACKWARD)
+ * MOE_ACT_RELU2 has no gate: du = dh * 2 max(U, 0), dX sums du W_up[e]^T only,
+ * W_gate, Wg_t and dW_gate may be NULL and dW_gate is not written.
  */
 MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY,
                                 const float* topk_w, const int32_t* row_token,

@@ -84,7 +84,8 @@ def backward_h_ambiguity(cfg, X, dY, idx, w, fn, act="swiglu", limit=None, exper
         if hi == lo:
             continue
         tok, sl = row_token[lo:hi], row_slot[lo:hi]
-        wg, wu, wd = (orc.bf16_decode(fn(n)(e)) for n in ("gate", "up", "down"))
+        wg = orc.bf16_decode(fn("gate")(e)) if orc.is_gated(act) else None
+        wu, wd = (orc.bf16_decode(fn(n)(e)) for n in ("up", "down"))
         dh = orc.h_ambiguity_rows(Xv[tok], wg, wu, act, limit)
         _, _, h, _ = orc.expert_forward_rows(Xv[tok], wg, wu, wd, act=act, limit=limit)
         dO_exact = w.reshape(-1)[sl][:, None] * dYv[tok]

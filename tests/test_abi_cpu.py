@@ -69,15 +69,38 @@ def test_validate_problem(args, expect):
 def test_validate_problem_activation():
     from grouped_gemm_router_amd import binding as B
     assert B.validate_problem(B.problem(64, 256, 128, 8, 2)) == 0
-    for act in ("swiglu", "geglu", "reglu"):
+    for act in ("swiglu", "geglu", "reglu", "relu2"):
         assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act)) == 0
     for act in ("swiglu_clamp", "swiglu_oai"):
         assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act, act_limit=7.0)) == 0
         assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act, act_limit=0.0)) == 1
         assert B.validate_problem(B.problem(64, 256, 128, 8, 2, activation=act, act_limit=float("nan"))) == 1
     p = B.problem(64, 256, 128, 8, 2)
-    p.activation = 5
+    p.activation = 6
     assert B.validate_problem(p) == 1
+    p.activation = -1
+    assert B.validate_problem(p) == 1
+
+
+def test_gate_pointers_optional_only_for_relu2():
+    """The two-weight ReLU^2 expert takes NULL gate pointers; every gated activation needs them
+    (argument errors, 1, come before the workspace check, 3, and the device check)."""
+    import ctypes
+    from grouped_gemm_router_amd import binding as B
+    lib = B.lib
+    v = ctypes.c_void_p(16)
+    for act, expect in (("swiglu", 1), ("reglu", 1), ("relu2", 3)):
+        p = B.problem(64, 256, 128, 8, 2, activation=act)
+        # decode-sized problem (T <= 64): the missing workspace is reported once the pointers pass
+        assert lib.moe_expert_mlp(ctypes.byref(p), v, v, v, None, v, v, None, None, None, v, v, None, 0,
+                                  None) == expect, act
+        ptrs = [v] * 17
+        ptrs[7] = ptrs[10] = ptrs[13] = None          # W_gate, Wg_t, dW_gate
+        assert lib.moe_backward(ctypes.byref(p), *ptrs, None, 0, None) == expect, act
+    pm = B.problem(64, 256, 128, 8, 2, "mxfp8", activation="relu2")
+    assert lib.moe_expert_mlp(ctypes.byref(pm), v, v, v, None, v, v, None, v, v, v, v, None, 0, None) == 3
+    pm = B.problem(64, 256, 128, 8, 2, "mxfp8")
+    assert lib.moe_expert_mlp(ctypes.byref(pm), v, v, v, v, v, v, None, v, v, v, v, None, 0, None) == 1
 
 
 def test_workspace_sizes():

@@ -16,7 +16,7 @@ from gpu_helpers import check_close, device_weights, host_weight_fn, to_dev, to_
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = ["h4096_i2048_e256_k6_clamp", "h6144_i2048_e256_k8", "h6144_i3072_e128_k4_oai"]
+SHAPES = ["h4096_i2048_e256_k6_clamp", "h6144_i2048_e256_k8", "h6144_i3072_e128_k4_oai", "h2688_i1856_e128_k6_relu2"]
 
 
 def _say(*a):
@@ -35,9 +35,9 @@ def test_forward_model_shape_sampled(name):
     tokens[0], tokens[-1] = 0, cfg.T - 1
     drawn = np.unique(idx[tokens])
     _say(name, "experts with weights", len(drawn))
-    W = {n: device_weights(cfg, n, experts=drawn) for n in ("gate", "up", "down")}
+    W = {n: device_weights(cfg, n, experts=drawn) for n in cfg.mats}
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=act,
-                     act_limit=cfg.act_limit).load_weights(W["gate"], W["up"], W["down"], keep_math=False)
+                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"], keep_math=False)
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X))
     torch.cuda.synchronize()
     pl = layer.plan(cfg.T)
@@ -46,7 +46,7 @@ def test_forward_model_shape_sampled(name):
     for g, r in zip((pl["offsets"], pl["row_token"], pl["row_slot"], pl["slot_row"]),
                     (off, row_token, row_slot, slot_row)):
         assert np.array_equal(g.cpu().numpy(), r)
-    fn = lambda n: host_weight_fn(cfg, n)
+    fn = lambda n: host_weight_fn(cfg, n) if n in cfg.mats else None
     Yref = orc.layer_forward_tokens(X, idx, w, fn("gate"), fn("up"), fn("down"), tokens, act=act, limit=limit)
     check_close(to_f64(pl["Y"][torch.from_numpy(tokens).cuda()]), Yref, f"{name} Y[sampled tokens]")
     # h and O rows: the sampled tokens' rows plus each drawn expert's first and last row
@@ -60,7 +60,8 @@ def test_forward_model_shape_sampled(name):
     Xv = orc.bf16_decode(X)
     for e in np.unique(owner):
         sel = np.nonzero(owner == e)[0]
-        _, _, h, O = orc.expert_forward_rows(Xv[row_token[rows[sel]]], orc.bf16_decode(fn("gate")(e)),
+        wg = orc.bf16_decode(fn("gate")(e)) if cfg.gated else None
+        _, _, h, O = orc.expert_forward_rows(Xv[row_token[rows[sel]]], wg,
                                              orc.bf16_decode(fn("up")(e)), orc.bf16_decode(fn("down")(e)),
                                              act=act, limit=limit)
         check_close(Hg[sel], h, f"{name} h[rows of expert {e}]")

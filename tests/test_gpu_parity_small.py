@@ -252,20 +252,25 @@ def remainder_logits(counts, E, seed):
     return np.ascontiguousarray(logits)
 
 
-def test_forward_backward_every_row_class():
-    _say("row classes", REMAINDER_COUNTS)
+@pytest.mark.parametrize("act", ["swiglu", "relu2"])
+def test_forward_backward_every_row_class(act):
+    _say("row classes", act, REMAINDER_COUNTS)
     from grouped_gemm_router_amd.layer import MoELayer
     E = len(REMAINDER_COUNTS)
     logits = remainder_logits(REMAINDER_COUNTS, E, 61)
     cfg = wl.config("tiny", name="row_classes", T=logits.shape[0], H=192, I=128, E=E, k=1, seed=61, backward=True)
+    gated = orc.is_gated(act)
     X, dY = wl.make_x(cfg), wl.make_dy(cfg)
-    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
-    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k).load_weights(W["gate"], W["up"], W["down"])
+    W = {n: device_weights(cfg, n) for n in (("gate", "up", "down") if gated else ("up", "down"))}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, activation=act).load_weights(W.get("gate"), W["up"], W["down"])
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=True)
     pl = layer.plan(cfg.T, True)
     torch.cuda.synchronize()
     fn = lambda n: host_weight_fn(cfg, n)
-    idx, w, off, h, O, Y, _, _ = _oracle_forward(cfg, logits, X, fn)
+    idx, w = orc.route(logits, cfg.k)
+    off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
+    h, O = orc.expert_mlp(X, row_token, off, fn("gate") if gated else None, fn("up"), fn("down"), act=act)
+    Y = orc.combine(O, slot_row, w)
     assert np.array_equal(np.diff(off), REMAINDER_COUNTS)
     assert np.array_equal(pl["offsets"].cpu().numpy(), off)
     check_close(to_f64(pl["H_rows"]), h, "h")
@@ -273,19 +278,19 @@ def test_forward_backward_every_row_class():
     check_close(to_f64(pl["Y"]), Y, "Y")
     dX, dWg, dWu, dWd, dtw = layer.backward(to_dev(X), to_dev(dY))
     torch.cuda.synchronize()
-    ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), E=cfg.E)
-    amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn)
+    ref = orc.backward(X, dY, idx, w, fn("gate") if gated else None, fn("up"), fn("down"), E=cfg.E, act=act)
+    amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn, act)
     check_close(to_f64(dX), ref["dX"], "dX")
     check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w", ambiguity=amb_dtw)
-    g = {"dWg": to_f64(dWg), "dWu": to_f64(dWu), "dWd": to_f64(dWd)}
-    for key in ("dWg", "dWu", "dWd"):
+    g = {"dWg": to_f64(dWg) if gated else None, "dWu": to_f64(dWu), "dWd": to_f64(dWd)}
+    for key in (("dWg", "dWu", "dWd") if gated else ("dWu", "dWd")):
         for e in range(cfg.E):
             check_close(g[key][e], ref["dW"][key][e], f"{key}[{e}] ({REMAINDER_COUNTS[e]} rows)",
                         ambiguity=amb_dwd.get(e) if key == "dWd" else None)
 
 
 ACTS = [("swiglu", 0.0), ("swiglu_clamp", 1.0), ("swiglu_oai", 1.0), ("swiglu_oai", 7.0), ("geglu", 0.0),
-        ("reglu", 0.0)]
+        ("reglu", 0.0), ("relu2", 0.0)]
 ACT_CFGS = [wl.config("tiny", name="act_rows", T=300, H=320, I=192, E=5, k=3, seed=51),
             wl.config("tiny", name="act_decode", T=24, H=256, I=128, E=16, k=4, seed=52),
             wl.config("tiny", name="act_mx", T=96, H=256, I=128, E=6, k=2, dtype="mxfp8", seed=53)]
@@ -294,14 +299,16 @@ ACT_CFGS = [wl.config("tiny", name="act_rows", T=300, H=320, I=192, E=5, k=3, se
 @pytest.mark.parametrize("act,limit", ACTS, ids=[f"{a}{l:g}" for a, l in ACTS])
 @pytest.mark.parametrize("cfg", ACT_CFGS, ids=[c.name for c in ACT_CFGS])
 def test_forward_activations_vs_oracle(cfg, act, limit):
-    """Every gated activation on the three forward paths (row tiles with a remainder,
-    small-token weight streaming, MXFP8); clamp 1.0 makes the clamps bind often."""
+    """Every activation on the three forward paths (row tiles with a remainder,
+    small-token weight streaming, MXFP8); clamp 1.0 makes the clamps bind often.  The
+    ungated ReLU^2 expert gets no gate weight at all."""
     from grouped_gemm_router_amd.layer import MoELayer
     _say("forward", act, limit, cfg)
+    gated = orc.is_gated(act)
     logits, X = wl.make_logits(cfg), wl.make_x(cfg)
-    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    W = {n: device_weights(cfg, n) for n in (("gate", "up", "down") if gated else ("up", "down"))}
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=act, act_limit=limit).load_weights(
-        W["gate"], W["up"], W["down"])
+        W.get("gate"), W["up"], W["down"])
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X))
     torch.cuda.synchronize()
     pl = layer.plan(cfg.T)
@@ -310,7 +317,8 @@ def test_forward_activations_vs_oracle(cfg, act, limit):
     off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
     mx = cfg.dtype == "mxfp8"
     lim = limit or None
-    h, O = orc.expert_mlp(X, row_token, off, fn("gate"), fn("up"), fn("down"), mxfp8=mx, act=act, limit=lim)
+    h, O = orc.expert_mlp(X, row_token, off, fn("gate") if gated else None, fn("up"), fn("down"), mxfp8=mx, act=act,
+                          limit=lim)
     amb_O = None
     if mx:
         Xv = orc.bf16_decode(X)
@@ -318,7 +326,8 @@ def test_forward_activations_vs_oracle(cfg, act, limit):
         for e in range(cfg.E):
             lo, hi = off[e], off[e + 1]
             if hi > lo:
-                wg, wu, wd = (orc.bf16_decode(fn(n)(e)) for n in ("gate", "up", "down"))
+                wg = orc.bf16_decode(fn("gate")(e)) if gated else None
+                wu, wd = (orc.bf16_decode(fn(n)(e)) for n in ("up", "down"))
                 G, U, _, _ = orc.expert_forward_rows(Xv[row_token[lo:hi]], wg, wu, wd, mxfp8=True, act=act,
                                                      limit=lim)
                 amb_O[lo:hi] = orc.mx_down_ambiguity(G, U, wd, act=act, limit=lim)
@@ -331,20 +340,26 @@ def test_backward_activations_vs_oracle(act, limit):
     from grouped_gemm_router_amd.layer import MoELayer
     cfg = wl.config("tiny", name="act_bwd", T=300, H=320, I=192, E=5, k=3, seed=54, backward=True)
     _say("backward", act, limit, cfg)
+    gated = orc.is_gated(act)
     logits, X, dY = wl.make_logits(cfg), wl.make_x(cfg), wl.make_dy(cfg)
-    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    W = {n: device_weights(cfg, n) for n in (("gate", "up", "down") if gated else ("up", "down"))}
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, activation=act, act_limit=limit).load_weights(
-        W["gate"], W["up"], W["down"])
+        W.get("gate"), W["up"], W["down"])
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=True)
     dX, dWg, dWu, dWd, dtw = layer.backward(to_dev(X), to_dev(dY))
     torch.cuda.synchronize()
     idx, w = orc.route(logits, cfg.k)
     fn = lambda n: host_weight_fn(cfg, n)
-    ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), E=cfg.E, act=act, limit=limit or None)
+    ref = orc.backward(X, dY, idx, w, fn("gate") if gated else None, fn("up"), fn("down"), E=cfg.E, act=act,
+                       limit=limit or None)
     amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn, act, limit or None)
     check_close(to_f64(dX), ref["dX"], f"{act} dX")
     check_close(dtw.cpu().numpy(), ref["d_topk_w"], f"{act} d_topk_w", ambiguity=amb_dtw)
+    if not gated:
+        assert dWg is None
     for key, t in (("dWg", dWg), ("dWu", dWu), ("dWd", dWd)):
+        if t is None:
+            continue
         g = to_f64(t)
         for e in range(cfg.E):
             check_close(g[e], ref["dW"][key][e], f"{act} {key}[{e}]",
