@@ -107,6 +107,8 @@ def cpu_baseline(cfg, logits, X, dY, min_s=10.0, max_reps=20):
     cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     ntok = {"prefill": cfg.T, "decode": cfg.T, "tiny": cfg.T, "prefill_rankzipf": 1024,
             "large_mxfp8": 128, "train": 16}.get(cfg.name, 64)
+    if cfg.H * cfg.I >= 4096 * 2048:
+        ntok = 2          # the large expert shapes: each sampled expert's weights take seconds to draw
     ntok = min(ntok, cfg.T)
     toks = np.sort(np.random.default_rng(0).choice(cfg.T, ntok, replace=False))
     idx, w = orc.route(logits, cfg.k)
