@@ -19,6 +19,7 @@ CASES = [
     wl.config("tiny", name="graph_rows", T=300, H=320, I=192, E=5, k=3, seed=41, backward=True),
     wl.config("tiny", name="graph_decode", T=24, H=256, I=128, E=64, k=4, seed=42),
     wl.config("tiny", name="graph_mx", T=96, H=256, I=128, E=6, k=2, dtype="mxfp8", seed=43),
+    wl.config("tiny", name="graph_relu2", T=300, H=320, I=192, E=5, k=3, seed=44, backward=True, activation="relu2"),
 ]
 
 
@@ -30,9 +31,9 @@ def _say(*a):
 def test_graph_replays_match_eager(cfg):
     from grouped_gemm_router_amd.layer import MoELayer
     _say("graph", cfg)
-    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
-    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(W["gate"], W["up"], W["down"],
-                                                                         keep_math=cfg.backward)
+    W = {n: device_weights(cfg, n) for n in cfg.mats}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation).load_weights(
+        W.get("gate"), W["up"], W["down"], keep_math=cfg.backward)
     logits = torch.from_numpy(wl.make_logits(cfg)).cuda()
     X = to_dev(wl.make_x(cfg))
     dY = to_dev(wl.make_dy(cfg)) if cfg.backward else None
@@ -49,7 +50,7 @@ def test_graph_replays_match_eager(cfg):
 
     def snapshot(outs):
         return [to_bits(t).copy() if t.dtype == torch.bfloat16 else t.cpu().numpy().view(np.int32).copy()
-                for t in outs]
+                for t in outs if t is not None]
 
     eager = snapshot(step(logits, X))
     torch.cuda.synchronize()
