@@ -125,9 +125,9 @@ MOE_API moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t 
                              float* topk_w, void* stream) {
   moe_status s = check_route_args(T, E, k);
   if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;                            // empty batch: nothing to read or write
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if ((s = device_ok()) != MOE_OK) return s;
-  if (T == 0) return MOE_OK;
   return from_hip(moe::launch_route(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
 }
 
@@ -135,9 +135,9 @@ MOE_API moe_status moe_route_backward(const int32_t* topk_idx, const float* topk
                                       int32_t T, int32_t E, int32_t k, float* d_logits, void* stream) {
   moe_status s = check_route_args(T, E, k);
   if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;                            // empty batch: nothing to read or write
   if (!topk_idx || !topk_w || !d_topk_w || !d_logits) return MOE_ERR_INVALID_ARG;
   if ((s = device_ok()) != MOE_OK) return s;
-  if (T == 0) return MOE_OK;
   return from_hip(moe::launch_route_backward(topk_idx, topk_w, d_topk_w, T, E, k, d_logits, (hipStream_t)stream));
 }
 
@@ -181,11 +181,13 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
   const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
-  if (!X || !expert_offsets || (gated && !Wg_t) || !Wu_t || !Wd_t || !H_rows || !O_rows) return MOE_ERR_INVALID_ARG;
-  if (p->T > 0 && !row_token) return MOE_ERR_INVALID_ARG;
+  const bool rows = p->T > 0;                            // token-sized arrays may be NULL for T = 0
+  if (!expert_offsets || (gated && !Wg_t) || !Wu_t || !Wd_t) return MOE_ERR_INVALID_ARG;
+  if (rows && (!X || !row_token || !H_rows || !O_rows)) return MOE_ERR_INVALID_ARG;
   const bool mx = p->dtype == MOE_DTYPE_MXFP8;
   if (mx != ((Sg || !gated) && Su && Sd)) return MOE_ERR_INVALID_ARG;
   if (!mx && (Sg || Su || Sd)) return MOE_ERR_INVALID_ARG;
+  if (!rows) return MOE_OK;                              // empty batch: nothing to compute
   const size_t need = mlp_ws(p);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if ((s = device_ok()) != MOE_OK) return s;
@@ -257,12 +259,14 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   if (s != MOE_OK) return s;
   if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
   const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
-  if (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !expert_offsets || (gated && !W_gate) ||
-      !W_up || !W_down || (gated && !Wg_t) || !Wu_t || !dX || (gated && !dW_gate) || !dW_up || !dW_down ||
-      !d_topk_w)
+  const bool rows = p->T > 0;                            // token-sized arrays may be NULL for T = 0
+  if (!expert_offsets || (gated && !W_gate) || !W_up || !W_down || (gated && !Wg_t) || !Wu_t ||
+      (gated && !dW_gate) || !dW_up || !dW_down)
+    return MOE_ERR_INVALID_ARG;
+  if (rows && (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !dX || !d_topk_w))
     return MOE_ERR_INVALID_ARG;
   const size_t need = bwd_ws(p);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if ((s = device_ok()) != MOE_OK) return s;
   const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
   uint8_t* w8 = (uint8_t*)ws;

@@ -9,7 +9,7 @@
  *
  *   moe_route       softmax over E logits -> top-k -> renormalise
  *   moe_dispatch    expert-major order of the T*k token-expert assignments
- *   moe_expert_mlp  grouped GEMM gate/up + SwiGLU, grouped GEMM down
+ *   moe_expert_mlp  grouped GEMM gate/up + activation, grouped GEMM down
  *   moe_combine     weighted sum of each token's k expert rows
  *   moe_backward    dX, dW_gate, dW_up, dW_down, d(top-k weights)
  *   moe_route_backward  d(router logits) from d(top-k weights)
@@ -29,6 +29,10 @@
  *   MOE_ERR_HIP.  No C++ exception crosses this interface.
  * - Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31; H and I multiples
  *   of 64 (MXFP8: multiples of 128).
+ * - An empty batch (T = 0) is valid: every token-sized array (logits, X, dY,
+ *   the routing and dispatch arrays, the row buffers, Y, dX, the top-k
+ *   gradients) may then be NULL.  moe_dispatch still writes expert_offsets
+ *   (all zero) and moe_backward still writes the weight gradients (zeros).
  * - Results are deterministic: the same inputs give bitwise-identical outputs
  *   (no floating-point atomics, fixed reduction orders).
  */

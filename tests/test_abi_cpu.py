@@ -144,3 +144,29 @@ def test_calls_reject_bad_arguments_before_touching_the_device():
     assert lib.moe_route_backward(None, v, v, 4, 8, 2, v, None) == 1
     assert lib.moe_route_backward(v, v, v, 4, 8, 9, v, None) == 1
     assert lib.moe_route_backward(v, v, v, 4, 2048, 2, v, None) == 2
+
+
+def test_empty_batch_accepts_null_token_arrays():
+    """T = 0 is a valid problem: token-sized pointers may be NULL.  Calls that compute nothing
+    return MOE_OK without touching the device; the others get past the argument checks and
+    stop at the device check (no GPU here) or run (on a GPU)."""
+    import ctypes
+    from grouped_gemm_router_amd import binding as B
+    lib = B.lib
+    v = ctypes.c_void_p(16)
+    assert lib.moe_route(None, 0, 8, 2, None, None, None) == 0
+    assert lib.moe_route_backward(None, None, None, 0, 8, 2, None, None) == 0
+    assert lib.moe_combine(None, None, None, 0, 2, 64, None, None) == 0
+    p = B.problem(0, 256, 128, 8, 2)
+    assert lib.moe_expert_mlp(ctypes.byref(p), None, None, v, v, v, v, None, None, None, None, None, None, 0,
+                              None) == 0
+    ptrs = [None] * 17
+    ptrs[6] = v                                     # expert_offsets
+    ptrs[7] = ptrs[8] = ptrs[9] = ptrs[10] = ptrs[11] = v            # weights
+    ptrs[13] = ptrs[14] = ptrs[15] = v                               # dW_gate, dW_up, dW_down
+    assert lib.moe_backward(ctypes.byref(p), *ptrs, None, 0, None) not in (1, 3)
+    # the weights and the expert offsets are still required
+    ptrs[8] = None
+    assert lib.moe_backward(ctypes.byref(p), *ptrs, None, 0, None) == 1
+    assert lib.moe_expert_mlp(ctypes.byref(p), None, None, None, v, v, v, None, None, None, None, None, None, 0,
+                              None) == 1

@@ -366,6 +366,29 @@ def test_backward_activations_vs_oracle(act, limit):
                         ambiguity=amb_dwd.get(e) if key == "dWd" else None)
 
 
+def test_empty_batch_forward_backward():
+    """T = 0: every call accepts the empty arrays, the forward produces nothing and the backward
+    writes exact zeros to every weight gradient."""
+    _say("empty batch")
+    from grouped_gemm_router_amd.layer import MoELayer
+    cfg = wl.config("tiny", name="empty", T=0, seed=71, backward=True)
+    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k).load_weights(W["gate"], W["up"], W["down"])
+    logits = torch.zeros(0, cfg.E, dtype=torch.float32, device="cuda")
+    X = torch.zeros(0, cfg.H, dtype=torch.bfloat16, device="cuda")
+    grads = layer.plan(0, True)["grads"]
+    for g in grads[1:4]:
+        g.fill_(1.0)                                     # must be overwritten with zeros
+    Y = layer.forward(logits, X, backward_plan=True)
+    dX, dWg, dWu, dWd, dtw = layer.backward(X, X)
+    dlog = layer.route_backward(0)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, cfg.H) and dX.shape == (0, cfg.H) and dtw.shape == (0, cfg.k) and dlog.shape == (0, cfg.E)
+    assert np.array_equal(layer.plan(0, True)["offsets"].cpu().numpy(), np.zeros(cfg.E + 1, np.int32))
+    for g in (dWg, dWu, dWd):
+        assert not torch.any(g.view(torch.int16) != 0)   # +0.0 bit patterns
+
+
 def test_forward_deterministic_and_unused_experts_unread():
     _say("determinism + NaN poisoning")
     cfg = wl.config("tiny", name="poison", T=48, H=256, I=128, E=256, k=2, seed=21)
