@@ -532,40 +532,72 @@ hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 // dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials.
+// One wave per (token, slice of 64 chunks of 8 fp32): the token's row indices are
+// wave-uniform, each lane issues the loads of four rows before it adds them (ascending j),
+// and the fp32 rows, read once, are loaded with the nontemporal hint.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4v load_nt_f32x4(const float* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(ptr));
+}
+__device__ __forceinline__ void add8(float (&acc)[8], const f32x4v& a, const f32x4v& b) {
+  acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+  acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+}
+
 __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, const int32_t* slot_row,
                                                           uint16_t* dX, float* dtw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunks = p.H / 8;
-  const long total = (long)p.T * chunks;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
-    int t = (int)(i / chunks), c = (int)(i % chunks);
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < p.k; ++j) {
-      int r = slot_row[t * p.k + j];
-      const float4* src = reinterpret_cast<const float4*>(p.dXr + (size_t)r * p.H + c * 8);
-      float4 a = src[0], b = src[1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  const int slices = (chunks + 63) / 64;
+  const long units = (long)p.T * slices;
+  for (long u = (long)blockIdx.x * 4 + wave; u < units; u += (long)gridDim.x * 4) {
+    const int t = (int)(u / slices), sl = (int)(u - (long)t * slices);
+    const int32_t* sr = slot_row + (size_t)t * p.k;
+    const int c = sl * 64 + lane;
+    const bool has = c < chunks;
+    const int cc = has ? c : 0;                     // in-bounds reads for idle lanes
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int j = 0;
+    for (; j + 4 <= p.k; j += 4) {
+      f32x4v v[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* src = p.dXr + (size_t)sr[j + q] * p.H + cc * 8;
+        v[q][0] = load_nt_f32x4(src);
+        v[q][1] = load_nt_f32x4(src + 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);           // all eight loads in flight before the adds
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add8(acc, v[q][0], v[q][1]);
     }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(dX + (size_t)t * p.H + c * 8) = o;
-    for (int j = c; j < p.k; j += chunks) {
-      int r = slot_row[t * p.k + j];
+    for (; j < p.k; ++j) {
+      const float* src = p.dXr + (size_t)sr[j] * p.H + cc * 8;
+      add8(acc, load_nt_f32x4(src), load_nt_f32x4(src + 4));
+    }
+    if (has) {
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(dX + (size_t)t * p.H + c * 8) = o;
+    }
+    // d_topk_w: lane j of the token's first slice sums slot j's partials (k <= 32 lanes)
+    if (sl == 0 && lane < p.k) {
+      const int r = sr[lane];
       float s = 0.f;
       for (int q = 0; q < p.nparts; ++q) s += p.dwt_part[(size_t)r * p.nparts + q];
-      dtw[t * p.k + j] = s;
+      dtw[t * p.k + lane] = s;
     }
   }
 }
 
 hipError_t launch_bwd_token_reduce(const GemmArgs& a, const int32_t* slot_row, uint16_t* dX,
                                    float* dtw, hipStream_t s) {
-  long total = (long)a.T * (a.H / 8);
-  long blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  const long units = (long)a.T * ((a.H / 8 + 63) / 64);
+  long blocks = (units + 3) / 4;
+  if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(k_bwd_token_reduce, dim3((int)blocks), dim3(256), 0, s, a, slot_row, dX, dtw);
   return hipGetLastError();
 }
