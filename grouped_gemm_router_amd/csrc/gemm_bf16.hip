@@ -243,6 +243,8 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
+  // its epilogue runs at the register limit: the plain two-stage schedule
+  static constexpr bool EARLY_NEXT = false;
   // one staged 32 x 32 bf16 block: 64-byte rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
   static constexpr int OUT = 32 * 64;
   static constexpr int NSLOT = RowEpiLds<C>::BYTES / OUT < 4 ? RowEpiLds<C>::BYTES / OUT : 4;

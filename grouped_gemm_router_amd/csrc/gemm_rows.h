@@ -215,6 +215,14 @@ struct RowEpiLds {
 // block scan's partial sums.
 constexpr int SCHED_LDS_INTS = 1024 + 1 + 16 + 1;
 
+// Whether Ops takes the two-stage schedule that issues the next tile's first k-tile in the
+// last k step (Ops::EARLY_NEXT, true when absent): an epilogue that already needs every
+// register keeps the plain schedule.
+template <class T, class = void>
+struct EarlyNext : std::true_type {};
+template <class T>
+struct EarlyNext<T, std::void_t<decltype(T::EARLY_NEXT)>> : std::bool_constant<T::EARLY_NEXT> {};
+
 // Every tile of Ops' schedule, with the stages at smem (C::NST * C::STAGE uint4) and the
 // schedule's scratch at sched_lds.  `carry` is XcdWalk's deal position, updated for a
 // schedule that follows on the same grid.
@@ -247,57 +255,121 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
       al.issue(p, tl, s * C::BK, smem + s * C::STAGE);
       bl.issue(p, tl, s * C::BK, smem + s * C::STAGE + C::A_SLOTS);
     }
-  while (true) {
-    f32x16 acc[C::FM][C::FN];
+  if constexpr (C::NST == 2 && EarlyNext<Ops>::value) {
+    // Two stages: the last k step of a tile issues the next tile's first k-tile into the
+    // other stage, the epilogue waits for it (one k step old) before its output stores and
+    // uses the stage just read as scratch, and the next tile's first k step needs no wait.
+    // The output stores then drain under that k step and are only waited for at the second
+    // one, instead of stalling every workgroup at the tile boundary.
+    int base = 0;                                         // stage of k-tile 0 of the current tile
+    bool prewaited = false;                               // k-tile 0 already waited for
+    while (true) {
+      f32x16 acc[C::FM][C::FN];
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
+      for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
+        for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
-    // k step kt: wait for k-tile kt, then compute it while (LOADS) issuing k-tile kt + NST - 1
-    auto kstep = [&](int kt, auto loads) {
-      const int ahead = nk - 1 - kt;                      // k-tiles issued after this one (capped)
-      if (kt == 0) wait_vmcnt<0>();
-      else wait_ktiles<C::NST, PERK>(ahead < C::NST - 2 ? ahead : C::NST - 2);
+          for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+      const Tile cur_tile = tl;
+      for (int kt = 0; kt < nk - 1; ++kt) {
+        if (kt > 0 || !prewaited) wait_vmcnt<0>();
+        __syncthreads();
+        const int cs = (base + kt) & 1;
+        uint4* st = smem + (cs ^ 1) * C::STAGE;
+        const int k0 = (kt + 1) * C::BK;
+        auto issue = [&](int j) {
+          if (j < AL::PER) al.issue_one(p, cur_tile, k0, st, j);
+          else bl.issue_one(p, cur_tile, k0, st + C::A_SLOTS, j - AL::PER);
+        };
+        mma_ktile_rows<C, true, PERK>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE), fa, acc, issue);
+      }
+      // last k step: its loads are the next tile's first k-tile
+      if (nk > 1 || !prewaited) wait_vmcnt<0>();
       __syncthreads();
-      const int nxt = kt + C::NST - 1;
-      uint4* st = smem + (nxt % C::NST) * C::STAGE;
-      auto issue = [&](int j) {
-        if (j < AL::PER) al.issue_one(p, tl, nxt * C::BK, st, j);
-        else bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
-      };
-      const uint8_t* cur = reinterpret_cast<const uint8_t*>(smem + (kt % C::NST) * C::STAGE);
-      mma_ktile_rows<C, decltype(loads)::value, PERK>(cur, fa, acc, issue);
-    };
-    // the last NST - 1 k steps issue nothing: peeled, not branched, so that the
-    // two instantiations never meet inside one loop body
-    int kt = 0;
-    for (; kt < nk - (C::NST - 1); ++kt) kstep(kt, std::true_type{});
-    for (; kt < nk; ++kt) kstep(kt, std::false_type{});
-    // every wave is past its last LDS read before any stage is refilled
-    __syncthreads();
-    const Tile done = tl;
-    walk.next();
-    const bool more = walk.valid();
-    if (more) {
-      // start the next tile's loads, then run this tile's epilogue under them
-      tl = sched.tile(walk.t);
-      al.init(p, tl);
-      bl.init(p, tl);
+      const int scratch = (base + nk - 1) & 1;            // the stage this step reads
+      walk.next();
+      const bool more = walk.valid();
+      {
+        // without a next tile the same loads fetch this tile's first k-tile again (in bounds,
+        // never read), so that the MFMA sequence has no branch around it
+        tl = more ? sched.tile(walk.t) : cur_tile;
+        al.init(p, tl);
+        bl.init(p, tl);
+        uint4* st = smem + (scratch ^ 1) * C::STAGE;
+        auto issue = [&](int j) {
+          if (j < AL::PER) al.issue_one(p, tl, 0, st, j);
+          else bl.issue_one(p, tl, 0, st + C::A_SLOTS, j - AL::PER);
+        };
+        mma_ktile_rows<C, true, PERK>(reinterpret_cast<const uint8_t*>(smem + scratch * C::STAGE), fa, acc, issue);
+      }
+      // every wave is past its last LDS read before the stage it read becomes scratch
+      __syncthreads();
+      wait_vmcnt<0>();                                    // the next tile's first k-tile (or the
+                                                          // unread reload: no LDS write may be
+                                                          // in flight when the workgroup ends)
+      uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + scratch * C::STAGE) + wave * RowEpiLds<C>::BYTES;
+      Ops::epilogue(p, cur_tile, acc, wm, wn, lane, wave_lds);
+      if (!more) break;
+      // the scratch stage receives the next tile's second k-tile: all waves must be done with it
+      __syncthreads();
+      base = scratch ^ 1;
       nk = (tl.k_hi - tl.k_lo) / C::BK;
-#pragma unroll
-      for (int s = 0; s < C::NST - 1; ++s)
-        if (s < nk) {
-          al.issue(p, tl, s * C::BK, smem + s * C::STAGE);
-          bl.issue(p, tl, s * C::BK, smem + s * C::STAGE + C::A_SLOTS);
-        }
+      prewaited = true;
     }
-    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + (C::NST - 1) * C::STAGE) + wave * RowEpiLds<C>::BYTES;
-    Ops::epilogue(p, done, acc, wm, wn, lane, wave_lds);
-    if (!more) break;
-    // the scratch stage is the next tile's last stage: all waves must be done with it
-    __syncthreads();
+  } else {
+    while (true) {
+      f32x16 acc[C::FM][C::FN];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+      // k step kt: wait for k-tile kt, then compute it while (LOADS) issuing k-tile kt + NST - 1
+      auto kstep = [&](int kt, auto loads) {
+        const int ahead = nk - 1 - kt;                      // k-tiles issued after this one (capped)
+        if (kt == 0) wait_vmcnt<0>();
+        else wait_ktiles<C::NST, PERK>(ahead < C::NST - 2 ? ahead : C::NST - 2);
+        __syncthreads();
+        const int nxt = kt + C::NST - 1;
+        uint4* st = smem + (nxt % C::NST) * C::STAGE;
+        auto issue = [&](int j) {
+          if (j < AL::PER) al.issue_one(p, tl, nxt * C::BK, st, j);
+          else bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
+        };
+        const uint8_t* cur = reinterpret_cast<const uint8_t*>(smem + (kt % C::NST) * C::STAGE);
+        mma_ktile_rows<C, decltype(loads)::value, PERK>(cur, fa, acc, issue);
+      };
+      // the last NST - 1 k steps issue nothing: peeled, not branched, so that the
+      // two instantiations never meet inside one loop body
+      int kt = 0;
+      for (; kt < nk - (C::NST - 1); ++kt) kstep(kt, std::true_type{});
+      for (; kt < nk; ++kt) kstep(kt, std::false_type{});
+      // every wave is past its last LDS read before any stage is refilled
+      __syncthreads();
+      const Tile done = tl;
+      walk.next();
+      const bool more = walk.valid();
+      if (more) {
+        // start the next tile's loads, then run this tile's epilogue under them
+        tl = sched.tile(walk.t);
+        al.init(p, tl);
+        bl.init(p, tl);
+        nk = (tl.k_hi - tl.k_lo) / C::BK;
+#pragma unroll
+        for (int s = 0; s < C::NST - 1; ++s)
+          if (s < nk) {
+            al.issue(p, tl, s * C::BK, smem + s * C::STAGE);
+            bl.issue(p, tl, s * C::BK, smem + s * C::STAGE + C::A_SLOTS);
+          }
+      }
+      uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + (C::NST - 1) * C::STAGE) + wave * RowEpiLds<C>::BYTES;
+      Ops::epilogue(p, done, acc, wm, wn, lane, wave_lds);
+      if (!more) break;
+      // the scratch stage is the next tile's last stage: all waves must be done with it
+      __syncthreads();
+    }
   }
 }
 
