@@ -210,6 +210,12 @@ __device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
   al.issue(p, tl, 0, smem);
   bl.issue(p, tl, 0, smem + C::A_SLOTS);
   issue_scales(0, 0);
+  // The last k step of a tile issues the next tile's first k-tile into the other stage, the
+  // epilogue waits for it (one k step old) before its output stores and uses the stage just
+  // read as scratch, and the next tile's first k step needs no wait: the output stores drain
+  // under that step instead of stalling every workgroup at the tile boundary.
+  int base = 0;                                         // stage of k-tile 0 of the current tile
+  bool prewaited = false;                               // k-tile 0 already waited for
   while (true) {
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -218,42 +224,51 @@ __device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
-    auto kstep = [&](int kt, auto loads) {
-      wait_vmcnt<0>();                                    // k-tile kt (and any earlier stores)
+    const Tile cur_tile = tl;
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      if (kt > 0 || !prewaited) wait_vmcnt<0>();
       __syncthreads();
-      const int nxt = kt + 1, ns = nxt & 1;
+      const int cs = (base + kt) & 1, ns = cs ^ 1;
       uint4* st = smem + ns * C::STAGE;
+      const int k0 = (kt + 1) * C::BK;
       auto issue = [&](int j) {
-        if (j < AL::PER) al.issue_one(p, tl, nxt * C::BK, st, j);
-        else if (j < AL::PER + BL::PER) bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
-        else issue_scales(nxt, ns);
+        if (j < AL::PER) al.issue_one(p, cur_tile, k0, st, j);
+        else if (j < AL::PER + BL::PER) bl.issue_one(p, cur_tile, k0, st + C::A_SLOTS, j - AL::PER);
+        else issue_scales(kt + 1, ns);
       };
-      const int cs = kt & 1;
-      mma_ktile_mx<C, decltype(loads)::value, PERK>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE),
-                                                    &sscale[cs][0], &sscale[cs][C::BM], fa, acc, lane, issue);
-    };
-    int kt = 0;
-    for (; kt < nk - 1; ++kt) kstep(kt, std::true_type{});
-    kstep(kt, std::false_type{});
-    // every wave is past its last LDS read before any stage is refilled
+      mma_ktile_mx<C, true, PERK>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE), &sscale[cs][0],
+                                  &sscale[cs][C::BM], fa, acc, lane, issue);
+    }
+    // last k step: its loads are the next tile's first k-tile (without a next tile, this
+    // tile's first k-tile again: in bounds, never read, and waited for before the exit)
+    if (nk > 1 || !prewaited) wait_vmcnt<0>();
     __syncthreads();
-    const Tile done = tl;
+    const int scratch = (base + nk - 1) & 1, ns = scratch ^ 1;
     walk.next();
     const bool more = walk.valid();
-    if (more) {
-      // start the next tile's first k-tile, then run this tile's epilogue under it
-      tl = sched.tile(walk.t);
-      init_loaders();
-      nk = (tl.k_hi - tl.k_lo) / C::BK;
-      al.issue(p, tl, 0, smem);
-      bl.issue(p, tl, 0, smem + C::A_SLOTS);
-      issue_scales(0, 0);
+    tl = more ? sched.tile(walk.t) : cur_tile;
+    init_loaders();
+    {
+      uint4* st = smem + ns * C::STAGE;
+      auto issue = [&](int j) {
+        if (j < AL::PER) al.issue_one(p, tl, 0, st, j);
+        else if (j < AL::PER + BL::PER) bl.issue_one(p, tl, 0, st + C::A_SLOTS, j - AL::PER);
+        else issue_scales(0, ns);
+      };
+      mma_ktile_mx<C, true, PERK>(reinterpret_cast<const uint8_t*>(smem + scratch * C::STAGE), &sscale[scratch][0],
+                                  &sscale[scratch][C::BM], fa, acc, lane, issue);
     }
-    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + C::STAGE) + wave * RowEpiLds<C>::BYTES;
-    Epi::apply(p, done, acc, wm, wn, lane, wave_lds);
-    if (!more) break;
-    // the scratch stage is the next tile's second stage: all waves must be done with it
+    // every wave is past its last LDS read before the stage it read becomes scratch
     __syncthreads();
+    wait_vmcnt<0>();
+    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(smem + scratch * C::STAGE) + wave * RowEpiLds<C>::BYTES;
+    Epi::apply(p, cur_tile, acc, wm, wn, lane, wave_lds);
+    if (!more) break;
+    // the scratch stage receives the next tile's second k-tile: all waves must be done with it
+    __syncthreads();
+    base = ns;
+    nk = (tl.k_hi - tl.k_lo) / C::BK;
+    prewaited = true;
   }
 }
 
