@@ -422,6 +422,31 @@ def expert_mlp(X, row_token, offsets, W_gate, W_up, W_down, mxfp8: bool = False,
     return h, O
 
 
+def grouped_gemm(A, B, m_indptr, mxfp8: bool = False, exact: bool = False):
+    """LightMoE "Grouped GEMM": contiguous expert-major rows A [M, K], weights B [E, N, K]
+    (bits or values, or a callable e -> [N, K]) and ``m_indptr`` [E + 1] (int32 offsets,
+    zero-row experts valid).  C[r] = bf16(A[r] . B[e]^T) for m_indptr[e] <= r < m_indptr[e+1],
+    with one rounding of the exact sum.  With ``mxfp8`` both operands are the values their
+    MXFP8 representation (blocks of 32 along K) holds.  Rows outside every expert stay 0.
+    Returns C [M, N] as float64."""
+    Av = _as_f64(A)
+    gb = _expert_getter(B)
+    off = np.asarray(m_indptr, dtype=np.int64)
+    E = off.shape[0] - 1
+    M = Av.shape[0]
+    N = gb(0).shape[0] if E else 0
+    C = np.zeros((M, N))
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        a, b = Av[lo:hi], gb(e)
+        if mxfp8:
+            a, b = mx_fake_quant(a), mx_fake_quant(b)
+        C[lo:hi] = a @ b.T
+    return C if exact else bf16_round(C)
+
+
 def combine(O, slot_row, topk_w, exact: bool = False):
     """Y[t] = bf16( sum over j ascending of w[t, j] * O[slot_row[t*k + j]] )."""
     w = np.asarray(topk_w, dtype=np.float64)
