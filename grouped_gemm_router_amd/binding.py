@@ -26,7 +26,7 @@ CALL_DISPATCH, CALL_EXPERT_MLP, CALL_BACKWARD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_validate_problem", "moe_workspace_size", "moe_check_device",
            "moe_route", "moe_dispatch", "moe_pack_weights", "moe_mx_quantize", "moe_expert_mlp",
-           "moe_combine", "moe_backward", "moe_route_backward")
+           "moe_combine", "moe_backward", "moe_route_backward", "moe_grouped_gemm")
 
 
 class MoEError(RuntimeError):
@@ -60,6 +60,7 @@ def _load() -> ctypes.CDLL:
         "moe_expert_mlp": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_combine": (ctypes.c_int, [P, P, P, I32, I32, I32, P, P]),
         "moe_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_gemm": (ctypes.c_int, [I32, P, I32, I64, I32, I32, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -217,6 +218,28 @@ def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=N
                                                 _ptr(Wg_t), _ptr(Wu_t), _ptr(Wd_t), _ptr(Sg), _ptr(Su),
                                                 _ptr(Sd), _ptr(H_rows), _ptr(O_rows), _ptr(ws), n, _stream()))
     return H_rows, O_rows
+
+
+def grouped_gemm(A, B_t, m_indptr, scales=None, C=None):
+    """Standalone grouped GEMM over expert-major rows: C[r] = bf16(A[r] B_t[e]^T) for the rows
+    m_indptr[e] <= r < m_indptr[e+1].  bf16: A [M, K], B_t [E, N, K] (pack_weights); MXFP8:
+    A and B_t as E4M3 codes with ``scales = (SA [M, K/32], SB [E, N, K/32])``."""
+    M, K = A.shape
+    E, N, _ = B_t.shape
+    mx = scales is not None
+    dt = torch.uint8 if mx else torch.bfloat16
+    _expect(A, "A", dt, (M, K))
+    _expect(B_t, "B_t", dt, (E, N, K))
+    _expect(m_indptr, "m_indptr", torch.int32, (E + 1,))
+    SA, SB = scales if mx else (None, None)
+    if mx:
+        _expect(SA, "SA", torch.uint8, (M, K // 32))
+        _expect(SB, "SB", torch.uint8, (E, N, K // 32))
+    C = torch.empty(M, N, dtype=torch.bfloat16, device=A.device) if C is None else C
+    _expect(C, "C", torch.bfloat16, (M, N))
+    _check("moe_grouped_gemm", lib.moe_grouped_gemm(DTYPE["mxfp8" if mx else "bf16"], _ptr(m_indptr), E, M, N, K,
+                                                    _ptr(A), _ptr(SA), _ptr(B_t), _ptr(SB), _ptr(C), _stream()))
+    return C
 
 
 def combine(O_rows, slot_row, topk_w, Y=None):

@@ -39,8 +39,10 @@ moe_status check_problem(const moe_problem* p) {
     return MOE_ERR_INVALID_ARG;
   const int align = p->dtype == MOE_DTYPE_MXFP8 ? 128 : 64;
   if (p->H % align || p->I % align) return MOE_ERR_UNSUPPORTED_SHAPE;
-  // element offsets of the largest tensors must fit the kernels' index math
-  if ((int64_t)p->T * p->k * (int64_t)p->H >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // the row loaders use 32-bit byte offsets: token rows (X, dY: T*H bf16) and expert-major
+  // rows (up to 2I bf16 each: dg|du) must stay below 4 GiB
+  if ((int64_t)p->T * p->H >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)p->T * p->k * (int64_t)p->I >= (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
   return MOE_OK;
 }
 
@@ -234,6 +236,44 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
   if (e == hipSuccess) e = moe::launch_mx_quantize((const uint16_t*)H_rows, (long)A, p->I, Hq, Hs, st);
   if (e == hipSuccess) e = moe::launch_mx_down(m, st);
   return from_hip(e);
+}
+
+MOE_API moe_status moe_grouped_gemm(int32_t dtype, const int32_t* m_indptr, int32_t E, int64_t M, int32_t N,
+                                    int32_t K, const void* A, const uint8_t* SA, const void* B_t, const uint8_t* SB,
+                                    void* C, void* stream) {
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || M < 0 || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  const bool mx = dtype == MOE_DTYPE_MXFP8;
+  const int align = mx ? 128 : 64;
+  if (E > MAX_E || N % align || K % align) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (M >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!m_indptr || !B_t) return MOE_ERR_INVALID_ARG;
+  if (M > 0 && (!A || !C)) return MOE_ERR_INVALID_ARG;
+  if (mx != (SA && SB)) return MOE_ERR_INVALID_ARG;
+  if (!mx && (SA || SB)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;                            // nothing to compute
+  moe_status s = device_ok();
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (!mx) {
+    // the down projection's kernel: rows of A ("h", K = I) times B_t ([E, N = H, K]) into C
+    moe::GemmArgs a = {};
+    a.T = (int)M; a.k = 1; a.H = N; a.I = K; a.E = E;
+    a.act = MOE_ACT_SWIGLU;
+    a.offsets = m_indptr;
+    a.Hrows = (uint16_t*)A;
+    a.Wd_t = (const uint16_t*)B_t;
+    a.Orows = (uint16_t*)C;
+    return from_hip(moe::launch_fwd_down(a, st));
+  }
+  moe::MxArgs m = {};
+  m.T = (int)M; m.k = 1; m.H = N; m.I = K; m.E = E;
+  m.act = MOE_ACT_SWIGLU;
+  m.offsets = m_indptr;
+  m.Hq = (const uint8_t*)A; m.Hs = SA;
+  m.Wd = (const uint8_t*)B_t; m.Sd = SB;
+  m.Orows = (uint16_t*)C;
+  return from_hip(moe::launch_mx_down(m, st));
 }
 
 MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, const float* topk_w, int32_t T,

@@ -13,6 +13,7 @@
  *   moe_combine     weighted sum of each token's k expert rows
  *   moe_backward    dX, dW_gate, dW_up, dW_down, d(top-k weights)
  *   moe_route_backward  d(router logits) from d(top-k weights)
+ *   moe_grouped_gemm    standalone grouped GEMM over expert-major rows
  *
  * Conventions shared by every call
  * --------------------------------
@@ -28,7 +29,8 @@
  *   gfx950 gives MOE_ERR_UNSUPPORTED_DEVICE.  A launch failure gives
  *   MOE_ERR_HIP.  No C++ exception crosses this interface.
  * - Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31; H and I multiples
- *   of 64 (MXFP8: multiples of 128).
+ *   of 64 (MXFP8: multiples of 128); T*H < 2^31 and T*k*I < 2^30 (the row
+ *   loaders address token rows and expert-major rows with 32-bit byte offsets).
  * - An empty batch (T = 0) is valid: every token-sized array (logits, X, dY,
  *   the routing and dispatch arrays, the row buffers, Y, dX, the top-k
  *   gradients) may then be NULL.  moe_dispatch still writes expert_offsets
@@ -257,6 +259,27 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
                                 const void* Wu_t, void* dX, void* dW_gate, void* dW_up,
                                 void* dW_down, float* d_topk_w, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/*
+ * Standalone grouped GEMM (LightMoE "Grouped GEMM": contiguous expert-major
+ * rows, m_indptr of E+1 int32 offsets, zero-row experts valid, b as
+ * [num_experts, N, K]; the same kernels as the expert MLP's down projection):
+ *   C[r] = bf16( A[r] B_t[e]^T )   for m_indptr[e] <= r < m_indptr[e+1]
+ * with fp32 accumulation.
+ *   dtype        MOE_DTYPE_BF16 or MOE_DTYPE_MXFP8
+ *   m_indptr     [E+1] int32 (device): m_indptr[0] = 0, non-decreasing,
+ *                m_indptr[E] <= M; rows past m_indptr[E] are not written
+ *   bf16:  A [M, K] bf16, B_t [E, N, K] bf16 (moe_pack_weights of [E, K, N]);
+ *          SA, SB must be NULL
+ *   MXFP8: A [M, K] and B_t [E, N, K] E4M3 codes with SA [M, K/32] and
+ *          SB [E, N, K/32] E8M0 scales (moe_mx_quantize)
+ *   C      [M, N] bf16 out
+ *   Limits: 1 <= E <= 1024; 0 <= M < 2^31 with M*K < 2^31; N and K multiples
+ *   of 64 (MXFP8: 128).  M = 0 is valid and does nothing.
+ */
+MOE_API moe_status moe_grouped_gemm(int32_t dtype, const int32_t* m_indptr, int32_t E, int64_t M,
+                                    int32_t N, int32_t K, const void* A, const uint8_t* SA,
+                                    const void* B_t, const uint8_t* SB, void* C, void* stream);
 
 #ifdef __cplusplus
 }

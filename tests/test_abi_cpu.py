@@ -170,3 +170,35 @@ def test_empty_batch_accepts_null_token_arrays():
     assert lib.moe_backward(ctypes.byref(p), *ptrs, None, 0, None) == 1
     assert lib.moe_expert_mlp(ctypes.byref(p), None, None, None, v, v, v, None, None, None, None, None, None, 0,
                               None) == 1
+
+
+def test_grouped_gemm_argument_checks():
+    """moe_grouped_gemm: shape limits (2), null pointers and scale/dtype mismatches (1), and an
+    empty row set that returns MOE_OK without touching the device."""
+    import ctypes
+    from grouped_gemm_router_amd import binding as B
+    f = B.lib.moe_grouped_gemm
+    v = ctypes.c_void_p(16)
+    bf16, mx = B.DTYPE["bf16"], B.DTYPE["mxfp8"]
+    assert f(bf16, v, 4, 0, 128, 64, None, None, v, None, None, None) == 0        # M = 0
+    assert f(bf16, v, 4, 10, 100, 64, v, None, v, None, v, None) == 2             # N % 64
+    assert f(bf16, v, 4, 10, 128, 96, v, None, v, None, v, None) == 2             # K % 64
+    assert f(mx, v, 4, 10, 128, 64, v, v, v, v, v, None) == 2                     # MXFP8 K % 128
+    assert f(bf16, v, 2048, 10, 128, 64, v, None, v, None, v, None) == 2          # E > 1024
+    assert f(bf16, v, 4, 2 ** 25, 128, 128, v, None, v, None, v, None) == 2       # M * K >= 2^31
+    assert f(bf16, None, 4, 10, 128, 64, v, None, v, None, v, None) == 1          # m_indptr
+    assert f(bf16, v, 4, 10, 128, 64, None, None, v, None, v, None) == 1          # A
+    assert f(bf16, v, 4, 10, 128, 64, v, v, v, None, v, None) == 1                # scales with bf16
+    assert f(mx, v, 4, 10, 128, 128, v, None, v, v, v, None) == 1                 # missing SA
+    assert f(7, v, 4, 10, 128, 64, v, None, v, None, v, None) == 1                # dtype
+    assert f(bf16, v, 0, 10, 128, 64, v, None, v, None, v, None) == 1             # E = 0
+
+
+def test_row_offset_limits():
+    """Token rows (T*H bf16) and expert-major rows (T*k rows of up to 2I bf16) stay below the
+    4 GiB the 32-bit byte offsets of the row loaders reach."""
+    from grouped_gemm_router_amd import binding as B
+    assert B.validate_problem(B.problem(2 ** 19, 2048, 256, 64, 2)) == 0          # T*H = 2^30, T*k*I = 2^28
+    assert B.validate_problem(B.problem(2 ** 20, 2048, 64, 64, 1)) == 2           # T*H = 2^31
+    assert B.validate_problem(B.problem(2 ** 18, 256, 1024, 64, 4)) == 2          # T*k*I = 2^30
+    assert B.validate_problem(B.problem(2 ** 18, 256, 512, 64, 4)) == 0           # T*k*I = 2^29

@@ -1,0 +1,67 @@
+"""GPU parity of the standalone grouped GEMM (moe_grouped_gemm: expert-major rows,
+B as [E, N, K], m_indptr offsets) against the oracle, in bf16 and MXFP8, over expert
+sizes on every remainder-tile boundary, zero-row experts, a partial column tile and rows
+past the last expert (which must stay untouched)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+from grouped_gemm_router_amd import workloads as wl
+
+from gpu_helpers import check_close, to_bits, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+COUNTS = [0, 1, 63, 65, 128, 129, 193, 256, 300, 0, 513]
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _operands(seed, M, N, K, E):
+    rng = np.random.default_rng(seed)
+    A = wl.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    Bt = wl.f32_to_bf16_bits((rng.standard_normal((E, N, K), dtype=np.float32) / np.sqrt(K)).astype(np.float32))
+    return A, Bt
+
+
+@pytest.mark.parametrize("dtype,N,K", [("bf16", 320, 192), ("mxfp8", 256, 256)])
+def test_grouped_gemm_vs_oracle(dtype, N, K):
+    from grouped_gemm_router_amd import binding as B
+    _say("grouped gemm", dtype, N, K, COUNTS)
+    E = len(COUNTS)
+    m_indptr = np.concatenate([[0], np.cumsum(COUNTS)]).astype(np.int32)
+    M = int(m_indptr[-1]) + 9                      # 9 rows past the last expert
+    A, Bt = _operands(81, M, N, K, E)
+    off = torch.from_numpy(m_indptr).cuda()
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if dtype == "bf16":
+        B.grouped_gemm(to_dev(A), to_dev(Bt), off, C=C)
+    else:
+        qa, sa = B.mx_quantize(to_dev(A))
+        qb, sb = B.mx_quantize(to_dev(Bt).reshape(E * N, K))
+        B.grouped_gemm(qa, qb.reshape(E, N, K), off, scales=(sa, sb.reshape(E, N, K // 32)), C=C)
+    torch.cuda.synchronize()
+    ref = orc.grouped_gemm(A, Bt, m_indptr, mxfp8=dtype == "mxfp8")
+    rows = int(m_indptr[-1])
+    check_close(to_f64(C[:rows]), ref[:rows], f"{dtype} C")
+    assert torch.isnan(C[rows:].float()).all(), "rows past the last expert were written"
+
+
+def test_expert_mlp_down_is_the_grouped_gemm():
+    """The layer's O rows equal the standalone grouped GEMM of its h rows with the packed
+    W_down, bit for bit (the same kernel and tiles)."""
+    from grouped_gemm_router_amd import binding as B
+    from grouped_gemm_router_amd.layer import MoELayer
+    from gpu_helpers import device_weights
+    cfg = wl.config("tiny", name="gg_layer", T=300, H=320, I=192, E=5, k=3, seed=82)
+    _say("grouped gemm vs layer", cfg)
+    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k).load_weights(W["gate"], W["up"], W["down"])
+    layer.forward(torch.from_numpy(wl.make_logits(cfg)).cuda(), to_dev(wl.make_x(cfg)))
+    pl = layer.plan(cfg.T)
+    C = B.grouped_gemm(pl["H_rows"], layer.Wd_t, pl["offsets"])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(C), to_bits(pl["O_rows"]))
