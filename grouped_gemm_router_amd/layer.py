@@ -98,6 +98,40 @@ class MoELayer:
         B.combine(pl["O_rows"], pl["slot_row"], pl["topk_w"], pl["Y"])
         return pl["Y"]
 
+    def forward_routed(self, topk_idx: torch.Tensor, topk_w: torch.Tensor, X: torch.Tensor,
+                       backward_plan: bool = False):
+        """The layer with the routing given by the caller (LightMoE "MoE inference": the call takes
+        the top-k ids, int32 with distinct experts per token, and their fp32 weights): dispatch,
+        expert MLP and combine.  The ids and weights are copied into the plan, so that a following
+        ``backward`` sees them."""
+        T = X.shape[0]
+        pl = self.plan(T, backward_plan)
+        for name, t, dt in (("topk_idx", topk_idx, torch.int32), ("topk_w", topk_w, torch.float32)):
+            if t.dtype != dt or tuple(t.shape) != (T, self.k) or t.device.type != self.device.type:
+                raise ValueError(f"{name} must be a [{T}, {self.k}] {dt} tensor on {self.device}")
+        pl["topk_idx"].copy_(topk_idx)
+        pl["topk_w"].copy_(topk_w)
+        B.dispatch(pl["topk_idx"], self.E, (pl["offsets"], pl["row_token"], pl["row_slot"], pl["slot_row"]),
+                   ws=pl["ws_dispatch"])
+        B.expert_mlp(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
+                     scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"],
+                     activation=self.activation, act_limit=self.act_limit)
+        B.combine(pl["O_rows"], pl["slot_row"], pl["topk_w"], pl["Y"])
+        return pl["Y"]
+
+    def run_routed(self, x_rows: torch.Tensor, m_indptr: torch.Tensor):
+        """The expert MLP over rows already in expert-major order (LightMoE "MoE inference":
+        frameworks with expert-major input): O[r] = MLP_e(x_rows[r]) for the rows
+        m_indptr[e] <= r < m_indptr[e+1] of every expert; no routing weights, no combine.
+        Returns O [rows, H] bf16."""
+        A = x_rows.shape[0]
+        key = ("rows", A)
+        if key not in self._plans:
+            self._plans[key] = torch.arange(A, dtype=torch.int32, device=self.device)
+        _, O = B.expert_mlp(x_rows, self._plans[key], m_indptr, self.Wg_t, self.Wu_t, self.Wd_t, 1,
+                            scales=self.scales, activation=self.activation, act_limit=self.act_limit)
+        return O
+
     def backward(self, X: torch.Tensor, dY: torch.Tensor):
         """Gradients of the last forward with the same X (needs backward_plan=True)."""
         if self.dtype != "bf16" or self.W_up is None:

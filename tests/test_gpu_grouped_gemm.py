@@ -65,3 +65,26 @@ def test_expert_mlp_down_is_the_grouped_gemm():
     C = B.grouped_gemm(pl["H_rows"], layer.Wd_t, pl["offsets"])
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(C), to_bits(pl["O_rows"]))
+
+
+def test_forward_routed_and_run_routed_match_the_layer():
+    """The layer with caller-given routing gives the routed forward's Y bit for bit, and the
+    expert MLP over pre-gathered expert-major rows gives its O rows bit for bit."""
+    from grouped_gemm_router_amd.layer import MoELayer
+    from gpu_helpers import device_weights
+    cfg = wl.config("tiny", name="routed", T=300, H=320, I=192, E=5, k=3, seed=83)
+    _say("forward_routed / run_routed", cfg)
+    W = {n: device_weights(cfg, n) for n in ("gate", "up", "down")}
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k).load_weights(W["gate"], W["up"], W["down"])
+    X = to_dev(wl.make_x(cfg))
+    Y = layer.forward(torch.from_numpy(wl.make_logits(cfg)).cuda(), X).clone()
+    pl = layer.plan(cfg.T)
+    idx, w = pl["topk_idx"].clone(), pl["topk_w"].clone()
+    O = pl["O_rows"].clone()
+    rows = X[pl["row_token"].long()].contiguous()
+    offsets = pl["offsets"].clone()
+    Y2 = layer.forward_routed(idx, w, X)
+    O2 = layer.run_routed(rows, offsets)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(Y2), to_bits(Y))
+    assert np.array_equal(to_bits(O2), to_bits(O))
