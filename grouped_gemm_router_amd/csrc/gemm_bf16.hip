@@ -128,8 +128,8 @@ struct RSrcGateUpWT {    // [W_gate | W_up] [E, H, I] read as [E, N = H, K = 2I]
 // ------------------------------------------------------------------------
 // Ops: schedule + loaders + epilogue of each GEMM
 // ------------------------------------------------------------------------
-// PART: which rows of each expert the schedule covers (all, or the full / tail
-// split of 256-row blocks).
+// PART: which rows of each expert the schedule covers (all of them, its full 256-row blocks,
+// or one of the three remainder classes; RowPart).
 template <class C, class SrcA_, class SrcB_, int PART = ROWS_ALL>
 struct RowOpsBase {
   using SrcA = SrcA_;
