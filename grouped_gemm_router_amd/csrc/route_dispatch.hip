@@ -8,18 +8,26 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router: one wave per token.  Each lane keeps E/64 (up to 16) logits in
-// registers; k rounds of a wave arg-max pick the experts in descending logit
-// order, ties to the lowest index.  The weights are exp(l_j - l_max) over the
-// chosen logits, normalised by their sum (softmax over E renormalised over k).
+// Router: a group of LPT lanes per token (16, 32 or 64; a wave routes 64/LPT
+// tokens).  Each lane keeps NPL logits (E <= LPT*NPL) in registers; k rounds
+// of a group arg-max pick the experts in descending logit order, ties to the
+// lowest index.  The weights are exp(l_j - l_max) over the chosen logits,
+// normalised by their sum (softmax over E renormalised over k).
 //
 // The arg-max runs on 64-bit keys that order exactly like (logit, -index):
 // high word = the fp32 logit mapped to an unsigned integer of the same order
-// (-0.0 first turned into +0.0), low word = ~index.  Inside each 16-lane row the
-// maximum key is spread with DPP lane permutations (no LDS round trip); the four
-// row maxima are combined through readlane.
+// (-0.0 first turned into +0.0), low word = ~index.  Inside each 16-lane row
+// the maximum key is spread with DPP lane permutations (no LDS round trip);
+// wider groups combine their row maxima through readlane.  Each round's
+// winner is uniform over the group, so every lane accumulates the softmax
+// numerators and their sum in round order, with no cross-lane sum.
+//
+// Narrow groups cut the VALU work per token (the work of a round grows with
+// NPL, less than linearly, while a wave serves 64/LPT tokens at once); small
+// batches keep whole-wave groups, whose rounds are shorter.
 // ---------------------------------------------------------------------------
 constexpr int ROUTE_MAX_PER_LANE = 16;
+constexpr int ROUTE_NARROW_MIN_T = 1024;   // batches from this size on use 16- or 32-lane groups
 
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
   uint32_t u = __float_as_uint(v + 0.0f);
@@ -46,69 +54,106 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Maximum key of the wave (every lane gets it).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+// Maximum key of each LPT-lane group (every lane of the group gets it).
+template <int LPT>
+__device__ __forceinline__ uint64_t group_max_key(uint64_t k, int lane) {
   k = max_u64(k, dpp_u64<0xb1>(k));    // quad_perm [1,0,3,2]: lane ^ 1
   k = max_u64(k, dpp_u64<0x4e>(k));    // quad_perm [2,3,0,1]: lane ^ 2
   k = max_u64(k, dpp_u64<0x141>(k));   // row_half_mirror: the other quad of each 8
   k = max_u64(k, dpp_u64<0x140>(k));   // row_mirror: the other half of each 16
-  return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
+  if constexpr (LPT == 16) {
+    return k;
+  } else {
+    const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
+    const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
+    const uint64_t lo = max_u64(r0, r1), hi = max_u64(r2, r3);
+    if constexpr (LPT == 32) return lane < 32 ? lo : hi;
+    else return max_u64(lo, hi);
+  }
 }
 
-// Routes one token with one wave, NPL logits per lane (E <= 64 NPL): writes
-// its k expert ids (descending logit) and renormalised weights.
-template <int NPL>
-__device__ __forceinline__ void route_token_n(const float* __restrict__ row, int E, int k, int lane,
-                                              int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+// Routes the tokens of one wave: token t0 + lane / LPT with the lanes of its
+// group; writes each token's k expert ids (descending logit) and renormalised
+// weights.  Every lane loads all its logits at once (an index past E reads
+// logit 0 and is masked); groups past T route token t0 and write nothing.
+template <int LPT, int NPL>
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int T, int E, int k, int t0,
+                                             int lane, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int l = lane % LPT;
+  const int t = t0 + lane / LPT;
+  const bool valid = t < T;
+  const float* row = logits + (size_t)(valid ? t : t0) * E;
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = row[(l + LPT * i < E) ? l + LPT * i : 0];
   uint64_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? route_key(row[e], e) : 0ull;   // 0 sorts below every real key
+    const int e = l + LPT * i;
+    key[i] = (e < E) ? route_key(v[i], e) : 0ull;       // 0 sorts below every real key
   }
-  uint64_t mine = 0;                                    // lane j < k keeps the j-th chosen key
+  int my_e = 0;                                         // lane j < k of the group keeps the j-th choice
+  float my_ex = 0.f, sum = 0.f, first = 0.f;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) best = max_u64(best, key[i]);
-    const uint64_t top = wave_max_key(best);
+    const uint64_t top = group_max_key<LPT>(best, lane);
     const int e = (int)~(uint32_t)top;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + 64 * i == e) key[i] = 0ull;            // taken
-    if (lane == j) mine = top;
+      if (l + LPT * i == e) key[i] = 0ull;              // taken
+    const float lg = route_key_logit(top);
+    if (j == 0) first = lg;
+    const float ex = expf(lg - first);
+    sum += ex;
+    if (l == j) {
+      my_e = e;
+      my_ex = ex;
+    }
   }
-  const float first = route_key_logit(readlane_u64(mine, 0));
-  const float ex = (lane < k) ? expf(route_key_logit(mine) - first) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-  if (lane < k) {
-    idx_out[lane] = (int)~(uint32_t)mine;
-    w_out[lane] = ex / sum;
+  if (valid && l < k) {
+    topk_idx[(size_t)t * k + l] = my_e;
+    topk_w[(size_t)t * k + l] = my_ex / sum;
   }
 }
 
-// The smallest logits-per-lane count that holds E (the per-round work scales with it).
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
-                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  if (E <= 64) route_token_n<1>(row, E, k, lane, idx_out, w_out);
-  else if (E <= 128) route_token_n<2>(row, E, k, lane, idx_out, w_out);
-  else if (E <= 256) route_token_n<4>(row, E, k, lane, idx_out, w_out);
-  else if (E <= 512) route_token_n<8>(row, E, k, lane, idx_out, w_out);
-  else route_token_n<ROUTE_MAX_PER_LANE>(row, E, k, lane, idx_out, w_out);
+// The smallest logits-per-lane count that holds E (the work of a round grows with it).
+template <int LPT>
+__device__ __forceinline__ void route_wave(const float* __restrict__ logits, int T, int E, int k, int t0, int lane,
+                                           int32_t* __restrict__ idx, float* __restrict__ w) {
+  if (E <= LPT) route_tokens<LPT, 1>(logits, T, E, k, t0, lane, idx, w);
+  else if (E <= 2 * LPT) route_tokens<LPT, 2>(logits, T, E, k, t0, lane, idx, w);
+  else if (E <= 4 * LPT) route_tokens<LPT, 4>(logits, T, E, k, t0, lane, idx, w);
+  else if (E <= 8 * LPT) route_tokens<LPT, 8>(logits, T, E, k, t0, lane, idx, w);
+  else route_tokens<LPT, ROUTE_MAX_PER_LANE>(logits, T, E, k, t0, lane, idx, w);
 }
 
+template <int LPT>
 __global__ void __launch_bounds__(256) k_route(const float* __restrict__ logits, int T, int E, int k,
                                                int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int TPW = 64 / LPT;                          // tokens per wave
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  route_token(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  if (t0 >= T) return;
+  route_wave<LPT>(logits, T, E, k, t0, lane, topk_idx, topk_w);
+}
+
+// Group width: 16 lanes while E <= 256 and k <= 16, 32 while E <= 512 (k <= 32
+// always), else 64; whole waves for batches under ROUTE_NARROW_MIN_T tokens.
+static int route_group_lanes(int T, int E, int k) {
+  if (T < ROUTE_NARROW_MIN_T || E > 32 * ROUTE_MAX_PER_LANE) return 64;
+  if (E > 16 * ROUTE_MAX_PER_LANE || k > 16) return 32;
+  return 16;
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+  const int lpt = route_group_lanes(T, E, k);
+  const int per_block = 4 * (64 / lpt);
+  const dim3 grid((T + per_block - 1) / per_block);
+  if (lpt == 16) hipLaunchKernelGGL(k_route<16>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
+  else if (lpt == 32) hipLaunchKernelGGL(k_route<32>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
+  else hipLaunchKernelGGL(k_route<64>, grid, dim3(256), 0, s, logits, T, E, k, idx, w);
   return hipGetLastError();
 }
 
@@ -211,8 +256,6 @@ __global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restric
                                                         int nsub, int32_t* __restrict__ counts) {
   __shared__ int hist[4][DISPATCH_MAX_E];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < 4 * DISPATCH_MAX_E; e += 256) (&hist[0][0])[e] = 0;
-  __syncthreads();
   const long base = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
   int ids[DISPATCH_WAVE_SLOTS / 64];          // all of this wave's ids in flight at once
 #pragma unroll
@@ -220,6 +263,8 @@ __global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restric
     const long s = base + g * 64 + lane;
     ids[g] = (s < A) ? idx[s] : -1;
   }
+  for (int e = threadIdx.x; e < E; e += 256) hist[0][e] = hist[1][e] = hist[2][e] = hist[3][e] = 0;
+  __syncthreads();
 #pragma unroll
   for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
     int e = ids[g];
@@ -236,6 +281,42 @@ __global__ void __launch_bounds__(256) k_dispatch_count(const int32_t* __restric
         make_int4(hist[0][e], hist[1][e], hist[2][e], hist[3][e]);
 }
 
+// Sums of an expert's per-wave counts, over the int4 groups q0, q0 + dq, ...
+// below nq (one group per chunk): of all of them, and of those of chunks
+// before `me`.  The counts of one expert are contiguous; sixteen int4 loads
+// are in flight at a time.
+__device__ __forceinline__ void expert_count_sums(const int4* __restrict__ c4, int q0, int nq, int dq, int me,
+                                                  int& all, int& before) {
+  all = 0;
+  before = 0;
+  int q = q0;
+  for (; q + 15 * dq < nq; q += 16 * dq) {
+    int4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c4[q + i * dq];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sq = v[i].x + v[i].y + v[i].z + v[i].w;
+      all += sq;
+      before += (q + i * dq < me) ? sq : 0;
+    }
+  }
+  for (; q < nq; q += dq) {
+    const int4 v = c4[q];
+    const int sq = v.x + v.y + v.z + v.w;
+    all += sq;
+    before += (q < me) ? sq : 0;
+  }
+}
+
+// Threads per expert in the scatter's count sums: the largest power of two
+// (at most 64, so a group stays inside one wave) with E * P <= 256, else 1.
+__device__ __forceinline__ int count_parts(int E) {
+  int P = 1;
+  while (P < 64 && 2 * P * E <= 256) P *= 2;
+  return P;
+}
+
 __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restrict__ idx, long A, int E, int k,
                                                           const int32_t* __restrict__ counts, int nsub,
                                                           int32_t* __restrict__ offsets,
@@ -243,45 +324,49 @@ __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restr
                                                           int32_t* __restrict__ row_slot,
                                                           int32_t* __restrict__ slot_row) {
   __shared__ int base[4][DISPATCH_MAX_E];
+  __shared__ int total[DISPATCH_MAX_E];
   __shared__ int red[8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // per-expert totals and the prefix over earlier sub-chunks (4 experts per thread);
-  // counts are expert-major, so each expert's sub-chunk counts are read as int4
-  int tot[4], pre[4][4];
+  const int me = (int)blockIdx.x;
+  // this wave's ids first: their loads overlap the count sums below
+  const long sbase = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
+  int ids[DISPATCH_WAVE_SLOTS / 64];
+#pragma unroll
+  for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
+    const long s = sbase + g * 64 + lane;
+    ids[g] = (s < A) ? idx[s] : -1;
+  }
+  // per expert (P threads each, summing every P-th chunk): its total, and per
+  // wave of this chunk the number of its slots in earlier chunks and earlier
+  // waves (relative to the expert's offset)
+  const int P = count_parts(E);
+  for (int e = threadIdx.x / P; e < E; e += 256 / P) {
+    const int4* c4 = reinterpret_cast<const int4*>(counts + (long)e * nsub);
+    const int4 mine = c4[me];
+    int all, before;
+    expert_count_sums(c4, (int)threadIdx.x % P, nsub / 4, P, me, all, before);
+    for (int o = 1; o < P; o <<= 1) {          // the P threads of an expert are adjacent lanes
+      all += __shfl_xor(all, o, 64);
+      before += __shfl_xor(before, o, 64);
+    }
+    if ((int)threadIdx.x % P == 0) {
+      total[e] = all;
+      base[0][e] = before;
+      base[1][e] = before + mine.x;
+      base[2][e] = before + mine.x + mine.y;
+      base[3][e] = before + mine.x + mine.y + mine.z;
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the totals over experts (4 consecutive experts per thread)
+  int tot[4];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = threadIdx.x * 4 + i;
-    int before = 0, all = 0;
-    int4 mine = make_int4(0, 0, 0, 0);
-    if (e < E) {
-      const int4* c4 = reinterpret_cast<const int4*>(counts + (long)e * nsub);
-      const int nq = nsub / 4;
-      const int me = (int)blockIdx.x;
-      int q = 0;
-      for (; q + 4 <= nq; q += 4) {
-        int4 v0 = c4[q], v1 = c4[q + 1], v2 = c4[q + 2], v3 = c4[q + 3];
-        int s0 = v0.x + v0.y + v0.z + v0.w, s1 = v1.x + v1.y + v1.z + v1.w;
-        int s2 = v2.x + v2.y + v2.z + v2.w, s3 = v3.x + v3.y + v3.z + v3.w;
-        all += s0 + s1 + s2 + s3;
-        before += (q < me ? s0 : 0) + (q + 1 < me ? s1 : 0) + (q + 2 < me ? s2 : 0) + (q + 3 < me ? s3 : 0);
-      }
-      for (; q < nq; ++q) {
-        int4 v = c4[q];
-        int sq = v.x + v.y + v.z + v.w;
-        all += sq;
-        if (q < me) before += sq;
-      }
-      mine = c4[me];
-    }
-    tot[i] = all;
-    pre[i][0] = before;
-    pre[i][1] = before + mine.x;
-    pre[i][2] = before + mine.x + mine.y;
-    pre[i][3] = before + mine.x + mine.y + mine.z;
-    sum += all;
+    tot[i] = (e < E) ? total[e] : 0;
+    sum += tot[i];
   }
-  // exclusive scan of the totals over experts
   int x = sum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -299,21 +384,14 @@ __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restr
     if (e < E) {
       if (blockIdx.x == 0) offsets[e] = ex;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) base[w][e] = ex + pre[i][w];
+      for (int w = 0; w < 4; ++w) base[w][e] += ex;
     }
     ex += tot[i];
   }
   if (blockIdx.x == 0 && threadIdx.x == 255) offsets[E] = ex;
   __syncthreads();
-  // stable scatter of this wave's 1024 slots
-  const long sbase = (long)blockIdx.x * DISPATCH_CHUNK + wave * DISPATCH_WAVE_SLOTS;
+  // stable scatter of this wave's slots
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int ids[DISPATCH_WAVE_SLOTS / 64];
-#pragma unroll
-  for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
-    const long s = sbase + g * 64 + lane;
-    ids[g] = (s < A) ? idx[s] : -1;
-  }
 #pragma unroll
   for (int g = 0; g < DISPATCH_WAVE_SLOTS / 64; ++g) {
     long s = sbase + g * 64 + lane;

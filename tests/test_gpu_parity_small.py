@@ -62,11 +62,17 @@ def test_route_and_dispatch_bit_exact(name):
 
 @pytest.mark.parametrize("name,T,E,k", [("tiny", 64, 8, 2), ("decode", 32, 256, 8), ("decode", 512, 256, 8),
                                          ("decode", 513, 256, 8), ("large_mxfp8", 409, 512, 10),
-                                         ("ties", 97, 1024, 32), ("ties", 1, 3, 3), ("ties", 200, 100, 5)])
+                                         ("ties", 97, 1024, 32), ("ties", 1, 3, 3), ("ties", 200, 100, 5),
+                                         ("ties", 1030, 96, 7), ("ties", 1024, 5, 5), ("ties", 2050, 256, 16),
+                                         ("ties", 1100, 200, 17), ("ties", 1500, 300, 20),
+                                         ("ties", 1200, 700, 9)])
 def test_route_dispatch_shapes_bit_exact(name, T, E, k):
     """Every logits-per-lane width of the router (E up to 64, 128, 256, 512,
-    1024) and both dispatch paths: one workgroup for T*k <= 4096 (all but the
-    513-token case), two-stage otherwise."""
+    1024) with whole-wave token groups (T < 1024), and from 1024 tokens on the
+    16-lane groups (E <= 256, k <= 16: 1, 8 and 16 logits per lane, a partial
+    last wave at T = 1030), 32-lane groups (k > 16 or E > 256) and whole waves
+    (E > 512); both dispatch paths: one workgroup for T*k <= 4096, two-stage
+    otherwise (with 1 to 32 threads per expert in its count sums)."""
     B = _B()
     _say("route+dispatch", name, T, E, k)
     if name == "ties":
