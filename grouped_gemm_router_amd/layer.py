@@ -81,8 +81,9 @@ class MoELayer:
     # -- forward / backward -----------------------------------------------------------
     def forward(self, logits: torch.Tensor, X: torch.Tensor, backward_plan: bool = False, mlp_events=None):
         """Runs route, dispatch, expert MLP and combine on the current stream.
-        ``mlp_events`` = (start, end) torch.cuda.Events recorded around the expert
-        MLP call (same stream as its kernels)."""
+        ``mlp_events`` = (start, end) timing events (objects with ``record()``, such as
+        torch.cuda.Event) recorded around the expert MLP call on the current stream,
+        the stream of its kernels."""
         T = X.shape[0]
         pl = self.plan(T, backward_plan)
         B.route(logits, self.k, pl["topk_idx"], pl["topk_w"])
