@@ -426,7 +426,6 @@ __global__ void __launch_bounds__(64 * DS_WAVES) k_dispatch_small(
   __shared__ int hist[DS_WAVES][DISPATCH_MAX_E];
   __shared__ int red[DS_WAVES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < DS_WAVES * DISPATCH_MAX_E; i += 64 * DS_WAVES) (&hist[0][0])[i] = 0;
   const int per = ((A + DS_WAVES - 1) / DS_WAVES + 63) / 64 * 64;     // slots per wave, whole groups of 64
   const int s0 = wave * per;
   int ids[DISPATCH_SMALL_A / DS_WAVES / 64];
@@ -436,6 +435,9 @@ __global__ void __launch_bounds__(64 * DS_WAVES) k_dispatch_small(
     int e = (g * 64 < per && s < A) ? idx[s] : -1;
     ids[g] = (e >= 0 && e < E) ? e : 0x400;                           // out-of-range ids are skipped
   }
+  for (int e = threadIdx.x; e < E; e += 64 * DS_WAVES)                // only the columns of real experts
+#pragma unroll
+    for (int w = 0; w < DS_WAVES; ++w) hist[w][e] = 0;
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < DISPATCH_SMALL_A / DS_WAVES / 64; ++g) {
@@ -444,11 +446,16 @@ __global__ void __launch_bounds__(64 * DS_WAVES) k_dispatch_small(
     if (key < 0x400 && (m >> lane) == 1ull) hist[wave][key] += __popcll(m);
   }
   __syncthreads();
-  // thread e: total of expert e, exclusive scan over experts, per-wave bases
+  // thread e: total of expert e, exclusive scan over experts, per-wave bases (the
+  // expert's DS_WAVES counts are read once into registers)
   const int e = threadIdx.x;
+  int cnt[DS_WAVES];
   int tot = 0;
-  if (e < E)
-    for (int w = 0; w < DS_WAVES; ++w) tot += hist[w][e];
+#pragma unroll
+  for (int w = 0; w < DS_WAVES; ++w) {
+    cnt[w] = (e < E) ? hist[w][e] : 0;
+    tot += cnt[w];
+  }
   int x = tot;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -463,10 +470,10 @@ __global__ void __launch_bounds__(64 * DS_WAVES) k_dispatch_small(
     offsets[e] = ex;
     if (e == E - 1) offsets[E] = ex + tot;
     int run = ex;
+#pragma unroll
     for (int w = 0; w < DS_WAVES; ++w) {
-      const int c = hist[w][e];
       hist[w][e] = run;
-      run += c;
+      run += cnt[w];
     }
   }
   __syncthreads();
