@@ -202,3 +202,13 @@ def test_row_offset_limits():
     assert B.validate_problem(B.problem(2 ** 20, 2048, 64, 64, 1)) == 2           # T*H = 2^31
     assert B.validate_problem(B.problem(2 ** 18, 256, 1024, 64, 4)) == 2          # T*k*I = 2^30
     assert B.validate_problem(B.problem(2 ** 18, 256, 512, 64, 4)) == 0           # T*k*I = 2^29
+
+
+def test_bench_refuses_several_gpus(monkeypatch, capsys):
+    """bench.py measures one GPU: any other --gpus exits with status 2 and a
+    message, before touching a device."""
+    import sys
+    import bench
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    assert "one GPU" in capsys.readouterr().err
