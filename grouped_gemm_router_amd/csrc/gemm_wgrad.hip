@@ -338,6 +338,9 @@ __global__ void __launch_bounds__(CfgWgGateUp::NT) k_bwd_dw_gateup(const GemmArg
 
 // Expert-major operand rows of the weight-gradient GEMMs, one wave per row r:
 // Xg[r] = X[token], dO[r] = bf16(w * dY[token]) (w = the row's top-k weight).
+constexpr int GATHER_UNROLL = 8;    // 16-byte chunks of a row per lane and batch (H = 4096: the whole row)
+typedef uint32_t gather_u4 __attribute__((ext_vector_type(4)));   // a register value (uint4 arrays go to scratch)
+
 __global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
   const long A = (long)p.T * p.k;
   const int chunks = p.H / 8;
@@ -345,19 +348,35 @@ __global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
   for (long r = blockIdx.x * 4L + (threadIdx.x >> 6); r < A; r += gridDim.x * 4L) {
     const int tok = p.row_token[r];
     const float w = p.topk_w[p.row_slot[r]];
-    const uint4* x = reinterpret_cast<const uint4*>(p.X + (size_t)tok * p.H);
-    const uint4* dy = reinterpret_cast<const uint4*>(p.dY + (size_t)tok * p.H);
-    uint4* xg = reinterpret_cast<uint4*>(p.Xg + (size_t)r * p.H);
-    uint4* dO = reinterpret_cast<uint4*>(p.dO + (size_t)r * p.H);
-    for (int c = lane; c < chunks; c += 64) {
-      xg[c] = x[c];
-      const uint4 v = dy[c];
-      uint4 o;
-      o.x = pack_bf16x2(w * bf16_to_f32(v.x & 0xffffu), w * bf16_to_f32(v.x >> 16));
-      o.y = pack_bf16x2(w * bf16_to_f32(v.y & 0xffffu), w * bf16_to_f32(v.y >> 16));
-      o.z = pack_bf16x2(w * bf16_to_f32(v.z & 0xffffu), w * bf16_to_f32(v.z >> 16));
-      o.w = pack_bf16x2(w * bf16_to_f32(v.w & 0xffffu), w * bf16_to_f32(v.w >> 16));
-      dO[c] = o;
+    const gather_u4* x = reinterpret_cast<const gather_u4*>(p.X + (size_t)tok * p.H);
+    const gather_u4* dy = reinterpret_cast<const gather_u4*>(p.dY + (size_t)tok * p.H);
+    gather_u4* xg = reinterpret_cast<gather_u4*>(p.Xg + (size_t)r * p.H);
+    gather_u4* dO = reinterpret_cast<gather_u4*>(p.dO + (size_t)r * p.H);
+    // GATHER_UNROLL chunks of both rows per lane in flight before any store
+    for (int c0 = 0; c0 < chunks; c0 += 64 * GATHER_UNROLL) {
+      gather_u4 xv[GATHER_UNROLL], dv[GATHER_UNROLL];
+#pragma unroll
+      for (int u = 0; u < GATHER_UNROLL; ++u) {
+        const int c = c0 + u * 64 + lane;
+        const int cc = c < chunks ? c : 0;          // in-bounds reads for lanes past the row
+        xv[u] = x[cc];
+        dv[u] = dy[cc];
+      }
+#pragma unroll
+      for (int u = 0; u < GATHER_UNROLL; ++u) {
+        // a lane past the row stores chunk 0 again, with the values lane 0 stores there: no
+        // branch around the stores
+        const int c = c0 + u * 64 + lane;
+        const int cc = c < chunks ? c : 0;
+        const gather_u4 v = dv[u];
+        gather_u4 o;
+        o.x = pack_bf16x2(w * bf16_to_f32(v.x & 0xffffu), w * bf16_to_f32(v.x >> 16));
+        o.y = pack_bf16x2(w * bf16_to_f32(v.y & 0xffffu), w * bf16_to_f32(v.y >> 16));
+        o.z = pack_bf16x2(w * bf16_to_f32(v.z & 0xffffu), w * bf16_to_f32(v.z >> 16));
+        o.w = pack_bf16x2(w * bf16_to_f32(v.w & 0xffffu), w * bf16_to_f32(v.w >> 16));
+        xg[cc] = xv[u];
+        dO[cc] = o;
+      }
     }
   }
 }
