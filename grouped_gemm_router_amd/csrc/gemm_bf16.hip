@@ -535,12 +535,11 @@ hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
 }
 // dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials.
 // One wave per (token, slice of 64 chunks of 8 fp32): the token's row indices are
-// wave-uniform, each lane issues the loads of four rows before it adds them (ascending j),
-// and the fp32 rows, read once, are loaded with the nontemporal hint.
+// wave-uniform, each lane issues the loads of four rows before it adds them (ascending j).
+// The fp32 rows take plain cached loads: part of them, just written by the dX-rows GEMM,
+// still sits in the caches (the nontemporal hint measured 10% slower on the training shape).
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4v load_nt_f32x4(const float* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(ptr));
-}
+__device__ __forceinline__ f32x4v load_f32x4(const float* ptr) { return *reinterpret_cast<const f32x4v*>(ptr); }
 __device__ __forceinline__ void add8(float (&acc)[8], const f32x4v& a, const f32x4v& b) {
   acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
   acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
@@ -566,8 +565,8 @@ __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, cons
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float* src = p.dXr + (size_t)sr[j + q] * p.H + cc * 8;
-        v[q][0] = load_nt_f32x4(src);
-        v[q][1] = load_nt_f32x4(src + 4);
+        v[q][0] = load_f32x4(src);
+        v[q][1] = load_f32x4(src + 4);
       }
       __builtin_amdgcn_sched_barrier(0);           // all eight loads in flight before the adds
 #pragma unroll
@@ -575,7 +574,7 @@ __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, cons
     }
     for (; j < p.k; ++j) {
       const float* src = p.dXr + (size_t)sr[j] * p.H + cc * 8;
-      add8(acc, load_nt_f32x4(src), load_nt_f32x4(src + 4));
+      add8(acc, load_f32x4(src), load_f32x4(src + 4));
     }
     if (has) {
       uint4 o;
@@ -599,7 +598,7 @@ hipError_t launch_bwd_token_reduce(const GemmArgs& a, const int32_t* slot_row, u
                                    float* dtw, hipStream_t s) {
   const long units = (long)a.T * ((a.H / 8 + 63) / 64);
   long blocks = (units + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > 16384) blocks = 16384;                // one unit per wave up to 8192 tokens of H = 4096
   hipLaunchKernelGGL(k_bwd_token_reduce, dim3((int)blocks), dim3(256), 0, s, a, slot_row, dX, dtw);
   return hipGetLastError();
 }
