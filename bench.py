@@ -6,15 +6,26 @@ input: routing, dispatch, the grouped-GEMM expert MLP (gate/up + SwiGLU,
 down) and the weighted combine; for the training workload also the backward
 (expert MLP and router).
 Inputs are resident in HBM before the timed region; weight packing happens at
-load time, outside it.  The timed region (the reported value) does not flush
-caches between steps; its per-step times give p10 / p50 / p90.  With
---cold-cache a second pass reads 512 MiB before every step, which evicts L2
+load time, outside it.
+
+Per workload, three passes over the same steps follow the warmup:
+  * the timed region (``ms_per_step``, ``value``): K steps with one timing event
+    on each side only (every recorded event leaves the GPU idle for a few
+    microseconds, so none sits between the steps);
+  * the roofline pass: K steps with HIP events around the expert-MLP call (and,
+    for training, around the backward call) on the stream its kernels run on,
+    giving the calls' average launch durations;
+  * the spread pass: K steps with one event between steps (p10 / p50 / p90).
+With --cold-cache a fourth pass reads 512 MiB before every step, which evicts L2
 and the Infinity Cache (and leaves clean lines, so the step pays no write-back
 of the flush), and times each step on its own (reported under cold_cache).
 
 Prints one JSON line.  Default workload: prefill (T=4096 tokens, hidden 2048,
-intermediate 512, 256 experts, top-8, bf16).  Other workloads (--workload
-decode | train | large_mxfp8 | tiny | prefill_rankzipf) are for diagnostics.
+intermediate 512, 256 experts, top-8, bf16); its line also carries a
+``configs`` block with the decode, large MXFP8 and training workloads measured
+the same way (each with its own roofline).  Other workloads (--workload decode
+| train | large_mxfp8 | tiny | prefill_rankzipf | model-contract shapes) are for
+diagnostics.
 """
 from __future__ import annotations
 
@@ -31,9 +42,10 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 FLUSH_BYTES = 512 << 20        # read before each cold-cache step: more than L2 (8 x 4 MB) + Infinity Cache (256 MB)
+EXTRA_CONFIGS = ("decode", "large_mxfp8", "train")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -43,39 +55,42 @@ def parse():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count T (sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="prefill only: leave out the decode / large MXFP8 / training block")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the warmup, copy 1 GiB device to device three times (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def recorded_traffic(workload):
     """HBM bytes of one moe_expert_mlp call from the committed counter runs, or None when there are
     none for this workload or the library sources changed since they were taken."""
-    from grouped_gemm_router_amd import profile_tools as pt
+    import bench_tools as bt
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha") != pt.source_hash(workload):
+    if rec.get("source_sha") != bt.source_hash(workload):
         return None
     return int(rec["traffic_bytes"])
 
 
-def device_weights(cfg, name, experts=None):
+def device_weights(cfg, name, experts=None, device_draw=False):
     """All experts' [E, K, N] bf16 weights on the device (experts not listed hold NaN).  Below 2^31
-    elements they are the seeded numpy draws the tests use; larger sets (the big expert shapes) are
-    drawn on the device from a seeded torch generator, N(0, 1/K) like the numpy ones, because the
-    host draw would take minutes.  Timing does not depend on the values."""
+    elements they are the seeded numpy draws the tests use, unless ``device_draw``; larger sets (the
+    big expert shapes) and device draws come from a seeded torch generator on the device, N(0, 1/K)
+    like the numpy ones, because the host draw would take minutes.  Timing does not depend on the
+    values."""
     import torch
     from concurrent.futures import ThreadPoolExecutor
     from grouped_gemm_router_amd import workloads as wl
     K, N = wl.weight_shape(cfg, name)
     out = torch.full((cfg.E, K, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     todo = range(cfg.E) if experts is None else sorted(set(int(e) for e in experts))
-    if cfg.E * K * N >= 2 ** 31:
+    if device_draw or cfg.E * K * N >= 2 ** 31:
         g = torch.Generator(device="cuda")
         g.manual_seed(cfg.seed * 16 + ("gate", "up", "down").index(name))
         for e in todo:
@@ -94,6 +109,18 @@ def step_flops(cfg, active_rows):
     fwd = 2.0 * m * A * H * I
     bwd = 4.0 * m * A * H * I if cfg.backward else 0.0
     return fwd, bwd
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(cfg, logits, X, dY, min_s=10.0, max_reps=20):
@@ -134,23 +161,33 @@ def cpu_baseline(cfg, logits, X, dY, min_s=10.0, max_reps=20):
     t_mlp /= reps
     f_fwd, f_bwd = step_flops(cfg, ntok * cfg.k)
     return {"value": round((f_fwd + f_bwd) / t_mlp / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "tokens_per_s": round(ntok / (t_mlp + t_route * ntok / cfg.T), 2),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "tokens_per_s": round(ntok / (t_mlp + t_route * ntok / cfg.T), 2),
             "sample": f"float64 numpy oracle, mean of {reps} runs: routing+dispatch of all {cfg.T} tokens "
                       f"({t_route:.3f} s) and the expert MLP + combine{' + backward' if cfg.backward else ''} "
                       f"of {ntok} sampled tokens ({t_mlp:.3f} s); TFLOP/s counts the sampled tokens' work"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer runs every "
-              "expert on one MI355X; see the design notes for how it would shard).", file=sys.stderr)
-        return 2
+def _roofline(kernel, flops, nbytes, ms, peak_tflops, traffic=None):
+    """Roofline of one call: the bound is the roofline with the longer time at peak."""
+    if nbytes / (PEAK_HBM_GBPS * 1e9) > flops / (peak_tflops * 1e12):
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(ms, 5)}
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tflops,
+            "unit": "TFLOP/s", "frac": round(achieved / peak_tflops, 4), "traffic": traffic,
+            "avg_launch_ms": round(ms, 5)}
+
+
+def measure(cfg, args, device_draw=False):
+    """Runs the workload (warmup, timed region, roofline pass, spread pass, optional cold-cache
+    pass) and returns its record; ``_inputs`` holds the host inputs for the CPU baseline."""
     import torch
     from grouped_gemm_router_amd import workloads as wl
     from grouped_gemm_router_amd.layer import MoELayer
 
-    cfg = wl.config(args.workload) if args.tokens is None else wl.config(args.workload, T=args.tokens)
     logits_np, X_np = wl.make_logits(cfg), wl.make_x(cfg)
     dY_np = wl.make_dy(cfg) if cfg.backward else None
     full_weights = cfg.E * cfg.H * cfg.I <= 128 * 4096 * 1024
@@ -161,22 +198,27 @@ def main():
         from grouped_gemm_router_amd import binding as B
         idx, _ = B.route(torch.from_numpy(logits_np).cuda(), cfg.k)
         experts = torch.unique(idx).cpu().numpy()
-    W = {n: device_weights(cfg, n, experts) for n in cfg.mats}
+    W = {n: device_weights(cfg, n, experts, device_draw) for n in cfg.mats}
     logits = torch.from_numpy(logits_np).cuda()
     X = torch.from_numpy(X_np.view(np.int16)).cuda().view(torch.bfloat16)
     dY = torch.from_numpy(dY_np.view(np.int16)).cuda().view(torch.bfloat16) if cfg.backward else None
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation,
                      act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"], keep_math=cfg.backward)
+    del W
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        layer.forward(logits, X, backward_plan=cfg.backward, mlp_events=ev)
+    def step(mlp_ev=None, bwd_ev=None):
+        layer.forward(logits, X, backward_plan=cfg.backward, mlp_events=mlp_ev)
         if cfg.backward:
+            if bwd_ev is not None:
+                bwd_ev[0].record()
             layer.backward(X, dY)
+            if bwd_ev is not None:
+                bwd_ev[1].record()
             layer.route_backward(cfg.T)
 
     if args.copy_calibration:
-        from grouped_gemm_router_amd.profile_tools import COPY_BYTES
+        from bench_tools import COPY_BYTES
         src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -193,31 +235,38 @@ def main():
             step()
         graph.replay()
         torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    # The timed region records the expert-MLP call's events (the roofline's launch time) and
-    # one event on each side; every timing event leaves the GPU idle for a few microseconds, so
-    # the per-step spread comes from a second pass with an event between steps.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: K steps, one event on each side
+    t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
-    for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step(evs[i])
+    for _ in range(args.steps):
+        run()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t_start.elapsed_time(t_end) / args.steps
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]   # step boundaries
+
+    # roofline pass: events around the expert-MLP call (and the backward call) of every step
+    mlp_ms = bwd_ms = None
+    if graph is None:
+        mlp_evs = [(ev(), ev()) for _ in range(args.steps)]
+        bwd_evs = [(ev(), ev()) for _ in range(args.steps)] if cfg.backward else [None] * args.steps
+        for i in range(args.steps):
+            step(mlp_evs[i], bwd_evs[i])
+        torch.cuda.synchronize()
+        mlp_ms = float(np.mean([a.elapsed_time(b) for a, b in mlp_evs]))
+        if cfg.backward:
+            bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_evs]))
+
+    # spread pass: one event between steps
+    marks = [ev() for _ in range(args.steps + 1)]
     marks[0].record()
     for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
+        run()
         marks[i + 1].record()
     torch.cuda.synchronize()
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
@@ -227,76 +276,110 @@ def main():
         # 512 MiB read before each step (its lines replace everything cached), each step timed alone
         flush = torch.full((FLUSH_BYTES // 4,), 1.0, dtype=torch.float32, device="cuda")
         n_cold = min(args.steps, 20)
-        cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+        cold = [(ev(), ev()) for _ in range(n_cold)]
         for i in range(n_cold):
             torch.amax(flush)
             cold[i][0].record()
-            if graph is not None:
-                graph.replay()
-            else:
-                step()
+            run()
             cold[i][1].record()
         torch.cuda.synchronize()
         cold_ms = np.array([a.elapsed_time(b) for a, b in cold])
         del flush
 
     pl = layer.plan(cfg.T, cfg.backward)
-    offsets = pl["offsets"].cpu().numpy()
-    n_active = int(np.count_nonzero(np.diff(offsets)))
+    n_active = int(np.count_nonzero(np.diff(pl["offsets"].cpu().numpy())))
+    del layer, pl
+    torch.cuda.empty_cache()
+
     f_fwd, f_bwd = step_flops(cfg, cfg.A)
     tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if cfg.dtype == "mxfp8" else PEAK_BF16_TFLOPS
     wbytes = 1 if cfg.dtype == "mxfp8" else 2
     weight_bytes = n_active * len(cfg.mats) * cfg.H * cfg.I * wbytes
-    act_bytes = cfg.T * cfg.E * 4 + cfg.T * cfg.H * 2 * 2
+    act_bytes = cfg.T * cfg.E * 4 + cfg.T * cfg.H * 2 * 2          # logits, X, Y
+    if cfg.backward:
+        # dY and dX, the weight gradients of the active experts, d_topk_w and d_logits
+        act_bytes += cfg.T * cfg.H * 2 * 2 + n_active * len(cfg.mats) * cfg.H * cfg.I * 2 + cfg.T * cfg.E * 4
+    rec = {
+        "workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
+        "top_k": cfg.k, "active_experts": n_active, "backward": cfg.backward,
+        "activation": cfg.activation if not cfg.act_limit else f"{cfg.activation}({cfg.act_limit:g})",
+        "dtype": "mxfp8" if cfg.dtype == "mxfp8" else "bf16",
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "value": round(tflops, 3), "unit": "TFLOP/s",
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "frac_of_mfma_peak": round(tflops / peak, 4),
+        "hbm_GBps_algorithmic": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes": int(weight_bytes + act_bytes),
+        "wall_s_timed_region": round(wall, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
+        "graph": bool(args.graph),
+        "_inputs": (logits_np, X_np, dY_np),
+    }
+    if cold_ms is not None:
+        rec["cold_cache"] = {"flush_bytes": FLUSH_BYTES, "steps": int(cold_ms.size),
+                             "step_ms_p10_p50_p90": [round(float(np.percentile(cold_ms, q)), 5) for q in (10, 50, 90)],
+                             "value_at_p50": round((f_fwd + f_bwd) / (float(np.median(cold_ms)) * 1e-3) / 1e12, 3)}
+    if mlp_ms is not None:
+        # algorithmic bytes of one expert-MLP call: the active experts' weights once, X rows in and
+        # h rows out (gate/up), h rows in and O rows out (down)
+        mlp_bytes = weight_bytes + cfg.A * (cfg.H + cfg.I) * 2 * 2
+        rec["roofline"] = _roofline("moe_expert_mlp (gate/up+activation and down grouped GEMMs)", f_fwd,
+                                    mlp_bytes, mlp_ms, peak, recorded_traffic(cfg.name))
+    if bwd_ms is not None:
+        # algorithmic bytes of one backward call: dY and X rows, the weights, h (recomputed) and the
+        # weight gradients of the active experts, dX
+        bwd_bytes = 2 * weight_bytes + cfg.T * cfg.H * 2 * 3
+        rec["backward_roofline"] = _roofline("moe_backward (P, recompute, dX rows, token reduce, weight "
+                                             "gradients)", f_bwd, bwd_bytes, bwd_ms, peak)
+    return rec
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer runs every "
+              "expert on one MI355X; see the design notes for how it would shard).", file=sys.stderr)
+        return 2
+    from grouped_gemm_router_amd import workloads as wl
+
+    cfg = wl.config(args.workload) if args.tokens is None else wl.config(args.workload, T=args.tokens)
+    rec = measure(cfg, args)
+    logits_np, X_np, dY_np = rec.pop("_inputs")
     out = {
         "metric": METRIC,
-        "value": round(tflops, 3),
+        "value": rec["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if cfg.dtype == "mxfp8" else "bf16",
+        "dtype": rec["dtype"],
         "data": "synthetic (seeded numpy draws; shapes and routing skew of the workload)",
-        "config": {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
-                   "top_k": cfg.k, "active_experts": n_active, "backward": cfg.backward,
-                   "activation": cfg.activation if not cfg.act_limit else f"{cfg.activation}({cfg.act_limit:g})",
-                   "graph": bool(args.graph)},
-        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
-        "frac_of_mfma_peak": round(tflops / peak, 4),
-        "hbm_GBps_algorithmic": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1),
-        "wall_s_timed_region": round(wall, 4),
-        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],   # second pass
+        "config": {k: rec[k] for k in ("workload", "T", "hidden", "intermediate", "experts", "top_k",
+                                       "active_experts", "backward", "activation", "graph")},
     }
-    if cold_ms is not None:
-        out["cold_cache"] = {"flush_bytes": FLUSH_BYTES, "steps": int(cold_ms.size),
-                             "step_ms_p10_p50_p90": [round(float(np.percentile(cold_ms, q)), 5) for q in (10, 50, 90)],
-                             "value_at_p50": round((f_fwd + f_bwd) / (float(np.median(cold_ms)) * 1e-3) / 1e12, 3)}
-    if graph is None:
-        mlp_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        mlp_flops = step_flops(cfg, cfg.A)[0]
-        # algorithmic bytes of one call: the active experts' weights once, X rows in and h rows
-        # out (gate/up), h rows in and O rows out (down)
-        mlp_bytes = weight_bytes + cfg.A * (cfg.H + cfg.I) * 2 * 2
-        # the roofline that bounds the call is the one with the longer time at peak
-        if mlp_bytes / (PEAK_HBM_GBPS * 1e9) > mlp_flops / (peak * 1e12):
-            achieved = mlp_bytes / (mlp_ms * 1e-3) / 1e9
-            out["roofline"] = {"kernel": "moe_expert_mlp (gate/up+activation and down)", "bound": "hbm",
-                               "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                               "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": recorded_traffic(cfg.name),
-                               "avg_launch_ms": round(mlp_ms, 5)}
-        else:
-            achieved = mlp_flops / (mlp_ms * 1e-3) / 1e12
-            out["roofline"] = {"kernel": "moe_expert_mlp (gate/up+activation and down grouped GEMMs)",
-                               "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                               "frac": round(achieved / peak, 4), "traffic": recorded_traffic(cfg.name),
-                               "avg_launch_ms": round(mlp_ms, 5)}
+    for k in ("tokens_per_s", "frac_of_mfma_peak", "hbm_GBps_algorithmic", "wall_s_timed_region",
+              "step_ms_p10_p50_p90", "cold_cache", "roofline", "backward_roofline"):
+        if k in rec:
+            out[k] = rec[k]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, logits_np, X_np, dY_np)
+    del logits_np, X_np, dY_np
+    if args.workload == "prefill" and args.tokens is None and not args.no_configs:
+        # the other workloads, measured the same way, with weights drawn on the device
+        configs = {}
+        for name in EXTRA_CONFIGS:
+            r = measure(wl.config(name), args, device_draw=True)
+            r.pop("_inputs")
+            r.pop("steps")
+            r.pop("warmup")
+            configs[name] = r
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
     return 0
 

@@ -2,17 +2,17 @@
 
 Usage (from the repository root, after the profiling runs):
 
-  python -m grouped_gemm_router_amd.profile_tools stats <rocprof-dir> <out.md> --cmd "<command>" --title "<title>"
+  python bench_tools.py stats <rocprof-dir> <out.md> --cmd "<command>" --title "<title>"
       kernel table (calls, average / min / max duration, share of GPU time) from
       <rocprof-dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace --stats --output-format csv -o run)
 
-  python -m grouped_gemm_router_amd.profile_tools traffic --fetch <dir> --write <dir> --workload <name> \\
+  python bench_tools.py traffic --fetch <dir> --write <dir> --workload <name> \\
       --out <traffic.json> [--md <out.md>] [--cmd-fetch "<command>"] [--cmd-write "<command>"]
       HBM traffic of one moe_expert_mlp call from two counter runs (rocprofv3 --pmc FETCH_SIZE,
       then --pmc WRITE_SIZE, --output-format csv -o run) of ``bench.py --copy-calibration``.  Each
       counter is scaled by what it reads for the calibration copy of a known number of bytes.
 
-  python -m grouped_gemm_router_amd.profile_tools mfma --pmc <dir> --stats <dir> --out <out.md> --cmd-pmc "<command>" \
+  python bench_tools.py mfma --pmc <dir> --stats <dir> --out <out.md> --cmd-pmc "<command>" \
       --cmd-stats "<command>" --title "<title>"
       MFMA utilisation per kernel from one counter run (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
       SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE) and the kernel
@@ -33,8 +33,8 @@ import json
 import os
 import sys
 
-PKG = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(PKG)
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.join(ROOT, "grouped_gemm_router_amd")
 COPY_BYTES = 1 << 30                    # bytes moved by bench.py --copy-calibration per copy
 COPY_KERNEL = "copyBuffer"              # the HIP runtime's device-to-device copy kernel
 MLP_KERNELS = {                         # kernels of one moe_expert_mlp call, per workload kind

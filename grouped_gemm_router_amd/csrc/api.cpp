@@ -56,7 +56,7 @@ size_t bwd_ws(const moe_problem* p) {
   const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
   const size_t nparts = moe::bwd_nparts(p->I, p->activation);
   return align_up(A * I * 4) + 2 * align_up(A * 2 * I * 2) + align_up(A * I * 2) + align_up(A * H * 4) +
-         align_up(A * nparts * 4);
+         align_up(A * H * 2) + align_up(A * nparts * 4);
 }
 
 // Device check, cached per device id.
@@ -338,6 +338,8 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   a.Xg = (uint16_t*)w8;
   a.dO = (uint16_t*)(w8 + A * H * 2);
   w8 += align_up(A * H * 4);
+  a.dO_lo = (uint16_t*)w8;
+  w8 += align_up(A * H * 2);
   a.dwt_part = (float*)w8;
   a.dWg = (uint16_t*)dW_gate;
   a.dWu = (uint16_t*)dW_up;

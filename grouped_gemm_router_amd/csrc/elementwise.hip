@@ -34,7 +34,8 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&a)[8]) {
 
 // One wave per (token, slice of 128 16-byte chunks): the token's k row indices and weights
 // are wave-uniform (scalar loads), and each lane sums two chunks, issuing the loads of four
-// rows for both before it adds them.
+// rows for both before it adds them.  A slot whose row index is negative (dispatch skipped an
+// out-of-range expert id) adds nothing (row 0 is loaded in its place, never added).
 constexpr int COMBINE_SLICE = 128;          // chunks of 8 bf16 per wave unit (two per lane)
 
 __global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ O, const int32_t* __restrict__ slot_row,
@@ -56,21 +57,26 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ O,
     int j = 0;
     for (; j + 4 <= k; j += 4) {
       uint4 v0[4], v1[4];
+      int rr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint16_t* row = O + (size_t)sr[j + q] * H;
+        rr[q] = sr[j + q];
+        const uint16_t* row = O + (size_t)max(rr[q], 0) * H;
         v0[q] = load_nt(row + cc0 * 8);
         v1[q] = load_nt(row + cc1 * 8);
       }
       __builtin_amdgcn_sched_barrier(0);           // all eight loads in flight before the adds
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if (rr[q] < 0) continue;
         combine_add(a0, wt[j + q], v0[q]);
         combine_add(a1, wt[j + q], v1[q]);
       }
     }
     for (; j < k; ++j) {
-      const uint16_t* row = O + (size_t)sr[j] * H;
+      const int r = sr[j];
+      if (r < 0) continue;
+      const uint16_t* row = O + (size_t)r * H;
       combine_add(a0, wt[j], load_nt(row + cc0 * 8));
       combine_add(a1, wt[j], load_nt(row + cc1 * 8));
     }

@@ -533,7 +533,8 @@ hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
                      dim3(CfgRows::NT), 0, s, a);
   return hipGetLastError();
 }
-// dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials.
+// dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials (slots
+// without a row, slot_row < 0, add nothing and get d_topk_w = 0).
 // One wave per (token, slice of 64 chunks of 8 fp32): the token's row indices are
 // wave-uniform, each lane issues the loads of four rows before it adds them (ascending j).
 // The fp32 rows take plain cached loads: part of them, just written by the dX-rows GEMM,
@@ -562,18 +563,23 @@ __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, cons
     int j = 0;
     for (; j + 4 <= p.k; j += 4) {
       f32x4v v[4][2];
+      int rr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float* src = p.dXr + (size_t)sr[j + q] * p.H + cc * 8;
+        rr[q] = sr[j + q];
+        const float* src = p.dXr + (size_t)max(rr[q], 0) * p.H + cc * 8;
         v[q][0] = load_f32x4(src);
         v[q][1] = load_f32x4(src + 4);
       }
       __builtin_amdgcn_sched_barrier(0);           // all eight loads in flight before the adds
 #pragma unroll
-      for (int q = 0; q < 4; ++q) add8(acc, v[q][0], v[q][1]);
+      for (int q = 0; q < 4; ++q)
+        if (rr[q] >= 0) add8(acc, v[q][0], v[q][1]);
     }
     for (; j < p.k; ++j) {
-      const float* src = p.dXr + (size_t)sr[j] * p.H + cc * 8;
+      const int r = sr[j];
+      if (r < 0) continue;
+      const float* src = p.dXr + (size_t)r * p.H + cc * 8;
       add8(acc, load_f32x4(src), load_f32x4(src + 4));
     }
     if (has) {
@@ -588,7 +594,7 @@ __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, cons
     if (sl == 0 && lane < p.k) {
       const int r = sr[lane];
       float s = 0.f;
-      for (int q = 0; q < p.nparts; ++q) s += p.dwt_part[(size_t)r * p.nparts + q];
+      for (int q = 0; r >= 0 && q < p.nparts; ++q) s += p.dwt_part[(size_t)r * p.nparts + q];
       dtw[t * p.k + lane] = s;
     }
   }

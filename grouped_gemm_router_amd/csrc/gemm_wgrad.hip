@@ -42,10 +42,10 @@ struct WgCfg {
   static constexpr int STAGE = A_SLOTS + NB * B_SLOTS;
   static_assert(BK % 16 == 0 && NST * STAGE * 16 <= 150 * 1024, "k-tile and LDS budget");
 };
-// 32-row k-tiles and three stages (two k-tiles in flight).  dW_down: 32 KB stages.
-// dW_gate/up: the x k-tile is shared by the bf16 values and the bf16 remainders
-// of [dg | du]: 48 KB stages.
-using CfgWgDown = WgCfg<256, 256, 2, 4, 32, 3, 1>;
+// 32-row k-tiles and three stages (two k-tiles in flight), 48 KB each: the A k-tile is
+// shared by the bf16 values and the bf16 remainders of the B operand (dO for dW_down,
+// [dg | du] for dW_gate/up), so that the exact value reaches the fp32 sums to about 2^-16.
+using CfgWgDown = WgCfg<256, 256, 2, 4, 32, 3, 2>;
 using CfgWgGateUp = WgCfg<256, 256, 2, 4, 32, 3, 2>;
 
 // Chunk position in a k-major LDS row: chunk c of row r sits at c ^ tr_swz(r).
@@ -290,14 +290,15 @@ __device__ __forceinline__ void wg_store(uint8_t* wlds, uint16_t* out, int ld, i
       [](int fn, int q) { return fn * 32 + q * 8; });
 }
 
-// dW_down[e] = sum_r h_r^T dO_r: A = h rows [A, I], B = dO rows [A, H].
+// dW_down[e] = sum_r h_r^T dO_r with dO_r = w_r dY[t_r]: A = h rows [A, I], B = dO rows [A, H]
+// as bf16 values (nb = 0) and bf16 remainders (nb = 1).
 struct WgDownOps {
   __device__ static int M(const GemmArgs& p) { return p.I; }
   __device__ static int N(const GemmArgs& p) { return p.H; }
   __device__ static int lda(const GemmArgs& p) { return p.I; }
   __device__ static int ldb(const GemmArgs& p) { return p.H; }
   __device__ static const uint16_t* a_rows(const GemmArgs& p) { return p.Hrows; }
-  __device__ static const uint16_t* b_rows(const GemmArgs& p, int) { return p.dO; }
+  __device__ static const uint16_t* b_rows(const GemmArgs& p, int nb) { return nb ? p.dO_lo : p.dO; }
   template <class C>
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
                                   int lane, uint8_t* wlds) {
@@ -337,12 +338,13 @@ __global__ void __launch_bounds__(CfgWgGateUp::NT) k_bwd_dw_gateup(const GemmArg
 }
 
 // Expert-major operand rows of the weight-gradient GEMMs, one wave per row r:
-// Xg[r] = X[token], dO[r] = bf16(w * dY[token]) (w = the row's top-k weight).
+// Xg[r] = X[token], dO[r] = bf16(w * dY[token]) and dO_lo[r] = bf16(w * dY[token] - dO[r])
+// (w = the row's top-k weight).  Rows past the last expert's (expert_offsets[E]) have no token.
 constexpr int GATHER_UNROLL = 8;    // 16-byte chunks of a row per lane and batch (H = 4096: the whole row)
 typedef uint32_t gather_u4 __attribute__((ext_vector_type(4)));   // a register value (uint4 arrays go to scratch)
 
 __global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
-  const long A = (long)p.T * p.k;
+  const long A = p.offsets[p.E];
   const int chunks = p.H / 8;
   const int lane = threadIdx.x & 63;
   for (long r = blockIdx.x * 4L + (threadIdx.x >> 6); r < A; r += gridDim.x * 4L) {
@@ -352,6 +354,7 @@ __global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
     const gather_u4* dy = reinterpret_cast<const gather_u4*>(p.dY + (size_t)tok * p.H);
     gather_u4* xg = reinterpret_cast<gather_u4*>(p.Xg + (size_t)r * p.H);
     gather_u4* dO = reinterpret_cast<gather_u4*>(p.dO + (size_t)r * p.H);
+    gather_u4* dOl = reinterpret_cast<gather_u4*>(p.dO_lo + (size_t)r * p.H);
     // GATHER_UNROLL chunks of both rows per lane in flight before any store
     for (int c0 = 0; c0 < chunks; c0 += 64 * GATHER_UNROLL) {
       gather_u4 xv[GATHER_UNROLL], dv[GATHER_UNROLL];
@@ -369,13 +372,17 @@ __global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
         const int c = c0 + u * 64 + lane;
         const int cc = c < chunks ? c : 0;
         const gather_u4 v = dv[u];
-        gather_u4 o;
-        o.x = pack_bf16x2(w * bf16_to_f32(v.x & 0xffffu), w * bf16_to_f32(v.x >> 16));
-        o.y = pack_bf16x2(w * bf16_to_f32(v.y & 0xffffu), w * bf16_to_f32(v.y >> 16));
-        o.z = pack_bf16x2(w * bf16_to_f32(v.z & 0xffffu), w * bf16_to_f32(v.z >> 16));
-        o.w = pack_bf16x2(w * bf16_to_f32(v.w & 0xffffu), w * bf16_to_f32(v.w >> 16));
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a = w * bf16_to_f32(d[q] & 0xffffu), b = w * bf16_to_f32(d[q] >> 16);
+          hi[q] = pack_bf16x2(a, b);
+          lo[q] = pack_bf16x2(a - bf16_to_f32(hi[q] & 0xffffu), b - bf16_to_f32(hi[q] >> 16));
+        }
         xg[cc] = xv[u];
-        dO[cc] = o;
+        dO[cc] = gather_u4{hi[0], hi[1], hi[2], hi[3]};
+        dOl[cc] = gather_u4{lo[0], lo[1], lo[2], lo[3]};
       }
     }
   }

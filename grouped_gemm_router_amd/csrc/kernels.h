@@ -32,6 +32,7 @@ struct GemmArgs {
   float* dXr;             // [A, H]
   uint16_t* Xg;           // [A, H]  X[token] per expert-major row
   uint16_t* dO;           // [A, H]  bf16(w * dY[token]) per expert-major row
+  uint16_t* dO_lo;        // [A, H]  bf16 of its remainder, w * dY[token] - bf16(w * dY[token])
   float* dwt_part;        // [A, nparts]
   int nparts;
   uint16_t* dWg;

@@ -404,6 +404,8 @@ __global__ void __launch_bounds__(256) k_dispatch_scatter(const int32_t* __restr
       row_token[pos] = (int)(s / k);
       row_slot[pos] = (int)s;
       slot_row[s] = pos;
+    } else if (s < A) {
+      slot_row[s] = -1;                       // a skipped slot has no row
     }
     // wave-wide order: all lanes read base before the leaders update it
     __builtin_amdgcn_wave_barrier();
@@ -489,6 +491,8 @@ __global__ void __launch_bounds__(64 * DS_WAVES) k_dispatch_small(
       row_token[pos] = s / k;
       row_slot[pos] = s;
       slot_row[s] = pos;
+    } else if (g * 64 < per && s < A) {
+      slot_row[s] = -1;                       // a skipped slot has no row
     }
     __builtin_amdgcn_wave_barrier();
     if (key < 0x400 && (m >> lane) == 1ull) hist[wave][key] += __popcll(m);

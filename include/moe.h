@@ -159,8 +159,12 @@ MOE_API moe_status moe_route_backward(const int32_t* topk_idx, const float* topk
  *   row_slot       [T*k] int32 out: slot of each row
  *   slot_row       [T*k] int32 out: row of each slot (inverse of row_slot)
  *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_DISPATCH)
- * Out-of-range expert ids are not detected on the device; they give
- * unspecified (but memory-safe) output.
+ * An expert id outside [0, E) is skipped: its slot gets no row and
+ * slot_row = -1, the rows of the valid slots keep their order, and
+ * expert_offsets[E] counts the valid slots only (row_token and row_slot past
+ * it are not written).  moe_combine and moe_backward give such a slot zero
+ * contribution (and d_topk_w = 0), so no later call reads outside its buffers.
+ * Ids repeated within a token are not detected: each copy gets its own row.
  */
 MOE_API moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
                                 int32_t* expert_offsets, int32_t* row_token,
@@ -225,6 +229,8 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
  * combine):  Y[t] = bf16( sum_{j=0..k-1} topk_w[t,j] * O_rows[slot_row[t*k+j]] ),
  * accumulated in fp32 in ascending j.
  *   O_rows [T*k, H] bf16, slot_row [T*k] int32, topk_w [T, k] fp32, Y [T, H] bf16 out
+ * slot_row must hold a row index in [0, T*k) or -1 (a slot moe_dispatch skipped,
+ * which adds nothing), as moe_dispatch writes it.
  */
 MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, const float* topk_w,
                                int32_t T, int32_t k, int32_t H, void* Y, void* stream);
@@ -237,7 +243,8 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
  *   G, U, h recomputed as in moe_expert_mlp;  P = dY[t] W_down[e]^T (fp32)
  *   d_topk_w[s] = <h, P>;  dh = w P
  *   du = dh * df/dU,  dg = dh * df/dG  (SwiGLU: du = dh * silu(G), dg = dh * U * silu'(G)),
- *   dO = bf16(w dY[t])
+ *   dO = w dY[t]   (P, dh, dg, du and dO are not rounded: the GEMMs that take dg, du and dO
+ *                   as operands contract their bf16 value and their bf16 remainder)
  *   dX[t]      = bf16( sum_j (dg W_gate[e]^T + du W_up[e]^T) ), j ascending
  *   dW_gate[e] = bf16( sum_r X[t]^T dg ),  dW_up[e] = bf16( sum_r X[t]^T du )
  *   dW_down[e] = bf16( sum_r h^T dO )      (all sums in fp32, fixed order;

@@ -49,11 +49,15 @@ design notes of the repository):
 * Combine adds the k weighted expert rows of a token in slot order
   (descending logit), in high precision, then rounds once.
 * Backward: bf16 roundings are straight-through (identity) in the
-  derivative.  The gradient of the expert output rows dO = w * dY is rounded
-  to bf16 (it feeds a bf16 weight-gradient GEMM); the gradients dg, du of the
-  gate and up pre-activations are kept exact; dX and dW_* are rounded once
-  after exact accumulation; the router-weight gradient is <h_r, dY_t W_down^T>
-  (no rounding).
+  derivative.  The only rounded intermediate is h (recomputed exactly as in
+  the forward); every other intermediate -- the gradient of the expert output
+  rows dO = w * dY, P = dY W_down^T, and the gradients dg, du of the gate and up
+  pre-activations -- is exact; dX and dW_* are rounded to bf16 once, after
+  exact accumulation; the router-weight gradient is <h_r, dY_t W_down^T> (not
+  rounded).
+* Accumulation is exact up to float64 rounding (the definition, computed as
+  closely as float64 allows), where an fp32 implementation accumulates in fp32;
+  the difference is far inside the comparison tolerance.
 """
 from __future__ import annotations
 
@@ -506,12 +510,11 @@ def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = Fals
     x_rows, dy_rows: [n, H] token inputs and output gradients of the rows;
     w_rows: [n] routing weights.  G, U, h are recomputed as in the forward.
     P = dY W_down^T; dwt = <h, P>; dh = w P; dg = dh * df/dG, du = dh * df/dU
-    (SwiGLU: du = dh * silu(G), dg = dh * U * silu'(G)); dO = bf16(w dY); dXr = dg Wg^T + du Wu^T;
+    (SwiGLU: du = dh * silu(G), dg = dh * U * silu'(G)); dO = w dY (exact); dXr = dg Wg^T + du Wu^T;
     dWg = x^T dg, dWu = x^T du, dWd = h^T dO (not yet rounded).  ReLU^2 has no gate:
     du = dh * 2 max(U, 0), dXr = du Wu^T, and dg, dWg are None.
     Returns dict of float64 arrays.
     """
-    rnd = (lambda a: a) if exact else bf16_round
     gated = is_gated(act)
     G = x_rows @ wg if gated else None
     U = x_rows @ wu
@@ -524,7 +527,7 @@ def expert_backward_rows(x_rows, dy_rows, w_rows, wg, wu, wd, exact: bool = Fals
     fg, fu = activation_grads(G, U, act, limit)
     du = dh * fu
     dg = dh * fg if gated else None
-    dO = rnd(w_rows[:, None] * dy_rows)
+    dO = w_rows[:, None] * dy_rows
     dXr = dg @ wg.T + du @ wu.T if gated else du @ wu.T
     return {"dwt": dwt, "dXr": dXr, "dWg": x_rows.T @ dg if gated else None, "dWu": x_rows.T @ du,
             "dWd": h.T @ dO, "dg": dg, "du": du, "h": h}

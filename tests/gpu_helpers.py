@@ -10,6 +10,9 @@ from oracle import moe_oracle as orc
 from grouped_gemm_router_amd import workloads as wl
 
 ATOL, RTOL = 1e-2, 2e-2
+# backward checks: elements that may lie outside the base bound and inside the h-rounding
+# allowance (a flipped h rounding moves a dW_down element by ulp(h) |dO|)
+H_RESCUE = 1e-3
 
 
 def to_dev(bits: np.ndarray) -> torch.Tensor:
@@ -27,25 +30,39 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().astype(np.float64)
 
 
-def check_close(gpu, ref, what: str, atol=ATOL, rtol=RTOL, ambiguity=None):
+def check_close(gpu, ref, what: str, atol=ATOL, rtol=RTOL, ambiguity=None, max_rescued=None):
     """Elementwise |gpu - ref| <= atol + rtol |ref|.  ``ambiguity`` (same shape)
     widens it where a quantised intermediate has several valid roundings: the
     GPU value must then lie within tolerance of one of the valid results (the
-    bound plus one bf16 ulp for the output's own rounding)."""
+    bound plus one bf16 ulp for the output's own rounding).  With ``max_rescued`` the
+    widening may only rescue a few elements: at most that fraction of them (and at
+    least 2) may lie outside the base bound, so that a real error cannot hide inside
+    it.  The message reports how large the widening is against the base bound."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.isfinite(gpu).all(), f"{what}: non-finite GPU values"
     err = np.abs(gpu - ref)
-    lim = atol + rtol * np.abs(ref)
+    base = atol + rtol * np.abs(ref)
+    lim = base
+    widen_msg = ""
+    rescued = 0
     if ambiguity is not None:
         amb = np.asarray(ambiguity, dtype=np.float64)
-        lim = lim + np.where(amb > 0, amb + (np.abs(ref) + amb) * 2.0 ** -7, 0.0)
+        widen = np.where(amb > 0, amb + (np.abs(ref) + amb) * 2.0 ** -7, 0.0)
+        lim = base + widen
+        rescued = int(((err > base) & (err <= lim)).sum())
+        ratio = widen / base
+        widen_msg = (f"; widened {np.mean(widen > 0):.3f} of the elements by {ratio.mean():.3f} of the base "
+                     f"bound on average (max {ratio.max():.3g}); {rescued} inside the widening only")
     bad = err > lim
     rel = err / np.maximum(np.abs(ref), 1e-6)
     msg = (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; max abs err {err.max():.3g}; "
-           f"mean_rel {float(np.mean(rel[np.abs(ref) > 1e-3])) if (np.abs(ref) > 1e-3).any() else 0:.3g}")
+           f"mean_rel {float(np.mean(rel[np.abs(ref) > 1e-3])) if (np.abs(ref) > 1e-3).any() else 0:.3g}"
+           + widen_msg)
     assert not bad.any(), msg
+    if max_rescued is not None:
+        assert rescued <= max(2, int(max_rescued * bad.size)), msg
     return msg
 
 
@@ -70,11 +87,36 @@ def host_weight_fn(cfg, name):
     return lambda e: wl.make_expert_weight(cfg, name, e)
 
 
+def oracle_forward(cfg, logits, X, wfn):
+    """The oracle's forward of a workload: (topk_idx, topk_w, offsets, h, O, Y, amb_O, amb_Y); the
+    ambiguities (MXFP8 only, else None) are what valid alternative roundings of the requantised h
+    can change (``mx_down_ambiguity``).  wfn(name) gives the per-expert weight getter."""
+    act, lim = cfg.activation, cfg.act_limit or None
+    gated = orc.is_gated(act)
+    idx, w = orc.route(logits, cfg.k)
+    off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
+    mx = cfg.dtype == "mxfp8"
+    h, O = orc.expert_mlp(X, row_token, off, wfn("gate") if gated else None, wfn("up"), wfn("down"), mxfp8=mx,
+                          act=act, limit=lim)
+    amb_O = amb_Y = None
+    if mx:
+        Xv = orc.bf16_decode(X)
+        amb_O = np.zeros_like(O)
+        for e in range(cfg.E):
+            lo, hi = off[e], off[e + 1]
+            if hi > lo:
+                wg = orc.bf16_decode(wfn("gate")(e)) if gated else None
+                G, U, _, _ = orc.expert_forward_rows(Xv[row_token[lo:hi]], wg, orc.bf16_decode(wfn("up")(e)),
+                                                     orc.bf16_decode(wfn("down")(e)), mxfp8=True, act=act, limit=lim)
+                amb_O[lo:hi] = orc.mx_down_ambiguity(G, U, orc.bf16_decode(wfn("down")(e)), act=act, limit=lim)
+        amb_Y = sum(w[:, j:j + 1] * amb_O[slot_row.reshape(-1, cfg.k)[:, j]] for j in range(cfg.k))
+    return idx, w, off, h, O, orc.combine(O, slot_row, w), amb_O, amb_Y
+
+
 def backward_h_ambiguity(cfg, X, dY, idx, w, fn, act="swiglu", limit=None, experts=None):
-    """What other valid bf16 roundings of h = bf16(f(G, U)) and dO = bf16(w dY) can change
-    (``bf16_round_delta``; both are rounding decisions on values the GPU knows to fp32):
-    per expert |delta h|^T |dO| + |h|^T |delta dO| (dW_down), per slot
-    sum_i |delta h_i| |P_i| (d_topk_w)."""
+    """What other valid bf16 roundings of h = bf16(f(G, U)) can change (``bf16_round_delta``:
+    h is a rounding decision on a value the GPU knows to fp32): per expert |delta h|^T |dO|
+    with the exact dO = w dY (dW_down), per slot sum_i |delta h_i| |P_i| (d_topk_w)."""
     off, row_token, row_slot, _ = orc.dispatch(idx, cfg.E)
     Xv, dYv = orc.bf16_decode(X), orc.bf16_decode(dY)
     amb_dwd = {}
@@ -87,9 +129,7 @@ def backward_h_ambiguity(cfg, X, dY, idx, w, fn, act="swiglu", limit=None, exper
         wg = orc.bf16_decode(fn("gate")(e)) if orc.is_gated(act) else None
         wu, wd = (orc.bf16_decode(fn(n)(e)) for n in ("up", "down"))
         dh = orc.h_ambiguity_rows(Xv[tok], wg, wu, act, limit)
-        _, _, h, _ = orc.expert_forward_rows(Xv[tok], wg, wu, wd, act=act, limit=limit)
-        dO_exact = w.reshape(-1)[sl][:, None] * dYv[tok]
-        dO = orc.bf16_round(dO_exact)
-        amb_dwd[e] = dh.T @ np.abs(dO) + np.abs(h).T @ orc.bf16_round_delta(dO_exact)
+        dO = w.reshape(-1)[sl][:, None] * dYv[tok]
+        amb_dwd[e] = dh.T @ np.abs(dO)
         amb_dtw.reshape(-1)[sl] = (dh * np.abs(dYv[tok] @ wd.T)).sum(axis=1)
     return amb_dwd, amb_dtw

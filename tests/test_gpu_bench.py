@@ -30,3 +30,22 @@ def test_bench_line_tiny(capsys, monkeypatch):
     assert r["achieved"] > 0 and r["peak"] > 0 and r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-2)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
+    assert c["cpu_model"]
+
+
+def test_bench_line_configs_block(capsys, monkeypatch):
+    """The default (prefill) line carries the other workloads, each measured the same way with its
+    own roofline (here only decode, to keep the test short)."""
+    import bench
+    print("[case] bench prefill + configs block", flush=True)
+    monkeypatch.setattr(bench, "EXTRA_CONFIGS", ("decode",))
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"])
+    assert bench.main() == 0
+    lines = [l for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
+    d = json.loads(lines[-1])
+    assert d["config"]["workload"] == "prefill" and set(d["configs"]) == {"decode"}
+    c = d["configs"]["decode"]
+    assert c["workload"] == "decode" and c["active_experts"] > 100 and c["ms_per_step"] > 0
+    assert 0 < c["frac_of_hbm_peak"] < 1
+    r = c["roofline"]
+    assert r["bound"] == "hbm" and r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-2)

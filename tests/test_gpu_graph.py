@@ -1,17 +1,20 @@
 """HIP-graph capture of the layer: a captured forward (and forward + backward)
 replayed several times, with eager work on other inputs through the same plan
-buffers between the replays, gives the eager result bit for bit every time.
-No call of the library allocates or clears memory with a memset, so the whole
-step can be captured."""
+buffers between the replays, gives the eager result bit for bit every time, and
+that result matches the oracle (routing bit for bit, outputs and gradients within
+the layer tolerance).  No call of the library allocates or clears memory with a
+memset, so the whole step can be captured."""
 import dataclasses
 
 import numpy as np
 import pytest
 import torch
 
+from oracle import moe_oracle as orc
 from grouped_gemm_router_amd import workloads as wl
 
-from gpu_helpers import device_weights, to_bits, to_dev
+from gpu_helpers import (H_RESCUE, backward_h_ambiguity, check_close, device_weights, host_weight_fn,
+                         oracle_forward, to_bits, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +75,26 @@ def test_graph_replays_match_eager(cfg):
         got = snapshot(outs)
         for i, (a, b) in enumerate(zip(got, eager)):
             assert np.array_equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+    # the replayed result against the oracle
+    fn = lambda n: host_weight_fn(cfg, n)
+    lg, xb = wl.make_logits(cfg), wl.make_x(cfg)
+    idx, w, off, h, O, Y, amb_O, amb_Y = oracle_forward(cfg, lg, xb, fn)
+    assert np.array_equal(layer.plan(cfg.T, cfg.backward)["topk_idx"].cpu().numpy(), idx)
+    assert np.array_equal(layer.plan(cfg.T, cfg.backward)["offsets"].cpu().numpy(), off)
+    check_close(orc.bf16_decode(got[0]), Y, "replayed Y", ambiguity=amb_Y)
+    if cfg.backward:
+        act = cfg.activation
+        gated = orc.is_gated(act)
+        dy = wl.make_dy(cfg)
+        ref = orc.backward(xb, dy, idx, w, fn("gate") if gated else None, fn("up"), fn("down"), E=cfg.E, act=act)
+        amb_dwd, amb_dtw = backward_h_ambiguity(cfg, xb, dy, idx, w, fn, act)
+        names = ["dX"] + (["dWg"] if gated else []) + ["dWu", "dWd", "d_topk_w", "d_logits"]
+        g = dict(zip(names, got[1:]))
+        check_close(orc.bf16_decode(g["dX"]), ref["dX"], "replayed dX")
+        check_close(g["d_topk_w"].view(np.float32), ref["d_topk_w"], "replayed d_topk_w", ambiguity=amb_dtw,
+                    max_rescued=H_RESCUE)
+        for key in (("dWg", "dWu", "dWd") if gated else ("dWu", "dWd")):
+            gv = orc.bf16_decode(g[key])
+            for e in range(cfg.E):
+                check_close(gv[e], ref["dW"][key][e], f"replayed {key}[{e}]",
+                            ambiguity=amb_dwd.get(e) if key == "dWd" else None, max_rescued=H_RESCUE)

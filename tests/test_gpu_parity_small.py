@@ -9,8 +9,8 @@ import torch
 from oracle import moe_oracle as orc
 from grouped_gemm_router_amd import workloads as wl
 
-from gpu_helpers import (backward_h_ambiguity, check_close, device_weights, host_weight_fn, to_bits, to_dev,
-                         to_f64)
+from gpu_helpers import (H_RESCUE, backward_h_ambiguity, check_close, device_weights, host_weight_fn,
+                         oracle_forward, to_bits, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -195,27 +195,6 @@ def _run_forward(cfg, Wg, Wu, Wd, logits, X):
     return layer, layer.plan(cfg.T)
 
 
-def _oracle_forward(cfg, logits, X, wfn):
-    idx, w = orc.route(logits, cfg.k)
-    off, row_token, row_slot, slot_row = orc.dispatch(idx, cfg.E)
-    mx = cfg.dtype == "mxfp8"
-    h, O = orc.expert_mlp(X, row_token, off, wfn("gate"), wfn("up"), wfn("down"), mxfp8=mx)
-    amb_O = amb_Y = None
-    if mx:
-        # valid alternative roundings of the requantised h (see mx_down_ambiguity)
-        Xv = orc.bf16_decode(X)
-        amb_O = np.zeros_like(O)
-        for e in range(cfg.E):
-            lo, hi = off[e], off[e + 1]
-            if hi > lo:
-                G, U, _, _ = orc.expert_forward_rows(Xv[row_token[lo:hi]], orc.bf16_decode(wfn("gate")(e)),
-                                                     orc.bf16_decode(wfn("up")(e)), orc.bf16_decode(wfn("down")(e)),
-                                                     mxfp8=True)
-                amb_O[lo:hi] = orc.mx_down_ambiguity(G, U, orc.bf16_decode(wfn("down")(e)))
-        amb_Y = sum(w[:, j:j + 1] * amb_O[slot_row.reshape(-1, cfg.k)[:, j]] for j in range(cfg.k))
-    return idx, w, off, h, O, orc.combine(O, slot_row, w), amb_O, amb_Y
-
-
 SMALL = [
     wl.config("tiny"),
     wl.config("tiny", name="ragged", T=300, H=320, I=192, E=5, k=3, seed=11),
@@ -234,7 +213,7 @@ def test_forward_small_vs_oracle(cfg):
     logits, X = wl.make_logits(cfg), wl.make_x(cfg)
     Wg, Wu, Wd = (device_weights(cfg, n) for n in ("gate", "up", "down"))
     layer, pl = _run_forward(cfg, Wg, Wu, Wd, logits, X)
-    idx, w, off, h, O, Y, amb_O, amb_Y = _oracle_forward(cfg, logits, X, lambda n: host_weight_fn(cfg, n))
+    idx, w, off, h, O, Y, amb_O, amb_Y = oracle_forward(cfg, logits, X, lambda n: host_weight_fn(cfg, n))
     assert np.array_equal(pl["topk_idx"].cpu().numpy(), idx)
     assert np.array_equal(pl["offsets"].cpu().numpy(), off)
     check_close(to_f64(pl["H_rows"]), h, "h")
@@ -287,12 +266,12 @@ def test_forward_backward_every_row_class(act):
     ref = orc.backward(X, dY, idx, w, fn("gate") if gated else None, fn("up"), fn("down"), E=cfg.E, act=act)
     amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn, act)
     check_close(to_f64(dX), ref["dX"], "dX")
-    check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w", ambiguity=amb_dtw)
+    check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w", ambiguity=amb_dtw, max_rescued=H_RESCUE)
     g = {"dWg": to_f64(dWg) if gated else None, "dWu": to_f64(dWu), "dWd": to_f64(dWd)}
     for key in (("dWg", "dWu", "dWd") if gated else ("dWu", "dWd")):
         for e in range(cfg.E):
             check_close(g[key][e], ref["dW"][key][e], f"{key}[{e}] ({REMAINDER_COUNTS[e]} rows)",
-                        ambiguity=amb_dwd.get(e) if key == "dWd" else None)
+                        ambiguity=amb_dwd.get(e) if key == "dWd" else None, max_rescued=H_RESCUE)
 
 
 ACTS = [("swiglu", 0.0), ("swiglu_clamp", 1.0), ("swiglu_oai", 1.0), ("swiglu_oai", 7.0), ("geglu", 0.0),
@@ -360,7 +339,7 @@ def test_backward_activations_vs_oracle(act, limit):
                        limit=limit or None)
     amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn, act, limit or None)
     check_close(to_f64(dX), ref["dX"], f"{act} dX")
-    check_close(dtw.cpu().numpy(), ref["d_topk_w"], f"{act} d_topk_w", ambiguity=amb_dtw)
+    check_close(dtw.cpu().numpy(), ref["d_topk_w"], f"{act} d_topk_w", ambiguity=amb_dtw, max_rescued=H_RESCUE)
     if not gated:
         assert dWg is None
     for key, t in (("dWg", dWg), ("dWu", dWu), ("dWd", dWd)):
@@ -369,7 +348,7 @@ def test_backward_activations_vs_oracle(act, limit):
         g = to_f64(t)
         for e in range(cfg.E):
             check_close(g[e], ref["dW"][key][e], f"{act} {key}[{e}]",
-                        ambiguity=amb_dwd.get(e) if key == "dWd" else None)
+                        ambiguity=amb_dwd.get(e) if key == "dWd" else None, max_rescued=H_RESCUE)
 
 
 def test_empty_batch_forward_backward():
@@ -439,7 +418,7 @@ def test_backward_small_vs_oracle(cfg):
     ref = orc.backward(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), E=cfg.E)
     amb_dwd, amb_dtw = backward_h_ambiguity(cfg, X, dY, idx, w, fn)
     check_close(to_f64(dX), ref["dX"], "dX")
-    check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w", ambiguity=amb_dtw)
+    check_close(dtw.cpu().numpy(), ref["d_topk_w"], "d_topk_w", ambiguity=amb_dtw, max_rescued=H_RESCUE)
     # router backward chained on the layer's d_topk_w, against the oracle's chain
     dlog = layer.route_backward(cfg.T).cpu().numpy().astype(np.float64)
     rdl = orc.route_backward(logits, cfg.k, ref["d_topk_w"])
@@ -450,7 +429,7 @@ def test_backward_small_vs_oracle(cfg):
     for key in ("dWg", "dWu", "dWd"):
         for e in range(cfg.E):
             check_close(g[key][e], ref["dW"][key][e], f"{key}[{e}]",
-                        ambiguity=amb_dwd.get(e) if key == "dWd" else None)
+                        ambiguity=amb_dwd.get(e) if key == "dWd" else None, max_rescued=H_RESCUE)
     # a second backward gives the same bits (fixed reduction order, no atomics)
     first = [to_bits(t).copy() for t in (dX, dWg, dWu, dWd)] + [dtw.cpu().numpy().copy()]
     layer.backward(to_dev(X), to_dev(dY))

@@ -133,3 +133,110 @@ def test_backward_tokens_matches_full_backward():
         dX, dwt = orc.backward_tokens(X, dY, idx, w, Wg, Wu, Wd, toks, exact=exact)
         np.testing.assert_allclose(dX, full["dX"][toks], rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(dwt, full["d_topk_w"][toks], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------
+# Rounded-mode pin: the backward of the rounded layer (h rounded to bf16 as in the forward;
+# dO = w dY, P, dg, du exact; dX and dW rounded once after exact sums) written as plain scalar
+# loops over tokens, slots and elements, with a bf16 rounding of its own (Python's round() is
+# round-half-even on the exactly scaled significand).  Nothing here calls the oracle's code.
+# ------------------------------------------------------------------------------------------
+import math
+
+
+def _rnd_bf16(x: float) -> float:
+    if x == 0.0:
+        return x
+    m, e = math.frexp(x)                     # x = m 2^e, 0.5 <= |m| < 1: 8 significant bits
+    return math.ldexp(round(math.ldexp(m, 8)), e - 8)
+
+
+def _near_bf16_midpoint(x: float, eps: float = 1e-6) -> bool:
+    """Whether x lies within eps bf16 steps of a rounding midpoint (either rounding is then a
+    matter of the summation order)."""
+    if x == 0.0:
+        return False
+    m, e = math.frexp(x)
+    f = abs(math.ldexp(m, 8))
+    return abs(f - math.floor(f) - 0.5) < eps
+
+
+def _scalar_backward(X, dY, idx, w, Wg, Wu, Wd, round_h=True, round_dO=False):
+    T, H = len(X), len(X[0])
+    k = len(idx[0])
+    E, I = len(Wg), len(Wg[0][0])
+    sig = lambda v: 1.0 / (1.0 + math.exp(-v))
+    dX = [[0.0] * H for _ in range(T)]
+    dwt = [[0.0] * k for _ in range(T)]
+    dWg = [[[0.0] * I for _ in range(H)] for _ in range(E)]
+    dWu = [[[0.0] * I for _ in range(H)] for _ in range(E)]
+    dWd = [[[0.0] * H for _ in range(I)] for _ in range(E)]
+    for t in range(T):
+        for j in range(k):
+            e, wt = int(idx[t][j]), float(w[t][j])
+            for i in range(I):
+                g = sum(X[t][c] * Wg[e][c][i] for c in range(H))
+                u = sum(X[t][c] * Wu[e][c][i] for c in range(H))
+                s = sig(g)
+                h = g * s * u
+                if round_h:
+                    h = _rnd_bf16(h)
+                p = sum(dY[t][c] * Wd[e][i][c] for c in range(H))
+                dwt[t][j] += h * p
+                dh = wt * p
+                du = dh * g * s                          # d(h)/du = silu(g)
+                dg = dh * u * s * (1.0 + g * (1.0 - s))  # d(h)/dg = u silu'(g)
+                for c in range(H):
+                    dX[t][c] += dg * Wg[e][c][i] + du * Wu[e][c][i]
+                    dWg[e][c][i] += X[t][c] * dg
+                    dWu[e][c][i] += X[t][c] * du
+                    dO = wt * dY[t][c]
+                    if round_dO:
+                        dO = _rnd_bf16(dO)
+                    dWd[e][i][c] += h * dO
+    return dX, dwt, dWg, dWu, dWd
+
+
+def _mismatches(unrounded, got, path=()):
+    """Elements where bf16(unrounded) differs from got, other than at rounding midpoints."""
+    if isinstance(unrounded, list):
+        out = []
+        for n, (a, b) in enumerate(zip(unrounded, got)):
+            out += _mismatches(a, b, path + (n,))
+        return out
+    if _rnd_bf16(unrounded) != float(got) and not _near_bf16_midpoint(unrounded):
+        return [path]
+    return []
+
+
+def _pin_problem():
+    X, Wg, Wu, Wd, dY, idx, w = _problem(11, T=6, H=8, I=4, E=3, k=2)
+    return X, Wg, Wu, Wd, dY, idx, w
+
+
+def test_rounded_backward_matches_scalar_loops():
+    """The oracle's rounded backward equals the scalar-loop definition element by element: dX,
+    dW_gate, dW_up and dW_down bit for bit after one bf16 rounding (up to ties the summation
+    order decides), d_topk_w to float64 rounding."""
+    X, Wg, Wu, Wd, dY, idx, w = _pin_problem()
+    assert len(set(idx.ravel().tolist())) == 3            # every expert has rows
+    g = orc.backward(X, dY, idx, w, Wg, Wu, Wd)
+    dX, dwt, dWg, dWu, dWd = _scalar_backward(X.tolist(), dY.tolist(), idx.tolist(), w.tolist(),
+                                              Wg.tolist(), Wu.tolist(), Wd.tolist())
+    assert _mismatches(dX, g["dX"].tolist()) == []
+    for name, ref in (("dWg", dWg), ("dWu", dWu), ("dWd", dWd)):
+        got = [g["dW"][name][e].tolist() for e in range(3)]
+        assert _mismatches(ref, got) == [], name
+    np.testing.assert_allclose(g["d_topk_w"], np.array(dwt), rtol=1e-12, atol=1e-14)
+
+
+def test_scalar_pin_tells_rounding_points_apart():
+    """The scalar-loop comparison above would catch a rounding point in the wrong place: an
+    oracle that rounded dO = w dY to bf16, or that did not round h, disagrees with the
+    definition on some dW_down elements of the same problem."""
+    X, Wg, Wu, Wd, dY, idx, w = _pin_problem()
+    g = orc.backward(X, dY, idx, w, Wg, Wu, Wd)
+    got = [g["dW"]["dWd"][e].tolist() for e in range(3)]
+    args = (X.tolist(), dY.tolist(), idx.tolist(), w.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist())
+    assert _mismatches(_scalar_backward(*args, round_dO=True)[4], got) != []
+    assert _mismatches(_scalar_backward(*args, round_h=False)[4], got) != []
