@@ -9,13 +9,14 @@ Inputs are resident in HBM before the timed region; weight packing happens at
 load time, outside it.
 
 Per workload, three passes over the same steps follow the warmup:
-  * the timed region (``ms_per_step``, ``value``): K steps with one timing event
-    on each side only (every recorded event leaves the GPU idle for a few
-    microseconds, so none sits between the steps);
   * the roofline pass: K steps with HIP events around the expert-MLP call (and,
     for training, around the backward call) on the stream its kernels run on,
     giving the calls' average launch durations;
-  * the spread pass: K steps with one event between steps (p10 / p50 / p90).
+  * the spread pass: K steps with one event between steps (p10 / p50 / p90);
+  * the timed region (``ms_per_step``, ``value``): K steps with one timing event
+    on each side only (every recorded event leaves the GPU idle for a few
+    microseconds, so none sits between the steps), after the two passes above,
+    so that it runs at the clocks of a GPU that has been busy for a while.
 With --cold-cache a fourth pass reads 512 MiB before every step, which evicts L2
 and the Infinity Cache (and leaves clean lines, so the step pays no write-back
 of the flush), and times each step on its own (reported under cold_cache).
@@ -238,18 +239,6 @@ def measure(cfg, args, device_draw=False):
     run = graph.replay if graph is not None else step
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    # timed region: K steps, one event on each side
-    t_start, t_end = ev(), ev()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for _ in range(args.steps):
-        run()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / args.steps
-
     # roofline pass: events around the expert-MLP call (and the backward call) of every step
     mlp_ms = bwd_ms = None
     if graph is None:
@@ -270,6 +259,18 @@ def measure(cfg, args, device_draw=False):
         marks[i + 1].record()
     torch.cuda.synchronize()
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+
+    # timed region: K steps, one event on each side
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        run()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / args.steps
 
     cold_ms = None
     if args.cold_cache:
