@@ -26,7 +26,7 @@ CALL_DISPATCH, CALL_EXPERT_MLP, CALL_BACKWARD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_validate_problem", "moe_workspace_size", "moe_check_device",
            "moe_route", "moe_dispatch", "moe_pack_weights", "moe_mx_quantize", "moe_expert_mlp",
-           "moe_combine", "moe_backward", "moe_route_backward", "moe_grouped_gemm")
+           "moe_combine", "moe_backward", "moe_route_backward", "moe_grouped_gemm", "moe_expert_mlp_static")
 
 
 class MoEError(RuntimeError):
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [P, P, P, I32, I32, I32, P, P]),
         "moe_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_gemm": (ctypes.c_int, [I32, P, I32, I64, I32, I32, P, P, P, P, P, P]),
+        "moe_expert_mlp_static": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -180,10 +181,11 @@ def mx_quantize(x: torch.Tensor):
 
 
 def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=None, O_rows=None, ws=None,
-               activation="swiglu", act_limit=0.0):
+               activation="swiglu", act_limit=0.0, static_ws=False):
     """Expert MLP over the dispatched rows.  bf16 weights [E, I, H] / [E, H, I]
     (pack_weights), or MXFP8 codes with ``scales = (Sg, Su, Sd)``.  For ReLU^2 the
-    gate weight (and Sg) is None."""
+    gate weight (and Sg) is None.  ``static_ws`` calls moe_expert_mlp_static (the
+    library's static workspace; ``ws`` must then be None)."""
     T, H = X.shape
     E, I, _ = Wu_t.shape
     mx = scales is not None
@@ -210,6 +212,14 @@ def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=N
     _expect(H_rows, "H_rows", torch.bfloat16, (T * k, I))
     _expect(O_rows, "O_rows", torch.bfloat16, (T * k, H))
     p = problem(T, H, I, E, k, "mxfp8" if mx else "bf16", activation, act_limit)
+    if static_ws:
+        if ws is not None:
+            raise ValueError("static_ws takes no workspace")
+        _check("moe_expert_mlp_static",
+               lib.moe_expert_mlp_static(ctypes.byref(p), _ptr(X), _ptr(row_token), _ptr(offsets), _ptr(Wg_t),
+                                         _ptr(Wu_t), _ptr(Wd_t), _ptr(Sg), _ptr(Su), _ptr(Sd), _ptr(H_rows),
+                                         _ptr(O_rows), _stream()))
+        return H_rows, O_rows
     if ws is None:
         ws, n = _workspace(p, CALL_EXPERT_MLP, dev)
     else:

@@ -78,6 +78,27 @@ moe_status device_ok() {
   return g_dev_state[dev] == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
 }
 
+// Workspace of moe_expert_mlp_static, for callers that cannot allocate: one array per GPU, held
+// until the process ends.  On the host, `scratch` names a host-side stand-in, never the device
+// array: its device address comes from hipGetSymbolAddress, once per device (g_scratch).
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+void* g_scratch[64];
+
+// The current device's address of `scratch` (looked up on the device's first call, under g_mu).
+moe_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -176,10 +197,16 @@ MOE_API moe_status moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8
   return from_hip(moe::launch_mx_quantize((const uint16_t*)x, rows, K, q, scales, (hipStream_t)stream));
 }
 
-MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token,
-                                  const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
-                                  const void* Wd_t, const uint8_t* Sg, const uint8_t* Su, const uint8_t* Sd,
-                                  void* H_rows, void* O_rows, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_expert_mlp, with the workspace given by the caller or (use_static) the library's static
+// array of MOE_STATIC_SCRATCH_BYTES on the current device.
+moe_status expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token, const int32_t* expert_offsets,
+                      const void* Wg_t, const void* Wu_t, const void* Wd_t, const uint8_t* Sg, const uint8_t* Su,
+                      const uint8_t* Sd, void* H_rows, void* O_rows, void* ws, size_t ws_bytes, bool use_static,
+                      void* stream) {
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
   const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
@@ -191,9 +218,14 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
   if (!mx && (Sg || Su || Sd)) return MOE_ERR_INVALID_ARG;
   if (!rows) return MOE_OK;                              // empty batch: nothing to compute
   const size_t need = mlp_ws(p);
-  if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (use_static) {
+    if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    ws_bytes = MOE_STATIC_SCRATCH_BYTES;
+  } else if (need && (!ws || ws_bytes < need)) {
+    return MOE_ERR_WORKSPACE;
+  }
   if ((s = device_ok()) != MOE_OK) return s;
-  if (p->T == 0) return MOE_OK;
+  if (use_static && (s = static_scratch(&ws)) != MOE_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   if (!mx) {
     moe::GemmArgs a = {};
@@ -236,6 +268,26 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
   if (e == hipSuccess) e = moe::launch_mx_quantize((const uint16_t*)H_rows, (long)A, p->I, Hq, Hs, st);
   if (e == hipSuccess) e = moe::launch_mx_down(m, st);
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token,
+                                  const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                  const void* Wd_t, const uint8_t* Sg, const uint8_t* Su, const uint8_t* Sd,
+                                  void* H_rows, void* O_rows, void* ws, size_t ws_bytes, void* stream) {
+  return expert_mlp(p, X, row_token, expert_offsets, Wg_t, Wu_t, Wd_t, Sg, Su, Sd, H_rows, O_rows, ws, ws_bytes,
+                    false, stream);
+}
+
+MOE_API moe_status moe_expert_mlp_static(const moe_problem* p, const void* X, const int32_t* row_token,
+                                         const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                         const void* Wd_t, const uint8_t* Sg, const uint8_t* Su, const uint8_t* Sd,
+                                         void* H_rows, void* O_rows, void* stream) {
+  return expert_mlp(p, X, row_token, expert_offsets, Wg_t, Wu_t, Wd_t, Sg, Su, Sd, H_rows, O_rows, nullptr, 0,
+                    true, stream);
 }
 
 MOE_API moe_status moe_grouped_gemm(int32_t dtype, const int32_t* m_indptr, int32_t E, int64_t M, int32_t N,

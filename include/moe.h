@@ -224,6 +224,28 @@ MOE_API moe_status moe_expert_mlp(const moe_problem* p, const void* X, const int
                                   void* O_rows, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): moe_expert_mlp with its
+ * workspace in a static device array of the library instead of a caller buffer.
+ *   Arguments, results, kernels and error behaviour as moe_expert_mlp, without
+ *   ws / ws_bytes.  The array holds MOE_STATIC_SCRATCH_BYTES on every GPU the
+ *   library runs this call on, from the first call on that GPU until the process
+ *   ends; a problem whose moe_workspace_size(MOE_CALL_EXPERT_MLP) exceeds it gives
+ *   MOE_ERR_WORKSPACE before anything is enqueued (bf16 needs at most 16 KiB; MXFP8
+ *   needs about T*H + T*k*I bytes).  The call allocates and frees nothing; its first
+ *   call on a GPU looks up the array's device address (hipGetSymbolAddress).
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents (each call writes all it reads): calls that overlap on one GPU
+ *   (other streams, other host threads) race and must be serialised by the caller.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+MOE_API moe_status moe_expert_mlp_static(const moe_problem* p, const void* X,
+                                         const int32_t* row_token, const int32_t* expert_offsets,
+                                         const void* Wg_t, const void* Wu_t, const void* Wd_t,
+                                         const uint8_t* Sg, const uint8_t* Su, const uint8_t* Sd,
+                                         void* H_rows, void* O_rows, void* stream);
+
+/*
  * Weighted combine (LigerCute "Forward pass": a final local combine applies
  * the router weights; LightMoE: routing-weight application and deterministic
  * combine):  Y[t] = bf16( sum_{j=0..k-1} topk_w[t,j] * O_rows[slot_row[t*k+j]] ),
