@@ -55,8 +55,8 @@ size_t mlp_ws(const moe_problem* p) {
 size_t bwd_ws(const moe_problem* p) {
   const size_t H = p->H, I = p->I, A = (size_t)p->T * p->k;
   const size_t nparts = moe::bwd_nparts(p->I, p->activation);
-  return align_up(A * I * 4) + 2 * align_up(A * 2 * I * 2) + align_up(A * I * 2) + align_up(A * H * 4) +
-         align_up(A * H * 2) + align_up(A * nparts * 4);
+  return align_up(A * I * 4) + 2 * align_up(A * 2 * I * 2) + 2 * align_up(A * I * 2) + align_up(A * H * 4) +
+         align_up(A * nparts * 4);
 }
 
 // Device check, cached per device id.
@@ -383,15 +383,12 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   w8 += align_up(A * 2 * I * 2);
   a.dGU_lo = (uint16_t*)w8;
   w8 += align_up(A * 2 * I * 2);
-  a.Hrows = (uint16_t*)w8;
+  a.hw = (uint16_t*)w8;
+  w8 += align_up(A * I * 2);
+  a.hw_lo = (uint16_t*)w8;
   w8 += align_up(A * I * 2);
   a.dXr = (float*)w8;
-  // once dX is reduced, the weight-gradient operand rows reuse the dXr area
-  a.Xg = (uint16_t*)w8;
-  a.dO = (uint16_t*)(w8 + A * H * 2);
   w8 += align_up(A * H * 4);
-  a.dO_lo = (uint16_t*)w8;
-  w8 += align_up(A * H * 2);
   a.dwt_part = (float*)w8;
   a.dWg = (uint16_t*)dW_gate;
   a.dWu = (uint16_t*)dW_up;
@@ -403,7 +400,6 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
     if (e == hipSuccess) e = moe::launch_bwd_recompute(a, st);
     if (e == hipSuccess) e = moe::launch_bwd_dx_rows(a, st);
     if (e == hipSuccess) e = moe::launch_bwd_token_reduce(a, slot_row, (uint16_t*)dX, d_topk_w, st);
-    if (e == hipSuccess) e = moe::launch_bwd_gather(a, st);
   }
   if (e == hipSuccess) e = moe::launch_bwd_dw_down(a, st);
   if (e == hipSuccess) e = moe::launch_bwd_dw_gateup(a, st);

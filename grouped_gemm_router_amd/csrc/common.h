@@ -112,4 +112,49 @@ __device__ __forceinline__ void gated_act_grad(float g, float u, int act, float 
   }
 }
 
+// fg = df/dg alone, computed as gated_act_grad computes it (the same value, bit for bit).
+__device__ __forceinline__ float gated_act_dg(float g, float u, int act, float lim) {
+  switch (act) {
+    case ACT_SWIGLU_CLAMP:
+    case ACT_SWIGLU_OAI: {
+      const float gc = fminf(g, lim), uc = fminf(fmaxf(u, -lim), lim);
+      const float pg = g <= lim ? 1.f : 0.f;
+      if (act == ACT_SWIGLU_CLAMP) {
+        const float s = sigmoid_f32(gc);
+        return uc * (s * (1.f + gc * (1.f - s))) * pg;
+      }
+      const float s = sigmoid_f32(OAI_ALPHA * gc);
+      return (s + OAI_ALPHA * gc * s * (1.f - s)) * (uc + 1.f) * pg;
+    }
+    case ACT_GEGLU: {
+      const float Phi = 0.5f * (1.f + erff(g * INV_SQRT2));
+      return (Phi + g * INV_SQRT_2PI * __expf(-0.5f * g * g)) * u;
+    }
+    case ACT_REGLU: return g > 0.f ? u : 0.f;
+    default: {
+      const float s = sigmoid_f32(g);
+      return u * (s * (1.f + g * (1.f - s)));
+    }
+  }
+}
+
+// fu = df/du alone, computed as gated_act_grad computes it (the same value, bit for bit).
+__device__ __forceinline__ float gated_act_du(float g, float u, int act, float lim) {
+  switch (act) {
+    case ACT_SWIGLU_CLAMP:
+    case ACT_SWIGLU_OAI: {
+      const float gc = fminf(g, lim);
+      const float pu = (u >= -lim && u <= lim) ? 1.f : 0.f;
+      const float s = act == ACT_SWIGLU_CLAMP ? sigmoid_f32(gc) : sigmoid_f32(OAI_ALPHA * gc);
+      return gc * s * pu;
+    }
+    case ACT_GEGLU: {
+      const float Phi = 0.5f * (1.f + erff(g * INV_SQRT2));
+      return g * Phi;
+    }
+    case ACT_REGLU: return fmaxf(g, 0.f);
+    default: return g * sigmoid_f32(g);
+  }
+}
+
 }  // namespace moe

@@ -232,11 +232,13 @@ __device__ __forceinline__ void split4(const float (&v)[4], uint2& hi, uint2& lo
   lo.y = pack_bf16x2(v[2] - bf16_to_f32(hi.y & 0xffffu), v[3] - bf16_to_f32(hi.y >> 16));
 }
 
-// Recompute G, U; with P give h, the router-weight partial sums <h, P>, dg and du.
-// A wave owns 32 intermediate columns of WTM rows.  P is read one 32-row block
-// ahead of its use; the five bf16 outputs (h, dg and du with their remainders) of
-// each 32-row block go through the wave's LDS scratch (NSLOT staged blocks at a
-// time) and leave as whole 64-byte row segments (16 bytes per lane).
+// Recompute G, U; with P give the router-weight partial sums <h, P> (h = bf16(f(G, U)))
+// and the operands of the weight gradients: w h, dg and du, each as a bf16 value and a
+// bf16 remainder.  A wave owns 32 intermediate columns of WTM rows.  P is read one 32-row
+// block ahead of its use; the six bf16 outputs of each 32-row block go through the wave's
+// LDS scratch (four staged blocks, then two) and leave as whole 64-byte row segments
+// (16 bytes per lane).  du is recomputed from the accumulators for the second round
+// rather than held in registers.
 template <class C, int PART = ROWS_ALL, int ACTK = ACT_SWIGLU>
 struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
   __device__ static void init_sched(typename RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART>::Sched& s,
@@ -247,9 +249,8 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
   static constexpr bool EARLY_NEXT = false;
   // one staged 32 x 32 bf16 block: 64-byte rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
   static constexpr int OUT = 32 * 64;
-  static constexpr int NSLOT = RowEpiLds<C>::BYTES / OUT < 4 ? RowEpiLds<C>::BYTES / OUT : 4;
   static_assert(C::FN * 16 == 32, "a wave owns 32 intermediate columns");
-  static_assert(NSLOT >= 1, "staging area too small");
+  static_assert(RowEpiLds<C>::BYTES >= (ACTK == ACT_ANY ? 2 : 4) * OUT, "staging area too small");
 
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t* wlds) {
@@ -283,55 +284,13 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
       auto slot = [&](int o, int fn, int q) {
         return reinterpret_cast<uint2*>(wlds + o * OUT + rl * 64 + (((2 * fn + q) ^ ((rl >> 2) & 3)) * 16) + h * 8);
       };
-      // outputs 0..4: h, dg, dg remainder, du, du remainder; with four slots the first four
-      // are staged as they are computed and the last waits in registers, with fewer all wait
-      constexpr int HELD = NSLOT >= 4 ? 1 : 5;
-      uint2 held[HELD][C::FN][2];
-      auto emit = [&](int o, int fn, int q, uint2 v) {
-        if constexpr (NSLOT >= 4) {
-          if (o < 4) *slot(o, fn, q) = v;
-          else held[0][fn][q] = v;
-        } else {
-          held[o][fn][q] = v;
-        }
-      };
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float4 pv = P4[fm & 1][fn][q];
-          const float Pv[4] = {pv.x, pv.y, pv.z, pv.w};
-          float hv[4], dg[4], du[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float hf, fg, fu;
-            gated_act_grad(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit,
-                           hf, fg, fu);
-            hv[j] = bf16_to_f32(f32_to_bf16(hf));
-            dot += hv[j] * Pv[j];
-            const float dh = w * Pv[j];
-            du[j] = dh * fu;
-            dg[j] = dh * fg;
-          }
-          if (cv) {
-            uint2 hi, lo;
-            emit(0, fn, q, make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])));
-            split4(dg, hi, lo);
-            emit(1, fn, q, hi);
-            emit(2, fn, q, lo);
-            split4(du, hi, lo);
-            emit(3, fn, q, hi);
-            emit(4, fn, q, lo);
-          }
-        }
-      // the other half of this row's columns sits in lane ^ 32
-      dot += __shfl_xor(dot, 32, 64);
-      if (r < t.m_end && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
-      if (!cv) continue;
+      const int act = act_code(ACTK, p.act);
       const int row0 = t.m0 + wm * C::WTM + fm * 32;
+      // output o: 0 w h, 1 its remainder, 2 dg, 3 its remainder, 4 du, 5 its remainder
       auto flush = [&](int s, int o) {
-        uint16_t* out = (o == 0 ? p.Hrows : (o == 1 || o == 3) ? p.dGU : p.dGU_lo) + (o >= 3 ? p.I : 0);
-        const int ld = o == 0 ? p.I : 2 * p.I;
+        uint16_t* out = o == 0 ? p.hw : o == 1 ? p.hw_lo : (o & 1) ? p.dGU_lo + (o == 5 ? p.I : 0)
+                                                                    : p.dGU + (o == 4 ? p.I : 0);
+        const int ld = o < 2 ? p.I : 2 * p.I;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int idx = i * 64 + lane, rr = idx >> 2, ch = idx & 3;
@@ -339,33 +298,105 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
           if (row0 + rr < t.m_end) *reinterpret_cast<uint4*>(out + (size_t)(row0 + rr) * ld + col0 + ch * 8) = v;
         }
       };
-      auto put = [&](int s, const uint2 (&v)[C::FN][2]) {
+      if constexpr (ACTK == ACT_ANY) {
+        // the run-time activation (its switch needs registers): three rounds of two slots, each
+        // computing one quantity from the accumulators -- w h with the partial sum, dg, du
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
+        for (int o = 0; o < 6; o += 2) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) *slot(s, fn, q) = v[fn][q];
-      };
-      if constexpr (NSLOT >= 4) {
+          for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-        for (int o = 0; o < 4; ++o) flush(o, o);
-        put(0, held[0]);
-        flush(0, 4);
-      } else {
+            for (int q = 0; q < 2; ++q) {
+              const float4 pv = P4[fm & 1][fn][q];
+              const float Pv[4] = {pv.x, pv.y, pv.z, pv.w};
+              float v[4];
 #pragma unroll
-        for (int o0 = 0; o0 < 5; o0 += NSLOT) {
-#pragma unroll
-          for (int o = o0; o < o0 + NSLOT && o < 5; ++o) put(o - o0, held[o]);
-#pragma unroll
-          for (int o = o0; o < o0 + NSLOT && o < 5; ++o) flush(o - o0, o);
+              for (int j = 0; j < 4; ++j) {
+                const float g = acc[fm][fn][4 * q + j], u = acc[fm][fn][4 * q + 8 + j];
+                if (o == 0) {
+                  const float hv = bf16_to_f32(f32_to_bf16(gated_act(g, u, act, p.act_limit)));
+                  dot += hv * Pv[j];
+                  v[j] = w * hv;
+                } else {
+                  v[j] = w * Pv[j] * (o == 2 ? gated_act_dg(g, u, act, p.act_limit)
+                                             : gated_act_du(g, u, act, p.act_limit));
+                }
+              }
+              uint2 hi, lo;
+              split4(v, hi, lo);
+              *slot(0, fn, q) = hi;
+              *slot(1, fn, q) = lo;
+            }
+          if (o == 0) {
+            // the other half of this row's columns sits in lane ^ 32
+            dot += __shfl_xor(dot, 32, 64);
+            if (r < t.m_end && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
+          }
+          if (cv) {
+            flush(0, o);
+            flush(1, o + 1);
+          }
         }
+        continue;
       }
+      // round 1: w h and dg (values and remainders) into slots 0..3, and the partial sum
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float4 pv = P4[fm & 1][fn][q];
+          const float Pv[4] = {pv.x, pv.y, pv.z, pv.w};
+          float hw[4], dg[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float hf, fg, fu;
+            gated_act_grad(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act, p.act_limit, hf, fg, fu);
+            const float hv = bf16_to_f32(f32_to_bf16(hf));
+            dot += hv * Pv[j];
+            hw[j] = w * hv;
+            dg[j] = w * Pv[j] * fg;
+          }
+          if (cv) {
+            uint2 hi, lo;
+            split4(hw, hi, lo);
+            *slot(0, fn, q) = hi;
+            *slot(1, fn, q) = lo;
+            split4(dg, hi, lo);
+            *slot(2, fn, q) = hi;
+            *slot(3, fn, q) = lo;
+          }
+        }
+      // the other half of this row's columns sits in lane ^ 32
+      dot += __shfl_xor(dot, 32, 64);
+      if (r < t.m_end && lane < 32) p.dwt_part[(size_t)r * p.nparts + t.nt * C::WAVES_N + wn] = dot;
+      if (!cv) continue;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) flush(o, o);
+      // round 2: du (value and remainder) into slots 0..1 (a wave's LDS operations keep their order)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float4 pv = P4[fm & 1][fn][q];
+          const float Pv[4] = {pv.x, pv.y, pv.z, pv.w};
+          float du[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            du[j] = w * Pv[j] * gated_act_du(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act, p.act_limit);
+          uint2 hi, lo;
+          split4(du, hi, lo);
+          *slot(0, fn, q) = hi;
+          *slot(1, fn, q) = lo;
+        }
+      flush(0, 4);
+      flush(1, 5);
     }
   }
 };
 
-// The ungated (ReLU^2) recompute: U again; with P give h = bf16(max(U, 0)^2), the
-// router-weight partial sums <h, P> and du = w P 2 max(U, 0) as a bf16 value and a bf16
-// remainder.  A wave owns 64 columns.  The three bf16 outputs are staged through the wave's
+// The ungated (ReLU^2) recompute: U again; with P give, for h = bf16(max(U, 0)^2), the
+// router-weight partial sums <h, P>, w h and du = w P 2 max(U, 0), each as a bf16 value and a
+// bf16 remainder.  A wave owns 64 columns.  The three bf16 outputs are staged through the wave's
 // LDS scratch one after another, each computed from U and P as it goes (P is read once per
 // output: holding it across them would spill).
 template <class C, int PART = ROWS_ALL>
@@ -407,8 +438,18 @@ struct BwdRecomputeUpOps : RowOpsBase<C, RSrcX, RSrcUpW, PART> {
     if (!cv) return;
     const int row0 = t.m0 + wm * C::WTM;
     auto col_of = [](int fn, int q) { return fn * 32 + q * 8; };
-    stage_store_bf16<C, C::WTN, 4>(wlds, p.Hrows, p.I, row0, t.m_end, col0, p.I, lane,
-                                   [&](int fm, int fn, int q, int j) { return relu2(acc[fm][fn][4 * q + j]); }, col_of);
+    // w h with h = bf16(max(U, 0)^2), as a bf16 value and a bf16 remainder
+    auto hw = [&](int fm, int fn, int q, int j) {
+      return p.topk_w[p.row_slot[row_of(fm)]] * bf16_to_f32(f32_to_bf16(relu2(acc[fm][fn][4 * q + j])));
+    };
+    stage_store_bf16<C, C::WTN, 4>(wlds, p.hw, p.I, row0, t.m_end, col0, p.I, lane, hw, col_of);
+    stage_store_bf16<C, C::WTN, 4>(
+        wlds, p.hw_lo, p.I, row0, t.m_end, col0, p.I, lane,
+        [&](int fm, int fn, int q, int j) {
+          const float v = hw(fm, fn, q, j);
+          return v - bf16_to_f32(f32_to_bf16(v));
+        },
+        col_of);
     // du for item j of group q: w P 2 max(U, 0)
     auto du = [&](int fm, int fn, int q, int j) {
       const int rc = row_of(fm);
@@ -474,13 +515,18 @@ template <class C, int PART>
 using FwdGateUpOpsAny = FwdGateUpOps<C, PART, ACT_ANY>;
 template <class C>
 using BwdRecomputeOpsAny = BwdRecomputeOps<C, ROWS_ALL, ACT_ANY>;
+// the gated recompute with a run-time activation: 128 x 256 tiles, three 48 KB stages (its
+// activation switch does not fit the registers of 256-row tiles)
+using CfgRecAny = RowCfg<128, 256, 2, 4, 64, 3>;
 
 MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps)
 MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny)
 MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps)
 MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps)
 MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
-MOE_ROWS_KERNEL(k_bwd_recompute_act, BwdRecomputeOpsAny)
+__global__ void __launch_bounds__(CfgRecAny::NT) k_bwd_recompute_act(const GemmArgs p) {
+  rows_gemm_body<CfgRecAny, BwdRecomputeOpsAny<CfgRecAny>, GemmArgs>(p);
+}
 MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps)
 // the ungated (ReLU^2) expert
 MOE_ROWS_SPLIT_KERNEL(k_fwd_up, FwdUpOps)
@@ -524,8 +570,10 @@ hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_bwd_recompute_up, dim3(row_grid<CfgRecUp>(a, a.I)), dim3(CfgRecUp::NT), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_bwd_recompute : k_bwd_recompute_act, dim3(row_grid<CfgRows>(a, 2 * a.I)),
-                     dim3(CfgRows::NT), 0, s, a);
+  if (a.act == ACT_SWIGLU)
+    hipLaunchKernelGGL(k_bwd_recompute, dim3(row_grid<CfgRows>(a, 2 * a.I)), dim3(CfgRows::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_bwd_recompute_act, dim3(row_grid<CfgRecAny>(a, 2 * a.I)), dim3(CfgRecAny::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {

@@ -1,8 +1,11 @@
-// Weight-gradient GEMMs of the MoE backward on gfx950 bf16 MFMA, and the row
-// gather that feeds them.  With the contraction running over the rows routed
-// to expert e (LigerCute, "Backward pass": the expert-weight gradients):
-//   dW_down[e]           = sum_r h_r^T dO_r                 [I, H]
-//   [dW_gate | dW_up][e] = sum_r x_r^T [dg | du]_r          [H, 2I]
+// Weight-gradient GEMMs of the MoE backward on gfx950 bf16 MFMA.  With the contraction
+// running over the rows routed to expert e (LigerCute, "Backward pass": the expert-weight
+// gradients; row r has token t_r and routing weight w_r):
+//   dW_down[e]           = sum_r (w_r h_r)^T dY[t_r]           [I, H]
+//   [dW_gate | dW_up][e] = sum_r X[t_r]^T [dg | du]_r           [H, 2I]
+// The operands w h and [dg | du] are fp32 values carried as a bf16 value plus a bf16
+// remainder (two parts of the operand, both contracted); dY and X are bf16 inputs, read
+// straight from their token rows through row_token (no gathered copy).
 //
 // Both operands are "k-major": a k-tile is BK consecutive expert-major rows,
 // each contiguous along M (or N).  The rows are copied to LDS unchanged by the
@@ -28,25 +31,30 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // Tile configuration: BM x BN output tiles, WAVES_M x WAVES_N waves, BK-row
-// k-tiles, NST LDS stages.  A stage holds the A k-tile and NB B k-tiles that
-// share it (the B rows of every pass over the same rows).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NST_, int NB_>
+// k-tiles, NST LDS stages.  A stage holds the NA parts of the A k-tile and the NB
+// parts of the B k-tile; MFMA pass q multiplies A part min(q, NA-1) by B part
+// min(q, NB-1), all into the same accumulators.  IDS token ids of the tile's rows
+// sit in LDS for a gathered operand.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NST_, int NA_, int NB_>
 struct WgCfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M_ * WAVES_N_;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int BK = BK_, NST = NST_, NB = NB_;
-  static constexpr int A_SLOTS = BM * BK / 8, B_SLOTS = BN * BK / 8;   // 16-byte slots per stage
-  static constexpr int STAGE = A_SLOTS + NB * B_SLOTS;
-  static_assert(BK % 16 == 0 && NST * STAGE * 16 <= 150 * 1024, "k-tile and LDS budget");
+  static constexpr int BK = BK_, NST = NST_, NA = NA_, NB = NB_, NP = NA_ > NB_ ? NA_ : NB_;
+  static constexpr int A_SLOTS = BM * BK / 8, B_SLOTS = BN * BK / 8;   // 16-byte slots per stage and part
+  static constexpr int B_OFF = NA * A_SLOTS;                           // first B slot of a stage
+  static constexpr int STAGE = NA * A_SLOTS + NB * B_SLOTS;
+  static constexpr int IDS = 2048;
+  static_assert(BK % 16 == 0 && NST * STAGE * 16 + IDS * 4 <= 156 * 1024, "k-tile and LDS budget");
+  static_assert(IDS % BK == 0 && IDS >= NST * BK, "whole k-tiles per id window");
 };
-// 32-row k-tiles and three stages (two k-tiles in flight), 48 KB each: the A k-tile is
-// shared by the bf16 values and the bf16 remainders of the B operand (dO for dW_down,
-// [dg | du] for dW_gate/up), so that the exact value reaches the fp32 sums to about 2^-16.
-using CfgWgDown = WgCfg<256, 256, 2, 4, 32, 3, 2>;
-using CfgWgGateUp = WgCfg<256, 256, 2, 4, 32, 3, 2>;
+// 32-row k-tiles and three stages (two k-tiles in flight), 48 KB each.
+//   dW_down:    A = w h as bf16 value and remainder (two parts), B = dY token rows.
+//   dW_gate/up: A = X token rows, B = [dg | du] as bf16 value and remainder (two parts).
+using CfgWgDown = WgCfg<256, 256, 2, 4, 32, 3, 2, 1>;
+using CfgWgGateUp = WgCfg<256, 256, 2, 4, 32, 3, 1, 2>;
 
 // Chunk position in a k-major LDS row: chunk c of row r sits at c ^ tr_swz(r).
 // The flip of chunk-index bits 1-3 by r mod 4 makes the four rows one transpose
@@ -75,18 +83,23 @@ struct KMajorLoad {
     const int chunk = (lane % CPR) ^ tr_swz(r);
     colb = (uint32_t)min(c0 + chunk * 8, ncols - 8) * 2u;
   }
-  // Load instruction i of the k-tile whose row 0 is at `rows` (ld bytes per row; rows
-  // past `last` are read from row `last`) into the operand's LDS area at `lds`.
-  __device__ void issue(const uint8_t* rows, uint32_t ld, int last, uint4* lds, int i) const {
+  // The k-tile row (before clamping) that load instruction i of this lane covers.
+  __device__ int row(int i) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    return (i * C::NW + wave) * RPI + rsub;
+  }
+  // Load instruction i: this lane's chunk of the row at base + rowoff (bytes) into the operand's
+  // LDS area at `lds`.
+  __device__ void issue(const uint8_t* base, uint32_t rowoff, uint4* lds, int i) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = (i * C::NW + wave) * 64;
-    const int r = min(S / CPR + rsub, last);
-    lds_dma16(rows, (uint32_t)r * ld + colb, lds_addr(lds + S));
+    lds_dma16(base, rowoff + colb, lds_addr(lds + S));
   }
 };
 
-// Byte offsets (in a stage) of this lane's transpose reads for sub-step 0, read 0;
-// sub-step kk, read j is at + (16 kk + 4 j) row strides; B operand nb at + nb B_SLOTS.
+// Byte offsets (in a stage) of this lane's transpose reads for sub-step 0, read 0, part 0;
+// sub-step kk, read j is at + (16 kk + 4 j) row strides; A part na at + na A_SLOTS, B part nb at
+// + nb B_SLOTS.
 template <class C>
 struct TrFragAddr {
   static constexpr uint32_t RA = C::BM * 2, RB = C::BN * 2;       // row strides in bytes
@@ -104,7 +117,7 @@ struct TrFragAddr {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const int ch = (wn * C::WTN + fn * 32) / 8 + sub;
-      b[fn] = C::A_SLOTS * 16 + r * RB + (uint32_t)(ch ^ tr_swz(r)) * 16u + in;
+      b[fn] = C::B_OFF * 16 + r * RB + (uint32_t)(ch ^ tr_swz(r)) * 16u + in;
     }
   }
 };
@@ -118,21 +131,24 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* st, uint32_t off, uint32
 
 // One k-tile (BK / 16 MFMA sub-steps), operand reads of sub-step kk + 1 in flight
 // under the MFMAs of sub-step kk; the NLOAD load instructions of a later k-tile
-// are spread over the sub-steps (as in the row-grouped GEMMs).  Every B operand
-// accumulates into the same accumulators.
+// are spread over the sub-steps (as in the row-grouped GEMMs).  Every operand part
+// pair accumulates into the same accumulators.
 template <class C, bool LOADS, int NLOAD, class Issue>
 __device__ __forceinline__ void mma_ktile_tr(const lds_u8* st, const TrFragAddr<C>& fa,
                                              f32x16 (&acc)[C::FM][C::FN], Issue issue) {
   constexpr int KK = C::BK / 16;
-  constexpr int NR = 2 * (C::FM + C::NB * C::FN), NM = C::FM * C::NB * C::FN;
+  constexpr int NR = 2 * (C::NA * C::FM + C::NB * C::FN), NM = C::FM * C::NP * C::FN;
   constexpr int LPS = MOE_ROWS_LPS < NLOAD ? MOE_ROWS_LPS : NLOAD;
   constexpr int LPS_ = LPS * KK >= NLOAD ? LPS : (NLOAD + KK - 1) / KK;
   static_assert(!LOADS || LPS_ * KK >= NLOAD, "every load of the k-tile must be issued");
   constexpr uint32_t RA = TrFragAddr<C>::RA, RB = TrFragAddr<C>::RB;
-  bf16x8 a[2][C::FM], b[2][C::NB][C::FN];
+  bf16x8 a[2][C::NA][C::FM], b[2][C::NB][C::FN];
   auto load = [&](int kk, int buf) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) a[buf][fm] = tr_frag(st, fa.a[fm] + 16u * kk * RA, RA);
+    for (int na = 0; na < C::NA; ++na)
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+        a[buf][na][fm] = tr_frag(st, fa.a[fm] + na * C::A_SLOTS * 16u + 16u * kk * RA, RA);
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -147,13 +163,14 @@ __device__ __forceinline__ void mma_ktile_tr(const lds_u8* st, const TrFragAddr<
     if constexpr (kk + 1 < KK) load(kk + 1, (kk + 1) & 1);
     static_for<0, NL>([&](auto jc) { issue(J0 + decltype(jc)::value); });
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int q = 0; q < C::NP; ++q)
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn)
-          acc[fm][fn] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][nb][fn], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk & 1][q < C::NB ? q : C::NB - 1][fn],
+                                                                a[kk & 1][q < C::NA ? q : C::NA - 1][fm],
+                                                                acc[fm][fn], 0, 0, 0);
     constexpr int EARLY = kk + 1 < KK ? 2 : 0;
     if constexpr (kk + 1 < KK) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -166,16 +183,20 @@ __device__ __forceinline__ void mma_ktile_tr(const lds_u8* st, const TrFragAddr<
   });
 }
 
-// Ops: M, N of dW[e]; a_rows / b_rows(nb): row 0 of the expert-major operand
-// arrays (B operand nb of C::NB); lda / ldb in elements; epilogue.
+// Ops: M, N of dW[e]; lda / ldb in elements; A_GATHER / B_GATHER: whether the operand is read
+// from token rows through row_token (one part) or from expert-major rows (a_rows(p, na) /
+// b_rows(p, nb): row 0 of part na / nb; token rows: the matrix itself); epilogue.
 template <class C, class Ops>
 __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
   __shared__ uint4 smem[C::NST * C::STAGE];
+  __shared__ int ids[C::IDS];                         // row_token of rows [wbase, wbase + IDS) of the tile
+  constexpr bool GA = Ops::A_GATHER, GB = Ops::B_GATHER;
+  static_assert((!GA || C::NA == 1) && (!GB || C::NB == 1), "a gathered operand has one part");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   using AL = KMajorLoad<C, C::BM>;
   using BL = KMajorLoad<C, C::BN>;
-  constexpr int PERK = AL::PER + C::NB * BL::PER;     // load instructions per k-tile per wave
+  constexpr int PERK = C::NA * AL::PER + C::NB * BL::PER;   // load instructions per k-tile per wave
   const int M = Ops::M(p), N = Ops::N(p);
   const uint32_t lda = (uint32_t)Ops::lda(p) * 2u, ldb = (uint32_t)Ops::ldb(p) * 2u;
 
@@ -190,32 +211,68 @@ __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
   AL al;
   BL bl;
 
-  // k-tile kt of tile t: its row-0 pointers and last valid row
-  struct KT { const uint8_t* a; const uint8_t* b[C::NB]; int last; };
+  // Token ids of a window of IDS rows of the tile's expert (relative rows [wbase, wbase + IDS)),
+  // read by every thread; ends with a barrier.  (Plain loads: their wait also waits for the
+  // direct loads in flight, once per window.)
+  int ids_e = -1, wbase = 0;
+  auto load_ids = [&](const Tile& t, int base_row) {
+    const int n = min(C::IDS, t.k_hi - t.k_lo - base_row);
+    for (int i = threadIdx.x; i < n; i += C::NT) ids[i] = p.row_token[t.k_lo + base_row + i];
+    __syncthreads();
+    ids_e = t.e;
+    wbase = base_row;
+  };
+
+  // k-tile kt of tile t: first row (relative to the expert's), last valid row of the k-tile, and
+  // for the gathered operand the byte offset of each of this lane's rows in the token matrix
+  constexpr int GPER = GA ? AL::PER : GB ? BL::PER : 1;
+  struct KT { int row0; int last; uint32_t goff[GPER]; };
   auto ktile = [&](const Tile& t, int kt) {
-    const int row0 = t.k_lo + kt * C::BK;
     KT r;
-    r.last = min(C::BK, t.k_hi - row0) - 1;
-    r.a = reinterpret_cast<const uint8_t*>(Ops::a_rows(p)) + (size_t)row0 * lda;
+    r.row0 = kt * C::BK;
+    r.last = min(C::BK, t.k_hi - t.k_lo - r.row0) - 1;
+    if constexpr (GA || GB) {
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) r.b[nb] = reinterpret_cast<const uint8_t*>(Ops::b_rows(p, nb)) + (size_t)row0 * ldb;
+      for (int i = 0; i < GPER; ++i) {
+        const int rr = min(GA ? al.row(i) : bl.row(i), r.last);
+        r.goff[i] = (uint32_t)ids[r.row0 + rr - wbase] * (GA ? lda : ldb);
+      }
+    }
     return r;
   };
-  auto issue_one = [&](const KT& k, uint4* st, int j) {
-    if (j < AL::PER) {
-      al.issue(k.a, lda, k.last, st, j);
+  auto issue_one = [&](const Tile& t, const KT& k, uint4* st, int j) {
+    if (j < C::NA * AL::PER) {
+      const int na = j / AL::PER, i = j % AL::PER;
+      uint4* dst = st + na * C::A_SLOTS;
+      if constexpr (GA) {
+        al.issue(reinterpret_cast<const uint8_t*>(Ops::a_rows(p, 0)), k.goff[i], dst, i);
+      } else {
+        const uint8_t* rows = reinterpret_cast<const uint8_t*>(Ops::a_rows(p, na)) + (size_t)(t.k_lo + k.row0) * lda;
+        al.issue(rows, (uint32_t)min(al.row(i), k.last) * lda, dst, i);
+      }
     } else {
-      const int nb = (j - AL::PER) / BL::PER, i = (j - AL::PER) % BL::PER;
-      bl.issue(k.b[nb], ldb, k.last, st + C::A_SLOTS + nb * C::B_SLOTS, i);
+      const int jb = j - C::NA * AL::PER;
+      const int nb = jb / BL::PER, i = jb % BL::PER;
+      uint4* dst = st + C::B_OFF + nb * C::B_SLOTS;
+      if constexpr (GB) {
+        bl.issue(reinterpret_cast<const uint8_t*>(Ops::b_rows(p, 0)), k.goff[i], dst, i);
+      } else {
+        const uint8_t* rows = reinterpret_cast<const uint8_t*>(Ops::b_rows(p, nb)) + (size_t)(t.k_lo + k.row0) * ldb;
+        bl.issue(rows, (uint32_t)min(bl.row(i), k.last) * ldb, dst, i);
+      }
     }
   };
+  // the first NST - 1 k-tiles of tile t (with its first id window in LDS)
   auto prologue = [&](const Tile& t, int nk) {
+    if constexpr (GA || GB) {
+      if (t.e != ids_e || wbase != 0) load_ids(t, 0);
+    }
 #pragma unroll
     for (int s = 0; s < C::NST - 1; ++s)
       if (s < nk) {
         const KT k = ktile(t, s);
 #pragma unroll
-        for (int j = 0; j < PERK; ++j) issue_one(k, smem + s * C::STAGE, j);
+        for (int j = 0; j < PERK; ++j) issue_one(t, k, smem + s * C::STAGE, j);
       }
   };
 
@@ -240,22 +297,29 @@ __device__ __forceinline__ void wgrad_body(const GemmArgs& p) {
       else wait_ktiles<C::NST, PERK>(ahead < C::NST - 2 ? ahead : C::NST - 2);
       __syncthreads();
       uint4* cur = smem + (kt % C::NST) * C::STAGE;
-      const int last = ktile(tl, kt).last;
+      const int last = min(C::BK, tl.k_hi - tl.k_lo - kt * C::BK) - 1;
       if (last < C::BK - 1) {
-        // rows past the segment: zeros in every B operand
+        // rows past the segment: zeros in every B part
         const int n = (C::BK - 1 - last) * BL::CPR;
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          uint4* zb = cur + C::A_SLOTS + nb * C::B_SLOTS + (last + 1) * BL::CPR;
+          uint4* zb = cur + C::B_OFF + nb * C::B_SLOTS + (last + 1) * BL::CPR;
           for (int i = threadIdx.x; i < n; i += C::NT) zb[i] = make_uint4(0, 0, 0, 0);
         }
         __syncthreads();
       }
       KT nx = {};
       const int nxt = kt + C::NST - 1;
-      if constexpr (decltype(loads)::value) nx = ktile(tl, nxt);
+      if constexpr (decltype(loads)::value) {
+        // a gathered operand's next k-tile outside the id window: the next window (all waves are
+        // past their reads of the current one)
+        if constexpr (GA || GB) {
+          if ((nxt + 1) * C::BK > wbase + C::IDS) load_ids(tl, nxt * C::BK);
+        }
+        nx = ktile(tl, nxt);
+      }
       uint4* st = smem + (nxt % C::NST) * C::STAGE;
-      auto issue = [&](int j) { issue_one(nx, st, j); };
+      auto issue = [&](int j) { issue_one(tl, nx, st, j); };
       mma_ktile_tr<C, decltype(loads)::value, PERK>(lds + (kt % C::NST) * C::STAGE * 16, fa, acc, issue);
     };
     // the last NST - 1 k steps issue nothing: peeled, not branched
@@ -290,15 +354,16 @@ __device__ __forceinline__ void wg_store(uint8_t* wlds, uint16_t* out, int ld, i
       [](int fn, int q) { return fn * 32 + q * 8; });
 }
 
-// dW_down[e] = sum_r h_r^T dO_r with dO_r = w_r dY[t_r]: A = h rows [A, I], B = dO rows [A, H]
-// as bf16 values (nb = 0) and bf16 remainders (nb = 1).
+// dW_down[e] = sum_r (w_r h_r)^T dY[t_r]: A = w h rows [A, I] as bf16 values (na = 0) and bf16
+// remainders (na = 1), B = dY token rows [T, H] through row_token.
 struct WgDownOps {
+  static constexpr bool A_GATHER = false, B_GATHER = true;
   __device__ static int M(const GemmArgs& p) { return p.I; }
   __device__ static int N(const GemmArgs& p) { return p.H; }
   __device__ static int lda(const GemmArgs& p) { return p.I; }
   __device__ static int ldb(const GemmArgs& p) { return p.H; }
-  __device__ static const uint16_t* a_rows(const GemmArgs& p) { return p.Hrows; }
-  __device__ static const uint16_t* b_rows(const GemmArgs& p, int nb) { return nb ? p.dO_lo : p.dO; }
+  __device__ static const uint16_t* a_rows(const GemmArgs& p, int na) { return na ? p.hw_lo : p.hw; }
+  __device__ static const uint16_t* b_rows(const GemmArgs& p, int) { return p.dY; }
   template <class C>
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
                                   int lane, uint8_t* wlds) {
@@ -307,15 +372,16 @@ struct WgDownOps {
   }
 };
 
-// [dW_gate | dW_up][e] = sum_r x_r^T [dg | du]_r: A = gathered x rows [A, H],
+// [dW_gate | dW_up][e] = sum_r X[t_r]^T [dg | du]_r: A = X token rows [T, H] through row_token,
 // B = [dg | du] rows [A, 2I] as bf16 values (nb = 0) and bf16 remainders (nb = 1).
 // The ungated (ReLU^2) expert has du rows [A, I] only and gets dW_up alone.
 struct WgGateUpOps {
+  static constexpr bool A_GATHER = true, B_GATHER = false;
   __device__ static int M(const GemmArgs& p) { return p.H; }
   __device__ static int N(const GemmArgs& p) { return act_gated(p.act) ? 2 * p.I : p.I; }
   __device__ static int lda(const GemmArgs& p) { return p.H; }
   __device__ static int ldb(const GemmArgs& p) { return N(p); }
-  __device__ static const uint16_t* a_rows(const GemmArgs& p) { return p.Xg; }
+  __device__ static const uint16_t* a_rows(const GemmArgs& p, int) { return p.X; }
   __device__ static const uint16_t* b_rows(const GemmArgs& p, int nb) { return nb ? p.dGU_lo : p.dGU; }
   template <class C>
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
@@ -337,57 +403,6 @@ __global__ void __launch_bounds__(CfgWgGateUp::NT) k_bwd_dw_gateup(const GemmArg
   wgrad_body<CfgWgGateUp, WgGateUpOps>(p);
 }
 
-// Expert-major operand rows of the weight-gradient GEMMs, one wave per row r:
-// Xg[r] = X[token], dO[r] = bf16(w * dY[token]) and dO_lo[r] = bf16(w * dY[token] - dO[r])
-// (w = the row's top-k weight).  Rows past the last expert's (expert_offsets[E]) have no token.
-constexpr int GATHER_UNROLL = 8;    // 16-byte chunks of a row per lane and batch (H = 4096: the whole row)
-typedef uint32_t gather_u4 __attribute__((ext_vector_type(4)));   // a register value (uint4 arrays go to scratch)
-
-__global__ void __launch_bounds__(256) k_bwd_gather(const GemmArgs p) {
-  const long A = p.offsets[p.E];
-  const int chunks = p.H / 8;
-  const int lane = threadIdx.x & 63;
-  for (long r = blockIdx.x * 4L + (threadIdx.x >> 6); r < A; r += gridDim.x * 4L) {
-    const int tok = p.row_token[r];
-    const float w = p.topk_w[p.row_slot[r]];
-    const gather_u4* x = reinterpret_cast<const gather_u4*>(p.X + (size_t)tok * p.H);
-    const gather_u4* dy = reinterpret_cast<const gather_u4*>(p.dY + (size_t)tok * p.H);
-    gather_u4* xg = reinterpret_cast<gather_u4*>(p.Xg + (size_t)r * p.H);
-    gather_u4* dO = reinterpret_cast<gather_u4*>(p.dO + (size_t)r * p.H);
-    gather_u4* dOl = reinterpret_cast<gather_u4*>(p.dO_lo + (size_t)r * p.H);
-    // GATHER_UNROLL chunks of both rows per lane in flight before any store
-    for (int c0 = 0; c0 < chunks; c0 += 64 * GATHER_UNROLL) {
-      gather_u4 xv[GATHER_UNROLL], dv[GATHER_UNROLL];
-#pragma unroll
-      for (int u = 0; u < GATHER_UNROLL; ++u) {
-        const int c = c0 + u * 64 + lane;
-        const int cc = c < chunks ? c : 0;          // in-bounds reads for lanes past the row
-        xv[u] = x[cc];
-        dv[u] = dy[cc];
-      }
-#pragma unroll
-      for (int u = 0; u < GATHER_UNROLL; ++u) {
-        // a lane past the row stores chunk 0 again, with the values lane 0 stores there: no
-        // branch around the stores
-        const int c = c0 + u * 64 + lane;
-        const int cc = c < chunks ? c : 0;
-        const gather_u4 v = dv[u];
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a = w * bf16_to_f32(d[q] & 0xffffu), b = w * bf16_to_f32(d[q] >> 16);
-          hi[q] = pack_bf16x2(a, b);
-          lo[q] = pack_bf16x2(a - bf16_to_f32(hi[q] & 0xffffu), b - bf16_to_f32(hi[q] >> 16));
-        }
-        xg[cc] = xv[u];
-        dO[cc] = gather_u4{hi[0], hi[1], hi[2], hi[3]};
-        dOl[cc] = gather_u4{lo[0], lo[1], lo[2], lo[3]};
-      }
-    }
-  }
-}
-
 template <class C>
 static int wgrad_grid(const GemmArgs& a, int M, int N) {
   long tiles = (long)a.E * ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
@@ -396,14 +411,6 @@ static int wgrad_grid(const GemmArgs& a, int M, int N) {
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
 
-hipError_t launch_bwd_gather(const GemmArgs& a, hipStream_t s) {
-  long rows = (long)a.T * a.k;
-  long blocks = (rows + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(k_bwd_gather, dim3((int)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_bwd_dw_down, dim3(wgrad_grid<CfgWgDown>(a, a.I, a.H)), dim3(CfgWgDown::NT), 0, s, a);
   return hipGetLastError();

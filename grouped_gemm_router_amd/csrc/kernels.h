@@ -24,15 +24,14 @@ struct GemmArgs {
   const uint16_t* Wg;     // [E, H, I]
   const uint16_t* Wu;     // [E, H, I]
   const uint16_t* Wd;     // [E, I, H]
-  uint16_t* Hrows;        // [A, I]
+  uint16_t* Hrows;        // [A, I]  h (forward)
   uint16_t* Orows;        // [A, H]
+  uint16_t* hw;           // [A, I]  bf16(w h) (backward; w = the row's top-k weight)
+  uint16_t* hw_lo;        // [A, I]  bf16 of its remainder, w h - bf16(w h)
   float* P;               // [A, I]
   uint16_t* dGU;          // [A, 2I]  bf16(dg) | bf16(du)
   uint16_t* dGU_lo;       // [A, 2I]  bf16 of the remainders (dg - bf16(dg), du - bf16(du))
   float* dXr;             // [A, H]
-  uint16_t* Xg;           // [A, H]  X[token] per expert-major row
-  uint16_t* dO;           // [A, H]  bf16(w * dY[token]) per expert-major row
-  uint16_t* dO_lo;        // [A, H]  bf16 of its remainder, w * dY[token] - bf16(w * dY[token])
   float* dwt_part;        // [A, nparts]
   int nparts;
   uint16_t* dWg;
@@ -65,7 +64,6 @@ hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s);
-hipError_t launch_bwd_gather(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s);
 // router-weight partial sums per row of the recompute (its column tiles times waves across)
