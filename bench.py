@@ -204,7 +204,7 @@ def measure(cfg, args, device_draw=False):
     X = torch.from_numpy(X_np.view(np.int16)).cuda().view(torch.bfloat16)
     dY = torch.from_numpy(dY_np.view(np.int16)).cuda().view(torch.bfloat16) if cfg.backward else None
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation,
-                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"], keep_math=cfg.backward)
+                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"])
     del W
     torch.cuda.synchronize()
 

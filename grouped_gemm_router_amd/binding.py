@@ -59,7 +59,7 @@ def _load() -> ctypes.CDLL:
         "moe_mx_quantize": (ctypes.c_int, [P, I64, I32, P, P, P]),
         "moe_expert_mlp": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_combine": (ctypes.c_int, [P, P, P, I32, I32, I32, P, P]),
-        "moe_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_gemm": (ctypes.c_int, [I32, P, I32, I64, I32, I32, P, P, P, P, P, P]),
         "moe_expert_mlp_static": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
     }
@@ -265,18 +265,17 @@ def combine(O_rows, slot_row, topk_w, Y=None):
     return Y
 
 
-def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, W_gate, W_up, W_down, Wg_t, Wu_t,
+def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, Wg_t, Wu_t, Wd_t,
              out=None, ws=None, activation="swiglu", act_limit=0.0):
-    """Returns (dX, dW_gate, dW_up, dW_down, d_topk_w); for ReLU^2 W_gate and Wg_t are None
-    and so is dW_gate."""
+    """Returns (dX, dW_gate, dW_up, dW_down, d_topk_w) from the packed weights Wg_t, Wu_t
+    [E, I, H] and Wd_t [E, H, I] (pack_weights); for ReLU^2 Wg_t is None and so is dW_gate."""
     T, H = X.shape
-    E, _, I = W_up.shape
+    E, I, _ = Wu_t.shape
     k = topk_w.shape[1]
     gated = activation not in UNGATED
-    for name, t, shape in (("X", X, (T, H)), ("dY", dY, (T, H)), ("W_gate", W_gate, (E, H, I)),
-                           ("W_up", W_up, (E, H, I)), ("W_down", W_down, (E, I, H)),
-                           ("Wg_t", Wg_t, (E, I, H)), ("Wu_t", Wu_t, (E, I, H))):
-        if gated or name not in ("W_gate", "Wg_t"):
+    for name, t, shape in (("X", X, (T, H)), ("dY", dY, (T, H)), ("Wg_t", Wg_t, (E, I, H)),
+                           ("Wu_t", Wu_t, (E, I, H)), ("Wd_t", Wd_t, (E, H, I))):
+        if gated or name != "Wg_t":
             _expect(t, name, torch.bfloat16, shape)
     _expect(topk_w, "topk_w", torch.float32, (T, k))
     for name, t in (("row_token", row_token), ("row_slot", row_slot), ("slot_row", slot_row)):
@@ -296,7 +295,7 @@ def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, W_gate, W_up
     else:
         n = ws.numel()
     _check("moe_backward", lib.moe_backward(ctypes.byref(p), _ptr(X), _ptr(dY), _ptr(topk_w), _ptr(row_token),
-                                            _ptr(row_slot), _ptr(slot_row), _ptr(offsets), _ptr(W_gate),
-                                            _ptr(W_up), _ptr(W_down), _ptr(Wg_t), _ptr(Wu_t), _ptr(dX),
-                                            _ptr(dWg), _ptr(dWu), _ptr(dWd), _ptr(dtw), _ptr(ws), n, _stream()))
+                                            _ptr(row_slot), _ptr(slot_row), _ptr(offsets), _ptr(Wg_t),
+                                            _ptr(Wu_t), _ptr(Wd_t), _ptr(dX), _ptr(dWg), _ptr(dWu), _ptr(dWd),
+                                            _ptr(dtw), _ptr(ws), n, _stream()))
     return dX, dWg, dWu, dWd, dtw

@@ -343,17 +343,15 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
 
 MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY, const float* topk_w,
                                 const int32_t* row_token, const int32_t* row_slot, const int32_t* slot_row,
-                                const int32_t* expert_offsets, const void* W_gate, const void* W_up,
-                                const void* W_down, const void* Wg_t, const void* Wu_t, void* dX,
-                                void* dW_gate, void* dW_up, void* dW_down, float* d_topk_w, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                const void* Wd_t, void* dX, void* dW_gate, void* dW_up, void* dW_down,
+                                float* d_topk_w, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
   if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
   const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
   const bool rows = p->T > 0;                            // token-sized arrays may be NULL for T = 0
-  if (!expert_offsets || (gated && !W_gate) || !W_up || !W_down || (gated && !Wg_t) || !Wu_t ||
-      (gated && !dW_gate) || !dW_up || !dW_down)
+  if (!expert_offsets || (gated && !Wg_t) || !Wu_t || !Wd_t || (gated && !dW_gate) || !dW_up || !dW_down)
     return MOE_ERR_INVALID_ARG;
   if (rows && (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !dX || !d_topk_w))
     return MOE_ERR_INVALID_ARG;
@@ -373,9 +371,7 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   a.dY = (const uint16_t*)dY;
   a.Wg_t = (const uint16_t*)Wg_t;
   a.Wu_t = (const uint16_t*)Wu_t;
-  a.Wg = (const uint16_t*)W_gate;
-  a.Wu = (const uint16_t*)W_up;
-  a.Wd = (const uint16_t*)W_down;
+  a.Wd_t = (const uint16_t*)Wd_t;
   a.nparts = moe::bwd_nparts(p->I, p->activation);
   a.P = (float*)w8;
   w8 += align_up(A * I * 4);

@@ -91,14 +91,6 @@ struct RSrcDU2 {
     return (uint32_t)clamp_row(t, row) * (uint32_t)p.I;
   }
 };
-struct RSrcUpWT2 {       // W_up [E, H, I] read twice along K, as [E, N = H, K = 2I]
-  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
-    return p.Wu + (size_t)t.e * p.H * p.I + (k0 < p.I ? k0 : k0 - p.I);
-  }
-  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
-    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
-  }
-};
 struct RSrcDownW {       // packed [E, H, I]
   __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
     return p.Wd_t + (size_t)t.e * p.H * p.I + k0;
@@ -107,22 +99,29 @@ struct RSrcDownW {       // packed [E, H, I]
     return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
   }
 };
-struct RSrcDownWT {      // W_down [E, I, H] read as [E, N = I, K = H]
-  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
-    return p.Wd + (size_t)t.e * p.I * p.H + k0;
+// k-major B sources of the backward's row GEMMs: the packed weights (the forward's layout)
+// read transposed, so the backward needs no math-layout copy (KMajorRowsB).
+struct KSrcDownWt {      // W_down^T: Wd_t [E, H, I] as [K = H, N = I]
+  __device__ static const uint16_t* kbase(const GemmArgs& p, const Tile& t, int k0) {
+    return p.Wd_t + (size_t)t.e * p.H * p.I + (size_t)k0 * p.I;
   }
-  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
-    return (uint32_t)min(t.n0 + row, p.I - 1) * (uint32_t)p.H;
-  }
+  __device__ static int ld(const GemmArgs& p) { return p.I; }
+  __device__ static int ncols(const GemmArgs& p) { return p.I; }
 };
-struct RSrcGateUpWT {    // [W_gate | W_up] [E, H, I] read as [E, N = H, K = 2I]
-  __device__ static const uint16_t* base(const GemmArgs& p, const Tile& t, int, int k0) {
-    const size_t e0 = (size_t)t.e * p.H * p.I;
-    return k0 < p.I ? p.Wg + e0 + k0 : p.Wu + e0 + (k0 - p.I);
+struct KSrcGateUpWt {    // [W_gate | W_up]^T: [Wg_t | Wu_t] [E, I, H] as [K = 2I, N = H]
+  __device__ static const uint16_t* kbase(const GemmArgs& p, const Tile& t, int k0) {
+    const size_t e0 = (size_t)t.e * p.I * p.H;
+    return k0 < p.I ? p.Wg_t + e0 + (size_t)k0 * p.H : p.Wu_t + e0 + (size_t)(k0 - p.I) * p.H;
   }
-  __device__ static uint32_t row_off(const GemmArgs& p, const Tile& t, int row) {
-    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)p.I;
+  __device__ static int ld(const GemmArgs& p) { return p.H; }
+  __device__ static int ncols(const GemmArgs& p) { return p.H; }
+};
+struct KSrcUpWt2 {       // W_up^T twice along K: Wu_t [E, I, H] as [K = 2I, N = H] (ReLU^2 dX)
+  __device__ static const uint16_t* kbase(const GemmArgs& p, const Tile& t, int k0) {
+    return p.Wu_t + (size_t)t.e * p.I * p.H + (size_t)(k0 < p.I ? k0 : k0 - p.I) * p.H;
   }
+  __device__ static int ld(const GemmArgs& p) { return p.H; }
+  __device__ static int ncols(const GemmArgs& p) { return p.H; }
 };
 
 // ------------------------------------------------------------------------
@@ -211,10 +210,11 @@ struct FwdDownOps : RowOpsBase<C, RSrcH, RSrcDownW, PART> {
   }
 };
 
-// P = dY[token] W_down^T (fp32)
+// P = dY[token] W_down^T (fp32), W_down^T read from the packed Wd_t
 template <class C, int PART = ROWS_ALL>
-struct BwdPOps : RowOpsBase<C, RSrcDY, RSrcDownWT, PART> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcDY, RSrcDownWT, PART>::Sched& s,
+struct BwdPOps : RowOpsBase<C, RSrcDY, KSrcDownWt, PART> {
+  static constexpr bool B_KMAJOR = true;
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDY, KSrcDownWt, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.I, p.H, pre, red);
   }
@@ -471,8 +471,9 @@ struct BwdRecomputeUpOps : RowOpsBase<C, RSrcX, RSrcUpW, PART> {
 // remainder (two passes over I): ReLU^2's du = w P 2 max(U, 0) reaches several units, and
 // its bf16 value alone leaves dX short of the exact-du result near cancellations
 template <class C, int PART = ROWS_ALL>
-struct BwdDXUpOps : RowOpsBase<C, RSrcDU2, RSrcUpWT2, PART> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcDU2, RSrcUpWT2, PART>::Sched& s,
+struct BwdDXUpOps : RowOpsBase<C, RSrcDU2, KSrcUpWt2, PART> {
+  static constexpr bool B_KMAJOR = true;
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDU2, KSrcUpWt2, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, 2 * p.I, pre, red);
   }
@@ -482,10 +483,11 @@ struct BwdDXUpOps : RowOpsBase<C, RSrcDU2, RSrcUpWT2, PART> {
   }
 };
 
-// dXr = [dg | du] [W_gate | W_up]^T (fp32 rows)
+// dXr = [dg | du] [W_gate | W_up]^T (fp32 rows), the weights read from the packed Wg_t, Wu_t
 template <class C, int PART = ROWS_ALL>
-struct BwdDXOps : RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART> {
-  __device__ static void init_sched(typename RowOpsBase<C, RSrcDGU, RSrcGateUpWT, PART>::Sched& s,
+struct BwdDXOps : RowOpsBase<C, RSrcDGU, KSrcGateUpWt, PART> {
+  static constexpr bool B_KMAJOR = true;
+  __device__ static void init_sched(typename RowOpsBase<C, RSrcDGU, KSrcGateUpWt, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, 2 * p.I, pre, red);
   }

@@ -56,6 +56,41 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
+// k-major operand tiles (rows along the contraction axis, contiguous along M or N) and
+// their MFMA operand reads.  ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the four-element pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4.  Pointing lane s of a group at row kb + s / 4, columns c0 + 4 (s % 4) .. + 3
+// therefore gives lane i column c0 + i of rows kb .. kb + 3 -- half of the eight k values a
+// lane of v_mfma_f32_32x32x16_bf16 holds (tr_frag reads both halves).
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Chunk position in a k-major LDS row: chunk c of row r sits at c ^ tr_swz(r).
+// The flip of chunk-index bits 1-3 by r mod 4 makes the four rows one transpose
+// read touches land in different banks, for both 16- and 32-lane LDS phases.
+__device__ __forceinline__ int tr_swz(int r) { return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0); }
+
+// Eight k values of one operand lane from a k-major tile: rows off and off + 4 row strides.
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* st, uint32_t off, uint32_t rs) {
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + off));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + off + 4 * rs));
+  const v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Byte offset, inside a k-major tile of `cols` columns (row stride 2 cols bytes), of this
+// lane's transpose read for the 32 columns starting at col0, sub-step 0 (sub-step kk: + 16 kk
+// row strides).
+__device__ __forceinline__ uint32_t tr_offset(int col0, int cols, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int r = 8 * (g >> 1) + (s >> 2);              // k row (lanes 32-63: k + 8)
+  const int sub = 2 * (g & 1) + ((s & 3) >> 1);       // chunk within the 32-column fragment
+  const int ch = col0 / 8 + sub;
+  return (uint32_t)r * (uint32_t)(cols * 2) + (uint32_t)(ch ^ tr_swz(r)) * 16u + 8u * (s & 1);
+}
+
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -107,11 +142,46 @@ struct DirectRows {
   }
 };
 
+// Loader of a k-major B operand of the row-grouped GEMMs: the BK x BN k-tile of a [K, N]
+// matrix whose k-rows are contiguous along N (the packed weights read transposed).  Src
+// provides kbase(p, tile, k0) (wave-uniform pointer to element (k0, 0) of the expert's
+// matrix), ld(p) (elements per k-row) and ncols(p) (N); columns past N read column N - 8.
+// Load instruction i of wave w fills LDS slots [64 (i NW + w), + 64): k-rows RPI (i NW + w)
+// + lane / CPR, 16-byte chunk c of a row at position c ^ tr_swz(row).
+template <class C, class Src, class P>
+struct KMajorRowsB {
+  static constexpr int CPR = C::BN / 8;                 // 16-byte chunks per k-row
+  static constexpr int RPI = 64 / CPR;                  // k-rows per load instruction
+  static constexpr int INST = C::BK * CPR / 64;
+  static constexpr int PER = INST / C::NW;
+  static_assert(CPR >= 16 && 64 % CPR == 0 && INST % C::NW == 0 && (RPI * C::NW) % 4 == 0, "k-major B tile");
+  uint32_t colb;                                        // byte offset of this lane's chunk in a k-row
+  int rsub;
+  __device__ void init(const P& p, const Tile& tl) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rsub = lane / CPR;
+    const int r = RPI * wave + rsub;                    // this lane's rows are r mod 4 for every i
+    const int chunk = (lane % CPR) ^ tr_swz(r);
+    colb = (uint32_t)min(tl.n0 + chunk * 8, Src::ncols(p) - 8) * 2u;
+  }
+  __device__ void issue_one(const P& p, const Tile& tl, int k0, uint4* lds, int i) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (i * C::NW + wave) * 64;
+    const uint8_t* b = reinterpret_cast<const uint8_t*>(Src::kbase(p, tl, k0));
+    lds_dma16(b, (uint32_t)(S / CPR + rsub) * (uint32_t)Src::ld(p) * 2u + colb, lds_addr(lds + S));
+  }
+  __device__ void issue(const P& p, const Tile& tl, int k0, uint4* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) issue_one(p, tl, k0, lds, i);
+  }
+};
+
 // Byte offsets of this lane's MFMA operand chunks inside a stage, for sub-step 0.
 // Chunk c of row r sits at position c ^ swz(r); a lane of half h reads chunk
 // 2 kk + h = (2 kk) ^ h at sub-step kk, so its position is (swz(r) ^ h) ^ 2 kk and
 // the byte offset is base ^ (32 kk): one XOR per read, no per-sub-step table.
-template <class C>
+// With BKM the B tile is k-major (KMajorRowsB) and b[] are its transpose-read offsets.
+template <class C, bool BKM = false>
 struct FragAddr {
   uint32_t a[C::FM], b[C::FN];
   __device__ void init(int wm, int wn, int lane) {
@@ -123,8 +193,12 @@ struct FragAddr {
     }
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int r = wn * C::WTN + fn * 32 + (lane & 31);
-      b[fn] = (uint32_t)(C::A_SLOTS + r * C::CPR + (swz<C::CPR>(r) ^ h)) * 16u;
+      if constexpr (BKM) {
+        b[fn] = (uint32_t)C::A_SLOTS * 16u + tr_offset(wn * C::WTN + fn * 32, C::BN, lane);
+      } else {
+        const int r = wn * C::WTN + fn * 32 + (lane & 31);
+        b[fn] = (uint32_t)(C::A_SLOTS + r * C::CPR + (swz<C::CPR>(r) ^ h)) * 16u;
+      }
     }
   }
 };
@@ -134,11 +208,11 @@ struct FragAddr {
 // NLOAD global->LDS load instructions of a later k-tile (issue(j), j < NLOAD)
 // are spread over the sub-steps, one between two MFMAs, so that no wave stalls
 // on a burst of vector-memory issues before its MFMAs.
-template <class C, bool LOADS, int NLOAD, class Issue>
-__device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragAddr<C>& fa,
+template <class C, bool LOADS, int NLOAD, bool BKM, class Issue>
+__device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragAddr<C, BKM>& fa,
                                                f32x16 (&acc)[C::FM][C::FN], Issue issue) {
   constexpr int KK = C::BK / 16;
-  constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+  constexpr int NR = C::FM + (BKM ? 2 : 1) * C::FN, NM = C::FM * C::FN;
   constexpr int LPS = MOE_ROWS_LPS < NLOAD ? MOE_ROWS_LPS : NLOAD;   // loads per sub-step, front-loaded
   static_assert(!LOADS || LPS * KK >= NLOAD, "every load of the k-tile must be issued");
   bf16x8 a[2][C::FM], b[2][C::FN];
@@ -147,8 +221,12 @@ __device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragA
     for (int fm = 0; fm < C::FM; ++fm)
       a[buf][fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.a[fm] ^ (32u * kk))));
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-      b[buf][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.b[fn] ^ (32u * kk))));
+    for (int fn = 0; fn < C::FN; ++fn) {
+      if constexpr (BKM)
+        b[buf][fn] = tr_frag((const lds_u8*)stage, fa.b[fn] + 16u * kk * (C::BN * 2), C::BN * 2);
+      else
+        b[buf][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.b[fn] ^ (32u * kk))));
+    }
   };
   load(0, 0);
   static_for<0, KK>([&](auto kkc) {
@@ -215,6 +293,13 @@ struct RowEpiLds {
 // block scan's partial sums.
 constexpr int SCHED_LDS_INTS = 1024 + 1 + 16 + 1;
 
+// Whether Ops' B operand is k-major (Ops::B_KMAJOR, false when absent): loaded by KMajorRowsB
+// and read with transpose reads.
+template <class T, class = void>
+struct BKMajor : std::false_type {};
+template <class T>
+struct BKMajor<T, std::void_t<decltype(T::B_KMAJOR)>> : std::bool_constant<T::B_KMAJOR> {};
+
 // Whether Ops takes the two-stage schedule that issues the next tile's first k-tile in the
 // last k step (Ops::EARLY_NEXT, true when absent): an epilogue that already needs every
 // register keeps the plain schedule.
@@ -231,8 +316,9 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
   static_assert(C::NT / 64 <= 16, "schedule scratch");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  constexpr bool BKM = BKMajor<Ops>::value;
   using AL = DirectRows<C, C::BM, typename Ops::SrcA, P>;
-  using BL = DirectRows<C, C::BN, typename Ops::SrcB, P>;
+  using BL = std::conditional_t<BKM, KMajorRowsB<C, typename Ops::SrcB, P>, DirectRows<C, C::BN, typename Ops::SrcB, P>>;
   constexpr int PERK = AL::PER + BL::PER;                 // real load instructions per k-tile per wave
 
   typename Ops::Sched sched;
@@ -241,7 +327,7 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
   carry = walk.init(sched.total, carry);
   if (!walk.valid()) return;
   Tile tl = sched.tile(walk.t);
-  FragAddr<C> fa;
+  FragAddr<C, BKM> fa;
   fa.init(wm, wn, lane);
   AL al;
   BL bl;
@@ -282,7 +368,7 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
           if (j < AL::PER) al.issue_one(p, cur_tile, k0, st, j);
           else bl.issue_one(p, cur_tile, k0, st + C::A_SLOTS, j - AL::PER);
         };
-        mma_ktile_rows<C, true, PERK>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE), fa, acc, issue);
+        mma_ktile_rows<C, true, PERK, BKM>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE), fa, acc, issue);
       }
       // last k step: its loads are the next tile's first k-tile
       if (nk > 1 || !prewaited) wait_vmcnt<0>();
@@ -301,7 +387,7 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
           if (j < AL::PER) al.issue_one(p, tl, 0, st, j);
           else bl.issue_one(p, tl, 0, st + C::A_SLOTS, j - AL::PER);
         };
-        mma_ktile_rows<C, true, PERK>(reinterpret_cast<const uint8_t*>(smem + scratch * C::STAGE), fa, acc, issue);
+        mma_ktile_rows<C, true, PERK, BKM>(reinterpret_cast<const uint8_t*>(smem + scratch * C::STAGE), fa, acc, issue);
       }
       // every wave is past its last LDS read before the stage it read becomes scratch
       __syncthreads();
@@ -339,7 +425,7 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
           else bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
         };
         const uint8_t* cur = reinterpret_cast<const uint8_t*>(smem + (kt % C::NST) * C::STAGE);
-        mma_ktile_rows<C, decltype(loads)::value, PERK>(cur, fa, acc, issue);
+        mma_ktile_rows<C, decltype(loads)::value, PERK, BKM>(cur, fa, acc, issue);
       };
       // the last NST - 1 k steps issue nothing: peeled, not branched, so that the
       // two instantiations never meet inside one loop body

@@ -25,11 +25,6 @@
 
 namespace moe {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-
 // Tile configuration: BM x BN output tiles, WAVES_M x WAVES_N waves, BK-row
 // k-tiles, NST LDS stages.  A stage holds the NA parts of the A k-tile and the NB
 // parts of the B k-tile; MFMA pass q multiplies A part min(q, NA-1) by B part
@@ -55,11 +50,6 @@ struct WgCfg {
 //   dW_gate/up: A = X token rows, B = [dg | du] as bf16 value and remainder (two parts).
 using CfgWgDown = WgCfg<256, 256, 2, 4, 32, 3, 2, 1>;
 using CfgWgGateUp = WgCfg<256, 256, 2, 4, 32, 3, 1, 2>;
-
-// Chunk position in a k-major LDS row: chunk c of row r sits at c ^ tr_swz(r).
-// The flip of chunk-index bits 1-3 by r mod 4 makes the four rows one transpose
-// read touches land in different banks, for both 16- and 32-lane LDS phases.
-__device__ __forceinline__ int tr_swz(int r) { return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0); }
 
 // Loader of one k-major operand: BK rows x COLS columns (cols [c0, c0 + COLS) of
 // the source rows).  Load instruction i of wave w fills LDS slots
@@ -121,13 +111,6 @@ struct TrFragAddr {
     }
   }
 };
-
-__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* st, uint32_t off, uint32_t rs) {
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + off));
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + off + 4 * rs));
-  const v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // One k-tile (BK / 16 MFMA sub-steps), operand reads of sub-step kk + 1 in flight
 // under the MFMAs of sub-step kk; the NLOAD load instructions of a later k-tile

@@ -21,9 +21,6 @@ struct GemmArgs {
   const uint16_t* Wg_t;   // [E, I, H]
   const uint16_t* Wu_t;   // [E, I, H]
   const uint16_t* Wd_t;   // [E, H, I]
-  const uint16_t* Wg;     // [E, H, I]
-  const uint16_t* Wu;     // [E, H, I]
-  const uint16_t* Wd;     // [E, I, H]
   uint16_t* Hrows;        // [A, I]  h (forward)
   uint16_t* Orows;        // [A, H]
   uint16_t* hw;           // [A, I]  bf16(w h) (backward; w = the row's top-k weight)

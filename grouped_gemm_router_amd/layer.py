@@ -23,20 +23,18 @@ class MoELayer:
         self.H, self.I, self.E, self.k, self.dtype = H, I, E, k, dtype
         self.activation, self.act_limit = activation, act_limit
         self.device = torch.device(device)
-        self.W_gate = self.W_up = self.W_down = None
         self._plans = {}
 
     # -- weights (once, outside any timed region) ---------------------------------
-    def load_weights(self, W_gate, W_up: torch.Tensor, W_down: torch.Tensor, keep_math=True):
+    def load_weights(self, W_gate, W_up: torch.Tensor, W_down: torch.Tensor):
         """W_gate, W_up [E, H, I] and W_down [E, I, H] bf16 on the device (W_gate None for the
-        two-weight ReLU^2 expert)."""
+        two-weight ReLU^2 expert).  The layer keeps only the packed copies (forward and backward
+        both read them; the caller's tensors may be freed)."""
         if (W_gate is None) != (self.activation in B.UNGATED):
             raise ValueError("ReLU^2 experts take no gate weight; every other activation needs one")
         self.Wg_t = B.pack_weights(W_gate) if W_gate is not None else None
         self.Wu_t = B.pack_weights(W_up)
         self.Wd_t = B.pack_weights(W_down)
-        if keep_math:
-            self.W_gate, self.W_up, self.W_down = W_gate, W_up, W_down
         self.scales = None
         if self.dtype == "mxfp8":
             qg, sg = B.mx_quantize(self.Wg_t) if self.Wg_t is not None else (None, None)
@@ -104,7 +102,8 @@ class MoELayer:
         """The layer with the routing given by the caller (LightMoE "MoE inference": the call takes
         the top-k ids, int32 with distinct experts per token, and their fp32 weights): dispatch,
         expert MLP and combine.  The ids and weights are copied into the plan, so that a following
-        ``backward`` sees them."""
+        ``backward`` sees them.  An id outside [0, E) is skipped as moe_dispatch documents: its slot
+        adds nothing to Y (and gets d_topk_w = 0)."""
         T = X.shape[0]
         pl = self.plan(T, backward_plan)
         for name, t, dt in (("topk_idx", topk_idx, torch.int32), ("topk_w", topk_w, torch.float32)):
@@ -135,12 +134,12 @@ class MoELayer:
 
     def backward(self, X: torch.Tensor, dY: torch.Tensor):
         """Gradients of the last forward with the same X (needs backward_plan=True)."""
-        if self.dtype != "bf16" or self.W_up is None:
-            raise ValueError("backward needs bf16 weights kept in the math layout")
+        if self.dtype != "bf16":
+            raise ValueError("the backward runs on bf16 weights")
         T = X.shape[0]
         pl = self.plan(T, True)
         return B.backward(X, dY, pl["topk_w"], pl["row_token"], pl["row_slot"], pl["slot_row"], pl["offsets"],
-                          self.W_gate, self.W_up, self.W_down, self.Wg_t, self.Wu_t, out=pl["grads"],
+                          self.Wg_t, self.Wu_t, self.Wd_t, out=pl["grads"],
                           ws=pl["ws_bwd"], activation=self.activation, act_limit=self.act_limit)
 
     def route_backward(self, T: int):

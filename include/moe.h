@@ -272,22 +272,22 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
  *   dW_down[e] = bf16( sum_r h^T dO )      (all sums in fp32, fixed order;
  *                                           experts without rows get zeros)
  *   X, dY [T, H] bf16;  topk_w [T, k] fp32;  dispatch arrays as above
- *   W_gate, W_up [E, H, I], W_down [E, I, H] bf16 (math layout)
- *   Wg_t, Wu_t [E, I, H] bf16 (moe_pack_weights of W_gate, W_up)
+ *   Wg_t, Wu_t [E, I, H], Wd_t [E, H, I] bf16: the packed weights moe_expert_mlp takes
+ *            (moe_pack_weights of W_gate, W_up [E, H, I] and W_down [E, I, H]); no other
+ *            copy of the weights is needed
  *   dX [T, H], dW_gate, dW_up [E, H, I], dW_down [E, I, H] bf16 out;
  *   d_topk_w [T, k] fp32 out
  *   ws, ws_bytes   workspace of moe_workspace_size(MOE_CALL_BACKWARD)
  * MOE_ACT_RELU2 has no gate: du = dh * 2 max(U, 0), dX sums du W_up[e]^T only,
- * W_gate, Wg_t and dW_gate may be NULL and dW_gate is not written.
+ * Wg_t and dW_gate may be NULL and dW_gate is not written.
  */
 MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY,
                                 const float* topk_w, const int32_t* row_token,
                                 const int32_t* row_slot, const int32_t* slot_row,
-                                const int32_t* expert_offsets, const void* W_gate,
-                                const void* W_up, const void* W_down, const void* Wg_t,
-                                const void* Wu_t, void* dX, void* dW_gate, void* dW_up,
-                                void* dW_down, float* d_topk_w, void* ws, size_t ws_bytes,
-                                void* stream);
+                                const int32_t* expert_offsets, const void* Wg_t,
+                                const void* Wu_t, const void* Wd_t, void* dX, void* dW_gate,
+                                void* dW_up, void* dW_down, float* d_topk_w, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /*
  * Standalone grouped GEMM (LightMoE "Grouped GEMM": contiguous expert-major

@@ -94,8 +94,8 @@ def test_gate_pointers_optional_only_for_relu2():
         # decode-sized problem (T <= 64): the missing workspace is reported once the pointers pass
         assert lib.moe_expert_mlp(ctypes.byref(p), v, v, v, None, v, v, None, None, None, v, v, None, 0,
                                   None) == expect, act
-        ptrs = [v] * 17
-        ptrs[7] = ptrs[10] = ptrs[13] = None          # W_gate, Wg_t, dW_gate
+        ptrs = [v] * 15
+        ptrs[7] = ptrs[11] = None                     # Wg_t, dW_gate
         assert lib.moe_backward(ctypes.byref(p), *ptrs, None, 0, None) == expect, act
     pm = B.problem(64, 256, 128, 8, 2, "mxfp8", activation="relu2")
     assert lib.moe_expert_mlp(ctypes.byref(pm), v, v, v, None, v, v, None, v, v, v, v, None, 0, None) == 3
@@ -139,7 +139,7 @@ def test_calls_reject_bad_arguments_before_touching_the_device():
     assert lib.moe_combine(v, v, v, 4, 2, 60, v, None) == 2
     assert lib.moe_mx_quantize(v, 4, 48, v, v, None) == 2
     assert lib.moe_pack_weights(v, 2, 100, 64, v, None) == 2
-    assert lib.moe_backward(ctypes.byref(pm), *([v] * 17), None, 0, None) == 2
+    assert lib.moe_backward(ctypes.byref(pm), *([v] * 15), None, 0, None) == 2
     # router backward: null pointers, k > E, E beyond the limit
     assert lib.moe_route_backward(None, v, v, 4, 8, 2, v, None) == 1
     assert lib.moe_route_backward(v, v, v, 4, 8, 9, v, None) == 1
@@ -160,10 +160,10 @@ def test_empty_batch_accepts_null_token_arrays():
     p = B.problem(0, 256, 128, 8, 2)
     assert lib.moe_expert_mlp(ctypes.byref(p), None, None, v, v, v, v, None, None, None, None, None, None, 0,
                               None) == 0
-    ptrs = [None] * 17
+    ptrs = [None] * 15
     ptrs[6] = v                                     # expert_offsets
-    ptrs[7] = ptrs[8] = ptrs[9] = ptrs[10] = ptrs[11] = v            # weights
-    ptrs[13] = ptrs[14] = ptrs[15] = v                               # dW_gate, dW_up, dW_down
+    ptrs[7] = ptrs[8] = ptrs[9] = v                                  # packed weights
+    ptrs[11] = ptrs[12] = ptrs[13] = v                               # dW_gate, dW_up, dW_down
     assert lib.moe_backward(ctypes.byref(p), *ptrs, None, 0, None) not in (1, 3)
     # the weights and the expert offsets are still required
     ptrs[8] = None

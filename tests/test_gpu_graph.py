@@ -36,7 +36,7 @@ def test_graph_replays_match_eager(cfg):
     _say("graph", cfg)
     W = {n: device_weights(cfg, n) for n in cfg.mats}
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation).load_weights(
-        W.get("gate"), W["up"], W["down"], keep_math=cfg.backward)
+        W.get("gate"), W["up"], W["down"])
     logits = torch.from_numpy(wl.make_logits(cfg)).cuda()
     X = to_dev(wl.make_x(cfg))
     dY = to_dev(wl.make_dy(cfg)) if cfg.backward else None

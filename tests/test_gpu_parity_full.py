@@ -27,8 +27,7 @@ def _setup(name, backward=False, T=None):
     active = np.unique(idx)
     _say(name, "active experts", len(active))
     W = {n: device_weights(cfg, n, experts=active) for n in ("gate", "up", "down")}
-    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(W["gate"], W["up"], W["down"],
-                                                                         keep_math=backward)
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(W["gate"], W["up"], W["down"])
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=backward)
     torch.cuda.synchronize()
     return cfg, layer, logits, X, idx, w

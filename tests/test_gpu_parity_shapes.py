@@ -37,7 +37,7 @@ def test_forward_model_shape_sampled(name):
     _say(name, "experts with weights", len(drawn))
     W = {n: device_weights(cfg, n, experts=drawn) for n in cfg.mats}
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=act,
-                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"], keep_math=False)
+                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"])
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X))
     torch.cuda.synchronize()
     pl = layer.plan(cfg.T)
