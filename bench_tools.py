@@ -8,9 +8,14 @@ Usage (from the repository root, after the profiling runs):
 
   python bench_tools.py traffic --fetch <dir> --write <dir> --workload <name> \\
       --out <traffic.json> [--md <out.md>] [--cmd-fetch "<command>"] [--cmd-write "<command>"]
-      HBM traffic of one moe_expert_mlp call from two counter runs (rocprofv3 --pmc FETCH_SIZE,
-      then --pmc WRITE_SIZE, --output-format csv -o run) of ``bench.py --copy-calibration``.  Each
-      counter is scaled by what it reads for the calibration copy of a known number of bytes.
+      HBM traffic of one moe_expert_mlp call from two counter runs of ``bench.py --copy-calibration``:
+      rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum (reads, summed
+      by request size), then --pmc WRITE_SIZE (writes); --output-format csv -o run.  The copy of a known
+      number of bytes is reported as the check of both.
+
+  python bench_tools.py reqsize <rocprof-dir> <out.md> --cmd "<command>"
+      read requests by size per kernel (the same three counters and TCC_BUBBLE_sum), and what
+      FETCH_SIZE's expression counts from them.
 
   python bench_tools.py mfma --pmc <dir> --stats <dir> --out <out.md> --cmd-pmc "<command>" \
       --cmd-stats "<command>" --title "<title>"
@@ -115,21 +120,41 @@ def _kind(workload: str) -> str:
     return "bf16"
 
 
+# Read traffic: the TCC->EA read requests counted by size.  On gfx950 almost every read request
+# is 128 bytes and TCC_BUBBLE (which FETCH_SIZE's expression takes as the 128-byte count) reads 0,
+# so FETCH_SIZE counts them as 64 bytes, half the bytes; the sizes summed give the bytes directly.
+READ_COUNTERS = ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
+READ_BYTES = (32, 64, 128)
+
+
+def read_bytes(src: str) -> dict:
+    """kernel short name -> list of (dispatch id, bytes read from memory) of a run with READ_COUNTERS."""
+    per = [_per_dispatch(src, c) for c in READ_COUNTERS]
+    out = collections.defaultdict(list)
+    for name, vals in per[-1].items():
+        for i, (d, _) in enumerate(vals):
+            out[name].append((d, sum(b * dict(p.get(name, [])).get(d, 0.0) for p, b in zip(per, READ_BYTES))))
+    return out
+
+
+def write_bytes(src: str) -> dict:
+    """kernel short name -> list of (dispatch id, bytes written) of a run with WRITE_SIZE (KiB)."""
+    return {k: [(d, v * 1024.0) for d, v in vals] for k, vals in _per_dispatch(src, "WRITE_SIZE").items()}
+
+
 def traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one moe_expert_mlp call, scaled by the copy."""
+    """Bytes read (request sizes) and written (WRITE_SIZE) by one moe_expert_mlp call; the copy of
+    COPY_BYTES bytes (bench.py --copy-calibration) is reported as the check of both counters."""
     res = {"workload": workload, "source_sha": source_hash(workload), "copy_bytes": COPY_BYTES}
-    for counter, src in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        per = _per_dispatch(src, counter)
+    for what, per in (("read", read_bytes(fetch_dir)), ("write", write_bytes(write_dir))):
         copy = sorted(v for k, vals in per.items() if COPY_KERNEL in k for _, v in vals)
         if not copy:
-            raise SystemExit(f"no {COPY_KERNEL} dispatch in {src}: run bench.py with --copy-calibration")
-        copy_kib = copy[len(copy) // 2]
-        factor = COPY_BYTES / (copy_kib * 1024.0)
+            raise SystemExit(f"no {COPY_KERNEL} dispatch: run bench.py with --copy-calibration")
         kernels = MLP_KERNELS[_kind(workload)]
         main = [k for k in kernels if k != "k_mx_quantize"][0]      # one dispatch per call
         calls = per.get(main, [])
         if not calls:
-            raise SystemExit(f"no {main} dispatch in {src}")
+            raise SystemExit(f"no {main} dispatch")
         first = calls[0][0]
         call = 0.0
         detail = {}
@@ -139,28 +164,52 @@ def traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
             vals = [v for d, v in per.get(k, []) if d >= first - 1]
             if not vals:
                 continue
-            b = sum(vals) / len(calls) * 1024.0 * factor
+            b = sum(vals) / len(calls)
             detail[k] = round(b)
             call += b
-        res[counter] = {"copy_kib_read": copy_kib, "factor": factor, "calls": len(calls),
-                        "per_kernel_bytes": detail, "call_bytes": round(call)}
-    res["traffic_bytes"] = res["FETCH_SIZE"]["call_bytes"] + res["WRITE_SIZE"]["call_bytes"]
+        res[what] = {"copy_bytes_counted": round(copy[len(copy) // 2]), "calls": len(calls),
+                     "per_kernel_bytes": detail, "call_bytes": round(call)}
+    res["traffic_bytes"] = res["read"]["call_bytes"] + res["write"]["call_bytes"]
     return res
 
 
 def traffic_md(t: dict, out: str, cmd_fetch: str, cmd_write: str) -> None:
     lines = [f"# HBM traffic of one moe_expert_mlp call, workload {t['workload']}", "",
-             "Commands (repository root, one MI355X; one counter per run):", "", "```", cmd_fetch, cmd_write, "```", "",
-             f"Calibration: the counters read for a device-to-device copy of {t['copy_bytes']} bytes "
-             "(the HIP runtime's copy kernel, run by `--copy-calibration`) give the scale factor "
-             "bytes / (KiB read x 1024) applied to every kernel.", "",
-             "| counter | copy reads (KiB) | factor | per kernel (bytes per launch) | per call (bytes) |",
-             "|---|---:|---:|---|---:|"]
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+             "Commands (repository root, one MI355X; reads and writes in separate counter runs):", "", "```",
+             cmd_fetch, cmd_write, "```", "",
+             "Reads are the TCC->EA read requests summed by size (32, 64 and 128 bytes); writes are WRITE_SIZE. "
+             f"Check: the device-to-device copy of {t['copy_bytes']} bytes (`--copy-calibration`) counts as the "
+             "bytes in the table (no scale factor is applied).", "",
+             "| direction | copy counted (bytes) | per kernel (bytes per launch) | per call (bytes) |",
+             "|---|---:|---|---:|"]
+    for c in ("read", "write"):
         d = t[c]
         per = ", ".join(f"{k}: {v / 1e6:.1f} MB" for k, v in d["per_kernel_bytes"].items())
-        lines.append(f"| {c} | {d['copy_kib_read']:.0f} | {d['factor']:.4f} | {per} | {d['call_bytes'] / 1e6:.1f} MB |")
+        lines.append(f"| {c} | {d['copy_bytes_counted']} | {per} | {d['call_bytes'] / 1e6:.1f} MB |")
     lines += ["", f"Total per call: {t['traffic_bytes'] / 1e6:.1f} MB.  Expert-MLP source sha256: `{t['source_sha']}`."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def reqsize_md(src: str, out: str, cmd: str) -> None:
+    """Per kernel: read requests by size, the bytes they give, and what FETCH_SIZE's expression would
+    count from the same requests (TCC_BUBBLE added)."""
+    per = {c: _per_dispatch(src, c) for c in READ_COUNTERS + ("TCC_BUBBLE_sum",)}
+    med = lambda vals: sorted(v for _, v in vals)[len(vals) // 2] if vals else 0.0
+    lines = ["# Read request sizes of the prefill workload's kernels (the FETCH_SIZE factor of 2)", "",
+             "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
+             "Median per dispatch.  Bytes = 32 x 32B + 64 x 64B + 128 x 128B requests.  FETCH_SIZE's "
+             "expression, (TCC_BUBBLE x 128 + (RDREQ - TCC_BUBBLE - RDREQ_32B) x 64 + RDREQ_32B x 32) / 1024 KiB, "
+             "takes TCC_BUBBLE as the 128-byte count; on this part TCC_BUBBLE reads 0 where 128-byte requests are "
+             "issued, so FETCH_SIZE counts them as 64 bytes.", "",
+             "| kernel | 32B | 64B | 128B | TCC_BUBBLE | bytes (sizes) | FETCH_SIZE x 1024 |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for name in sorted(per[READ_COUNTERS[-1]]):
+        n = [med(per[c].get(name, [])) for c in READ_COUNTERS]
+        bub = med(per["TCC_BUBBLE_sum"].get(name, []))
+        b = sum(x * y for x, y in zip(n, READ_BYTES))
+        fetch = bub * 128 + (sum(n) - bub - n[0]) * 64 + n[0] * 32
+        lines.append(f"| `{name[:48]}` | {n[0]:.0f} | {n[1]:.0f} | {n[2]:.0f} | {bub:.0f} | {b / 1e6:.1f} MB | "
+                     f"{fetch / 1e6:.1f} MB |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -247,6 +296,10 @@ def main(argv=None) -> int:
     t.add_argument("--md")
     t.add_argument("--cmd-fetch", default="")
     t.add_argument("--cmd-write", default="")
+    q = sub.add_parser("reqsize")
+    q.add_argument("src")
+    q.add_argument("out")
+    q.add_argument("--cmd", required=True)
     m = sub.add_parser("mfma")
     m.add_argument("--pmc", required=True)
     m.add_argument("--stats", required=True)
@@ -259,6 +312,8 @@ def main(argv=None) -> int:
         mfma_md(a.pmc, a.stats, a.out, a.cmd_pmc, a.cmd_stats, a.title)
     elif a.action == "stats":
         stats_md(a.src, a.out, a.cmd, a.title, a.note)
+    elif a.action == "reqsize":
+        reqsize_md(a.src, a.out, a.cmd)
     else:
         res = traffic(a.fetch, a.write, a.workload)
         with open(a.out, "w") as fh:
