@@ -14,6 +14,10 @@ namespace {
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 32;
 constexpr size_t ALIGN = 256;
+// MI355X's last-level (Infinity) cache.  The MXFP8 down projection's output rows are stored
+// non-temporally when they exceed it: the combine then finds few of them cached either way, and
+// the streamed stores leave L2 to the row and weight tiles the GEMM re-reads.
+constexpr size_t LAST_LEVEL_CACHE_BYTES = (size_t)256 << 20;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -263,6 +267,7 @@ moe_status expert_mlp(const moe_problem* p, const void* X, const int32_t* row_to
   m.Hrows = (uint16_t*)H_rows;
   m.Hq = Hq; m.Hs = Hs;
   m.Orows = (uint16_t*)O_rows;
+  m.stream_out = A * H * 2 > LAST_LEVEL_CACHE_BYTES;
   hipError_t e = moe::launch_mx_quantize((const uint16_t*)X, p->T, p->H, Xq, Xs, st);
   if (e == hipSuccess) e = moe::launch_mx_gateup(m, st);
   if (e == hipSuccess) e = moe::launch_mx_quantize((const uint16_t*)H_rows, (long)A, p->I, Hq, Hs, st);
@@ -325,6 +330,7 @@ MOE_API moe_status moe_grouped_gemm(int32_t dtype, const int32_t* m_indptr, int3
   m.Hq = (const uint8_t*)A; m.Hs = SA;
   m.Wd = (const uint8_t*)B_t; m.Sd = SB;
   m.Orows = (uint16_t*)C;
+  m.stream_out = (size_t)M * N * 2 > LAST_LEVEL_CACHE_BYTES;
   return from_hip(moe::launch_mx_down(m, st));
 }
 

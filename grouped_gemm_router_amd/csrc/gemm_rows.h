@@ -64,6 +64,7 @@ __device__ __forceinline__ int swz(int r) {
 // lane of v_mfma_f32_32x32x16_bf16 holds (tr_frag reads both halves).
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4nt __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -102,8 +103,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the stage being read, does not make every later LDS read wait for it; the
 // loops wait for these loads explicitly (s_waitcnt vmcnt) before the barrier
 // that publishes a stage.
+// A wave-uniform pointer as a scalar-register value (the compiler may compute one in vector
+// registers, which an "s" operand of inline assembly cannot take).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(base)), "s"(lds)
+               : "m0");
+}
+
+// The lane index as a value the compiler cannot see through: addresses derived
+// from it are computed where they are used instead of being hoisted out of the
+// tile loop and held in registers (or spilled) across the k loop.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
 }
 
 // Loader of one operand: rows [0, ROWS) of the tile.  Src provides
@@ -111,14 +129,17 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, ui
 //       rows [row0, row0 + 64 / CPR) for k-tile k0 (element 0 of the k-tile);
 //   static uint32_t row_off(const P&, const Tile&, int row): element offset of the (clamped, valid)
 //       row relative to that base.
-template <class C, int ROWS, class Src, class P>
+// OPAQUE recomputes the lane-derived part of the offsets at every tile instead of letting the
+// compiler hold it across the tile loop (for kernels short of registers; it costs VALU work at
+// each tile start).
+template <class C, int ROWS, class Src, class P, bool OPAQUE = false>
 struct DirectRows {
   static constexpr int INST = ROWS * C::CPR / 64;        // load instructions per stage
   static constexpr int PER = INST / C::NW;               // ... per wave
   uint32_t off[PER];                                     // byte offsets from the wave-uniform base
 
   __device__ void init(const P& p, const Tile& tl) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = OPAQUE ? opaque_lane(threadIdx.x & 63) : (threadIdx.x & 63), wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int s = (i * C::NW + wave) * 64 + lane;
@@ -252,14 +273,6 @@ __device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragA
     if constexpr (NM - EARLY > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - EARLY, 0);
     __builtin_amdgcn_sched_barrier(0);
   });
-}
-
-// The lane index as a value the compiler cannot see through: addresses derived
-// from it are computed where they are used instead of being hoisted out of the
-// tile loop and held in registers (or spilled) across the k loop.
-__device__ __forceinline__ int opaque_lane(int lane) {
-  asm volatile("" : "+v"(lane));
-  return lane;
 }
 
 template <int N>
@@ -496,8 +509,9 @@ __device__ __forceinline__ void rows_gemm_split_body(const P& p) {
 // CW * 2 contiguous bytes per row).  val(fm, fn, q, j) gives the value of
 // accumulator item 4q + j of fragment (fm, fn); col_of(fn, q) the column (in the
 // wave's CW-wide slab) of that item group for lane half 0 (lane half 1 adds 4).
-// NQ item groups per fragment are stored.
-template <class C, int CW, int NQ, class Val, class Col>
+// NQ item groups per fragment are stored.  NT marks the global stores non-temporal (streamed
+// through L2 without displacing the operand tiles other workgroups are still reading).
+template <class C, int CW, int NQ, bool NT = false, class Val, class Col>
 __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, int ld, int row0, int row_end,
                                                  int col0, int ncols, int lane_, Val val, Col col_of) {
   const int lane = opaque_lane(lane_);
@@ -530,7 +544,13 @@ __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, i
       const uint4 v = *reinterpret_cast<const uint4*>(wlds + rr * PITCH + pos(rr, ch) * 16);
       const int grow = row0 + fm * 32 + rr;
       const int gcol = col0 + ch * 8;
-      if (grow < row_end && gcol < ncols) *reinterpret_cast<uint4*>(out + (size_t)grow * ld + gcol) = v;
+      if (grow < row_end && gcol < ncols) {
+        uint16_t* dst = out + (size_t)grow * ld + gcol;
+        if constexpr (NT)
+          __builtin_nontemporal_store(u32x4nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4nt*>(dst));
+        else
+          *reinterpret_cast<uint4*>(dst) = v;
+      }
     }
   }
 }

@@ -71,12 +71,13 @@ __device__ int block_exclusive_scan(int v, int* red /* NT/64 + 1 ints */) {
 // every expert's remainder is one tile at most BMF / 4 - 1 rows taller than it.
 enum RowPart { ROWS_ALL = 0, ROWS_FULL = 1, ROWS_REM_Q1 = 2, ROWS_REM_Q2 = 3, ROWS_REM_Q3 = 4 };
 
-template <int BM, int BN, int NT, int PART = ROWS_ALL, int BMF = BM>
+template <int BM, int BN, int NT, int PART = ROWS_ALL, int BMF = BM, int GROUP_M = 1>
 struct RowGroups {
   static constexpr int QUARTER = PART >= ROWS_REM_Q1 ? PART - ROWS_REM_Q1 + 1 : 0;
   static_assert(PART != ROWS_FULL || BMF == BM, "full tiles are BMF rows");
   static_assert(QUARTER == 0 || (BMF % 4 == 0 && BM * 4 == QUARTER * BMF), "one remainder tile per class");
   static constexpr int MAX_E = 1024;
+  static_assert(GROUP_M >= 1, "m-tiles per group");
   // tiles of expert e with n rows, and the first of its rows they cover
   __device__ static int count(int n) {
     if constexpr (PART == ROWS_ALL) return (n + BM - 1) / BM;
@@ -116,19 +117,36 @@ struct RowGroups {
     total = prefix[E] * ntiles_n;
   }
 
+  // Tile t of the schedule.  An expert's tiles are contiguous.  With GROUP_M = 1 they run m-tile
+  // by m-tile, n fastest.  Otherwise they run in groups of GROUP_M m-tiles, n-tiles outermost
+  // inside a group: the workgroups of one XCD that run at the same time (consecutive tiles) then
+  // share GROUP_M row blocks and a few weight column blocks, and the next n-tiles of the group
+  // find the row blocks still in L2; this pays where the K extent is short (row blocks of a few
+  // hundred KB) and N is wide.
   __device__ Tile tile(int t) const {
-    int mt = t / ntiles_n, nt = t - mt * ntiles_n;
-    // largest e with prefix[e] <= mt (experts with no tiles have prefix[e] == prefix[e+1])
+    const int mt_lin = t / ntiles_n;
+    // largest e with prefix[e] <= mt_lin (experts with no tiles have prefix[e] == prefix[e+1])
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+      if (prefix[mid] <= mt_lin) lo = mid; else hi = mid - 1;
+    }
+    const int li = t - prefix[lo] * ntiles_n;            // tile index inside the expert
+    const int me = prefix[lo + 1] - prefix[lo];           // its m-tiles
+    int mt, nt;
+    if constexpr (GROUP_M == 1) {
+      mt = li / ntiles_n;
+      nt = li - mt * ntiles_n;
+    } else {
+      const int g = li / (GROUP_M * ntiles_n), r = li - g * GROUP_M * ntiles_n;
+      const int gm = min(GROUP_M, me - g * GROUP_M);      // m-tiles in this group
+      mt = g * GROUP_M + r % gm;
+      nt = r / gm;
     }
     // every lane computes the same tile: keep its fields in scalar registers
     Tile tl;
     tl.e = __builtin_amdgcn_readfirstlane(lo);
-    tl.m0 = __builtin_amdgcn_readfirstlane(offsets[lo] + first_row(offsets[lo + 1] - offsets[lo]) +
-                                           (mt - prefix[lo]) * BM);
+    tl.m0 = __builtin_amdgcn_readfirstlane(offsets[lo] + first_row(offsets[lo + 1] - offsets[lo]) + mt * BM);
     tl.m_end = __builtin_amdgcn_readfirstlane(offsets[lo + 1]);
     tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
     tl.nt = __builtin_amdgcn_readfirstlane(nt);

@@ -88,6 +88,7 @@ struct MxArgs {
   uint16_t* Hrows;                          // [A, I] bf16
   const uint8_t* Hq;  const uint8_t* Hs;    // [A, I], [A, I/32]
   uint16_t* Orows;                          // [A, H]
+  int stream_out;                           // store Orows non-temporally (it exceeds the last-level cache)
 };
 hipError_t launch_mx_gateup(const MxArgs& a, hipStream_t s);
 hipError_t launch_mx_down(const MxArgs& a, hipStream_t s);

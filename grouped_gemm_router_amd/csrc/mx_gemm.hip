@@ -28,14 +28,16 @@ __device__ __forceinline__ int mx_clamp_row(const Tile& t, int row) { return min
 // Data sources (codes seen as 16-bit words: k0 and offsets count words) and the
 // byte address of each row's first scale (scale k-tile kt is 4 bytes further per kt).
 struct MxSrcX {        // gathered token rows of the quantised X
+  static constexpr bool NARROW = true;   // scale rows: wave-uniform base + 32-bit offset
   __device__ static const uint16_t* base(const MxArgs& p, const Tile&, int, int k0) {
     return reinterpret_cast<const uint16_t*>(p.Xq) + k0;
   }
   __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
     return (uint32_t)p.row_token[mx_clamp_row(t, row)] * (uint32_t)(p.H / 2);
   }
-  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
-    return p.Xs + (size_t)p.row_token[mx_clamp_row(t, row)] * (p.H / 32);
+  __device__ static const uint8_t* sbase(const MxArgs& p, const Tile&) { return p.Xs; }
+  __device__ static uint32_t soff(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)p.row_token[mx_clamp_row(t, row)] * (uint32_t)(p.H / 32);
   }
 };
 // Packed gate / up codes [E, I, H], interleaved like the bf16 gate/up B tile:
@@ -53,59 +55,98 @@ struct MxSrcGateUpW {
   __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
     return (uint32_t)col(p, t, row) * (uint32_t)(p.H / 2);
   }
+  // gate and up rows alternate inside a wave and their scales are separate arrays: a 64-bit
+  // address per lane
+  static constexpr bool NARROW = false;
   __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
     const bool up = (row % 32) >= 16;
     return (up ? p.Su : p.Sg) + ((size_t)t.e * p.I + col(p, t, row)) * (p.H / 32);
   }
 };
 struct MxSrcUpW {      // packed up codes [E, I, H]: the B rows of the ungated (ReLU^2) up GEMM
+  static constexpr bool NARROW = true;   // scale rows: wave-uniform base + 32-bit offset
   __device__ static const uint16_t* base(const MxArgs& p, const Tile& t, int, int k0) {
     return reinterpret_cast<const uint16_t*>(p.Wu) + (size_t)t.e * p.I * (p.H / 2) + k0;
   }
   __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
     return (uint32_t)min(t.n0 + row, p.I - 1) * (uint32_t)(p.H / 2);
   }
-  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
-    return p.Su + ((size_t)t.e * p.I + min(t.n0 + row, p.I - 1)) * (p.H / 32);
+  __device__ static const uint8_t* sbase(const MxArgs& p, const Tile& t) { return p.Su + (size_t)t.e * p.I * (p.H / 32); }
+  __device__ static uint32_t soff(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.I - 1) * (uint32_t)(p.H / 32);
   }
 };
 struct MxSrcH {        // expert-major quantised h rows
+  static constexpr bool NARROW = true;   // scale rows: wave-uniform base + 32-bit offset
   __device__ static const uint16_t* base(const MxArgs& p, const Tile&, int, int k0) {
     return reinterpret_cast<const uint16_t*>(p.Hq) + k0;
   }
   __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
     return (uint32_t)mx_clamp_row(t, row) * (uint32_t)(p.I / 2);
   }
-  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
-    return p.Hs + (size_t)mx_clamp_row(t, row) * (p.I / 32);
+  __device__ static const uint8_t* sbase(const MxArgs& p, const Tile&) { return p.Hs; }
+  __device__ static uint32_t soff(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)mx_clamp_row(t, row) * (uint32_t)(p.I / 32);
   }
 };
 struct MxSrcDownW {    // packed down codes [E, H, I]
+  static constexpr bool NARROW = true;   // scale rows: wave-uniform base + 32-bit offset
   __device__ static const uint16_t* base(const MxArgs& p, const Tile& t, int, int k0) {
     return reinterpret_cast<const uint16_t*>(p.Wd) + (size_t)t.e * p.H * (p.I / 2) + k0;
   }
   __device__ static uint32_t row_off(const MxArgs& p, const Tile& t, int row) {
     return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)(p.I / 2);
   }
-  __device__ static const uint8_t* scales(const MxArgs& p, const Tile& t, int row) {
-    return p.Sd + ((size_t)t.e * p.H + min(t.n0 + row, p.H - 1)) * (p.I / 32);
+  __device__ static const uint8_t* sbase(const MxArgs& p, const Tile& t) { return p.Sd + (size_t)t.e * p.H * (p.I / 32); }
+  __device__ static uint32_t soff(const MxArgs& p, const Tile& t, int row) {
+    return (uint32_t)min(t.n0 + row, p.H - 1) * (uint32_t)(p.I / 32);
   }
 };
 
 // Scale words of the tile rows: 4 dword loads of 64 lanes per operand; wave w
 // of group g (waves 0-3: A, 4-7: B) loads rows 64 w .. 64 w + 63 of its operand.
+template <class SrcA, class SrcB>
 struct MxScaleRows {
-  const uint8_t* ptr;
-  template <class SrcA, class SrcB>
+  static constexpr bool NARROW = SrcA::NARROW && SrcB::NARROW;
+  const uint8_t* base;        // NARROW: wave-uniform base and this lane's 32-bit offset;
+  uint32_t off;               // otherwise base is this lane's address (off unused)
   __device__ void init(const MxArgs& p, const Tile& tl, int wave) {
-    const int row = (wave & 3) * 64 + (threadIdx.x & 63);
-    ptr = wave < 4 ? SrcA::scales(p, tl, row) : SrcB::scales(p, tl, row);
+    const int row = (wave & 3) * 64 + opaque_lane(threadIdx.x & 63);
+    // (a wave-uniform branch: a select between the two sources became a private array)
+    off = 0;
+    if (wave < 4) {
+      if constexpr (NARROW) {
+        base = SrcA::sbase(p, tl);
+        off = SrcA::soff(p, tl, row);
+      } else {
+        base = scales_of<SrcA>(p, tl, row);
+      }
+    } else {
+      if constexpr (NARROW) {
+        base = SrcB::sbase(p, tl);
+        off = SrcB::soff(p, tl, row);
+      } else {
+        base = scales_of<SrcB>(p, tl, row);
+      }
+    }
+  }
+  template <class S>
+  __device__ static const uint8_t* scales_of(const MxArgs& p, const Tile& tl, int row) {
+    if constexpr (S::NARROW) return S::sbase(p, tl) + S::soff(p, tl, row);
+    else return S::scales(p, tl, row);
   }
   // this wave's 64 scale words of k-tile kt into lds (the operand's word array)
   __device__ void issue(int kt, uint32_t* lds, int wave) const {
-    const uint8_t* a = ptr + (size_t)kt * 4;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(a), "s"(lds_addr(lds + (wave & 3) * 64))
-                 : "m0");
+    if constexpr (NARROW) {
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off + (uint32_t)kt * 4u), "s"(uniform_ptr(base)),
+                   "s"(lds_addr(lds + (wave & 3) * 64))
+                   : "m0");
+    } else {
+      const uint8_t* a = base + (size_t)kt * 4;
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(a),
+                   "s"(lds_addr(lds + (wave & 3) * 64))
+                   : "m0");
+    }
   }
 };
 
@@ -114,11 +155,10 @@ struct MxScaleRows {
 template <class C>
 struct MxFragAddr {
   uint32_t a[C::FM], b[C::FN];
-  int ra, rb;                 // tile rows of fragment 0 (fragment f: + 32 f), for the scale words
   __device__ void init(int wm, int wn, int lane) {
     const int h = lane >> 5;
-    ra = wm * C::WTM + (lane & 31);
-    rb = wn * C::WTN + (lane & 31);
+    const int ra = wm * C::WTM + (lane & 31);
+    const int rb = wn * C::WTN + (lane & 31);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int r = ra + fm * 32;
@@ -147,10 +187,14 @@ __device__ __forceinline__ void mma_ktile_mx(const uint8_t* stage, const uint32_
                                              Issue issue) {
   const int h = lane >> 5;
   uint32_t wa[C::FM], wb[C::FN];
+  // the scale rows of this lane's fragments, recomputed here rather than held across the kernel
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ra = (wave / C::WAVES_N) * C::WTM + (opaque_lane(lane) & 31);
+  const int rb = (wave % C::WAVES_N) * C::WTN + (opaque_lane(lane) & 31);
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) wa[fm] = sA[fa.ra + 32 * fm];
+  for (int fm = 0; fm < C::FM; ++fm) wa[fm] = sA[ra + 32 * fm];
 #pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) wb[fn] = sB[fa.rb + 32 * fn];
+  for (int fn = 0; fn < C::FN; ++fn) wb[fn] = sB[rb + 32 * fn];
   static_for<0, 2>([&](auto kkc) {
     constexpr int kk = decltype(kkc)::value;
     const int sh = 8 * (2 * kk + h);
@@ -176,7 +220,7 @@ __device__ __forceinline__ void mma_ktile_mx(const uint8_t* stage, const uint32_
 
 // Persistent body (two stages; the bf16 row GEMM's pipeline with the scale
 // words added).  Waves 0-3 load the A scales, waves 4-7 the B scales.
-template <class C, class SrcA, class SrcB, class Epi>
+template <class C, class SrcA, class SrcB, class Epi, int GROUP_M = 1>
 __device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
   __shared__ uint4 smem[2 * C::STAGE];
   __shared__ uint32_t sscale[2][C::BM + C::BN];
@@ -184,11 +228,11 @@ __device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  using AL = DirectRows<C, C::BM, SrcA, MxArgs>;
-  using BL = DirectRows<C, C::BN, SrcB, MxArgs>;
+  using AL = DirectRows<C, C::BM, SrcA, MxArgs, true>;
+  using BL = DirectRows<C, C::BN, SrcB, MxArgs, true>;
   constexpr int PERK = AL::PER + BL::PER + 1;             // data loads + one scale load per wave
 
-  RowGroups<C::BM, C::BN, C::NT> sched;
+  RowGroups<C::BM, C::BN, C::NT, ROWS_ALL, C::BM, GROUP_M> sched;
   sched.init(p.offsets, p.E, N, K / 2, sched_lds, sched_lds + 1025);   // K in 16-bit words
   XcdWalk walk;
   walk.init(sched.total);
@@ -198,11 +242,11 @@ __device__ __forceinline__ void mx_rows_body(const MxArgs& p, int N, int K) {
   fa.init(wm, wn, lane);
   AL al;
   BL bl;
-  MxScaleRows sc;
+  MxScaleRows<SrcA, SrcB> sc;
   auto init_loaders = [&]() {
     al.init(p, tl);
     bl.init(p, tl);
-    sc.init<SrcA, SrcB>(p, tl, wave);
+    sc.init(p, tl, wave);
   };
   auto issue_scales = [&](int kt, int st) { sc.issue(kt, &sscale[st][wave < 4 ? 0 : C::BM], wave); };
   init_loaders();
@@ -297,13 +341,17 @@ struct MxRelu2Epi {  // h = bf16(max(U, 0)^2) -> Hrows (the ungated expert)
 };
 
 template <class C>
-struct MxStoreOEpi {  // O = bf16(acc) -> Orows
+struct MxStoreOEpi {  // O = bf16(acc) -> Orows (streamed past L2 when the host sets stream_out)
   __device__ static void apply(const MxArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
                                int lane, uint8_t* wlds) {
-    stage_store_bf16<C, C::WTN, 4>(
-        wlds, p.Orows, p.H, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.H, lane,
-        [&](int fm, int fn, int q, int j) { return acc[fm][fn][4 * q + j]; },
-        [](int fn, int q) { return fn * 32 + q * 8; });
+    auto val = [&](int fm, int fn, int q, int j) { return acc[fm][fn][4 * q + j]; };
+    auto col = [](int fn, int q) { return fn * 32 + q * 8; };
+    if (p.stream_out)
+      stage_store_bf16<C, C::WTN, 4, true>(wlds, p.Orows, p.H, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN,
+                                           p.H, lane, val, col);
+    else
+      stage_store_bf16<C, C::WTN, 4>(wlds, p.Orows, p.H, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.H,
+                                     lane, val, col);
   }
 };
 
@@ -319,7 +367,8 @@ __global__ void __launch_bounds__(CfgMx::NT) k_mx_up(const MxArgs p) {
   mx_rows_body<CfgMx, MxSrcX, MxSrcUpW, MxRelu2Epi<CfgMx>>(p, p.I, p.H);
 }
 __global__ void __launch_bounds__(CfgMx::NT) k_mx_down(const MxArgs p) {
-  mx_rows_body<CfgMx, MxSrcH, MxSrcDownW, MxStoreOEpi<CfgMx>>(p, p.H, p.I);
+  // K = I is short: m-tile groups keep the row blocks in L2 while the weight columns stream
+  mx_rows_body<CfgMx, MxSrcH, MxSrcDownW, MxStoreOEpi<CfgMx>, 8>(p, p.H, p.I);
 }
 
 static int mx_grid(const MxArgs& a, int N) {

@@ -9,9 +9,6 @@ parks in VGPR lanes touch no memory and are allowed).  The check compiles the so
 for gfx950 with the build's own flags and reads the compiler's resource
 remarks.
 
-The MXFP8 kernels (mx_gemm.hip) are exempt: their pipeline has two stages, so
-every k step waits for all outstanding memory operations (vmcnt(0)) and a spill
-costs time but cannot break a wait.  They do spill in the epilogue.
 """
 import os
 import re
@@ -22,7 +19,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "grouped_gemm_router_amd", "csrc")
-GEMM_SOURCES = ["gemm_bf16.hip", "gemm_wgrad.hip", "decode.hip"]
+GEMM_SOURCES = ["gemm_bf16.hip", "gemm_wgrad.hip", "decode.hip", "mx_gemm.hip"]
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                                 reason="hipcc not available")
