@@ -4,7 +4,9 @@ Usage (from the repository root, after the profiling runs):
 
   python bench_tools.py stats <rocprof-dir> <out.md> --cmd "<command>" --title "<title>"
       kernel table (calls, average / min / max duration, share of GPU time) from
-      <rocprof-dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace --stats --output-format csv -o run)
+      <rocprof-dir>/run_kernel_trace.csv (rocprofv3 --kernel-trace --stats --output-format csv -o run);
+      --split-at <kernel> makes one table of the dispatches before that kernel's first one and one
+      of the rest
 
   python bench_tools.py traffic --fetch <dir> --write <dir> --workload <name> \\
       --out <traffic.json> [--md <out.md>] [--cmd-fetch "<command>"] [--cmd-write "<command>"]
@@ -76,22 +78,43 @@ def _short(name: str) -> str:
     return name.split("(")[0].replace("moe::", "")
 
 
-def stats_md(src: str, out: str, cmd: str, title: str, note: str = "") -> None:
-    rows = list(csv.DictReader(open(os.path.join(src, "run_kernel_stats.csv"))))
+def _trace_table(rows: list) -> list:
+    """markdown rows (calls, avg / min / max duration, share of the section's GPU time) per kernel
+    of kernel-trace rows, longest total first."""
+    dur = collections.defaultdict(list)
+    for r in rows:
+        dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in dur.values()) or 1.0
+    lines = ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for name, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        n = name.replace("|", "/")
+        if len(n) > 90:
+            n = n[:87] + "..."
+        lines.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} "
+                     f"| {100 * sum(v) / total:.2f} |")
+    return lines
+
+
+def stats_md(src: str, out: str, cmd: str, title: str, note: str = "", split_at: str = "") -> None:
+    """Kernel table of one trace run.  With split_at (part of a kernel's name), the dispatches that
+    start before that kernel's first dispatch and the rest get a table each (bench.py's default
+    run measures its own workload first and then the other configurations)."""
+    trace = list(csv.DictReader(open(os.path.join(src, "run_kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     agent = list(csv.DictReader(open(os.path.join(src, "run_agent_info.csv"))))
     gpus = [a for a in agent if a.get("Agent_Type", "").upper() == "GPU"]
     dev = gpus[0].get("Name", "?") if gpus else "?"
     lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
-             f"Device: {dev}.  Per-kernel durations from the kernel trace (`run_kernel_stats.csv`).", ""]
+             f"Device: {dev}.  Per-kernel durations from the kernel trace (`run_kernel_trace.csv`).", ""]
     if note:
         lines += [note, ""]
-    lines += ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
-    for r in rows:
-        n = r["Name"].replace("|", "/")
-        if len(n) > 90:
-            n = n[:87] + "..."
-        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} "
-                     f"| {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    if split_at:
+        first = next((i for i, r in enumerate(trace) if split_at in _short(r["Kernel_Name"])), len(trace))
+        lines += [f"Dispatches before the first `{split_at}`:", ""] + _trace_table(trace[:first])
+        if first < len(trace):
+            lines += ["", f"From the first `{split_at}` on:", ""] + _trace_table(trace[first:])
+    else:
+        lines += _trace_table(trace)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -288,6 +311,7 @@ def main(argv=None) -> int:
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--note", default="")
+    s.add_argument("--split-at", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -311,7 +335,7 @@ def main(argv=None) -> int:
     if a.action == "mfma":
         mfma_md(a.pmc, a.stats, a.out, a.cmd_pmc, a.cmd_stats, a.title)
     elif a.action == "stats":
-        stats_md(a.src, a.out, a.cmd, a.title, a.note)
+        stats_md(a.src, a.out, a.cmd, a.title, a.note, a.split_at)
     elif a.action == "reqsize":
         reqsize_md(a.src, a.out, a.cmd)
     else:
