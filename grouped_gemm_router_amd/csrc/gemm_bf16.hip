@@ -249,8 +249,12 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
   static constexpr bool EARLY_NEXT = false;
   // one staged 32 x 32 bf16 block: 64-byte rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
   static constexpr int OUT = 32 * 64;
+  // three rounds of two staged blocks (w h, dg, du each computed from the accumulators) for the
+  // run-time activation, whose switch needs the registers, and for tiles whose LDS scratch holds
+  // two blocks only; else two rounds (four blocks, then two)
+  static constexpr bool THREE_ROUNDS = ACTK == ACT_ANY || RowEpiLds<C>::BYTES < 4 * OUT;
   static_assert(C::FN * 16 == 32, "a wave owns 32 intermediate columns");
-  static_assert(RowEpiLds<C>::BYTES >= (ACTK == ACT_ANY ? 2 : 4) * OUT, "staging area too small");
+  static_assert(RowEpiLds<C>::BYTES >= (THREE_ROUNDS ? 2 : 4) * OUT, "staging area too small");
 
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t* wlds) {
@@ -298,9 +302,9 @@ struct BwdRecomputeOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
           if (row0 + rr < t.m_end) *reinterpret_cast<uint4*>(out + (size_t)(row0 + rr) * ld + col0 + ch * 8) = v;
         }
       };
-      if constexpr (ACTK == ACT_ANY) {
-        // the run-time activation (its switch needs registers): three rounds of two slots, each
-        // computing one quantity from the accumulators -- w h with the partial sum, dg, du
+      if constexpr (THREE_ROUNDS) {
+        // three rounds of two slots, each computing one quantity from the accumulators -- w h
+        // with the partial sum, dg, du
 #pragma unroll
         for (int o = 0; o < 6; o += 2) {
 #pragma unroll
@@ -500,11 +504,6 @@ struct BwdDXOps : RowOpsBase<C, RSrcDGU, KSrcGateUpWt, PART> {
 // ------------------------------------------------------------------------
 // Kernels and launchers
 // ------------------------------------------------------------------------
-#define MOE_ROWS_KERNEL(NAME, OPS)                                                 \
-  __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {          \
-    rows_gemm_body<CfgRows, OPS<CfgRows>, GemmArgs>(p);                            \
-  }
-
 #define MOE_ROWS_SPLIT_KERNEL(NAME, OPS)                                                            \
   __global__ void __launch_bounds__(CfgRows::NT) NAME(const GemmArgs p) {                            \
     rows_gemm_split_body<CfgRows, CfgRem192, CfgRem128, CfgRem64, OPS<CfgRows, ROWS_FULL>,           \
@@ -525,7 +524,15 @@ MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps)
 MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny)
 MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps)
 MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps)
-MOE_ROWS_KERNEL(k_bwd_recompute, BwdRecomputeOps)
+// the recompute over the four row passes: the remainders of at most 64 rows take 64 x 256 tiles
+// of 8 waves of 32 x 64 (every pass keeps 4 waves across the 256 columns, as the router-weight
+// partial sums are laid out)
+using CfgRecRem64 = RowCfg<64, 256, 2, 4, 64, 3>;
+__global__ void __launch_bounds__(CfgRows::NT) k_bwd_recompute(const GemmArgs p) {
+  rows_gemm_split_body<CfgRows, CfgRem192, CfgRem128, CfgRecRem64, BwdRecomputeOps<CfgRows, ROWS_FULL>,
+                       BwdRecomputeOps<CfgRem192, ROWS_REM_Q3>, BwdRecomputeOps<CfgRem128, ROWS_REM_Q2>,
+                       BwdRecomputeOps<CfgRecRem64, ROWS_REM_Q1>, GemmArgs>(p);
+}
 __global__ void __launch_bounds__(CfgRecAny::NT) k_bwd_recompute_act(const GemmArgs p) {
   rows_gemm_body<CfgRecAny, BwdRecomputeOpsAny<CfgRecAny>, GemmArgs>(p);
 }

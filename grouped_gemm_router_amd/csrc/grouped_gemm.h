@@ -33,13 +33,19 @@ struct Tile {
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of up to 4 * NT values held 4 per thread.
 // ---------------------------------------------------------------------------
+// The lane index passes through an empty asm and the shifts are explicit ds_bpermute reads: the
+// source addresses are computed here, not shared with another scan of the same kernel and held in
+// registers in between.
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* red /* NT/64 + 1 ints */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
+    // lanes below d read a wrapped lane (bits 7:2 of the address) and keep their own value
+    const int y = __builtin_amdgcn_ds_bpermute((lane - d) << 2, x);
     if (lane >= d) x += y;
   }
   if (lane == 63) red[wave] = x;
@@ -96,19 +102,23 @@ struct RowGroups {
     K = K_;
     offsets = offs;
     ntiles_n = (N + BN - 1) / BN;
-    // each thread owns 4 consecutive experts
+    // each thread owns 4 consecutive experts (the thread index passes through an empty asm: the
+    // addresses derived from it are computed here, not shared with another schedule of the same
+    // kernel and held in registers through the passes in between)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     int cnt[4];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = threadIdx.x * 4 + i;
+      int e = tid * 4 + i;
       cnt[i] = (e < E) ? count(offs[e + 1] - offs[e]) : 0;
       sum += cnt[i];
     }
     int ex = block_exclusive_scan<NT>(sum, red);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = threadIdx.x * 4 + i;
+      int e = tid * 4 + i;
       if (e < E) prefix[e] = ex;
       ex += cnt[i];
     }
