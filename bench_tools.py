@@ -19,6 +19,14 @@ Usage (from the repository root, after the profiling runs):
       read requests by size per kernel (the same three counters and TCC_BUBBLE_sum), and what
       FETCH_SIZE's expression counts from them.
 
+  python bench_tools.py waves --dirs <d1> <d2> <d3> --kernels <k...> --cmds "<c1>" "<c2>" "<c3>" \\
+      --out <out.md> --title "<title>"
+      wave-state, LDS and L2 counters of the named kernels from the three WAVE_PASSES runs.
+
+  python bench_tools.py library <out.md> --cmd "<command>"
+      (on a GPU) times the vendor library (torch.matmul, hipBLASLt) on dense bf16 GEMMs of the
+      grouped GEMMs' shapes, for context.
+
   python bench_tools.py mfma --pmc <dir> --stats <dir> --out <out.md> --cmd-pmc "<command>" \
       --cmd-stats "<command>" --title "<title>"
       MFMA utilisation per kernel from one counter run (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
@@ -302,6 +310,114 @@ def mfma_md(pmc_dir: str, stats_dir: str, out: str, cmd_pmc: str, cmd_stats: str
         fh.write("\n".join(lines) + "\n")
 
 
+# Dense bf16 GEMMs of the same shapes as the grouped GEMMs, run by the vendor library (torch.matmul
+# on ROCm: hipBLASLt), for context: (label, batch, M, N, K).  A batch of equal experts stands in
+# for the grouped GEMM (the prefill workload's routing puts 4096 rows on each of 8 experts).
+LIBRARY_SHAPES = (
+    ("prefill gate/up: 8 experts x [4096 x 2048] x [2048 x 1024]", 8, 4096, 1024, 2048),
+    ("prefill down: 8 experts x [4096 x 512] x [512 x 2048]", 8, 4096, 2048, 512),
+    ("prefill gate/up rows as one GEMM: [32768 x 2048] x [2048 x 1024]", 1, 32768, 1024, 2048),
+    ("training gate/up: 128 experts x [512 x 4096] x [4096 x 2048]", 128, 512, 2048, 4096),
+    ("square 8192", 1, 8192, 8192, 8192),
+)
+
+
+def library_md(out: str, cmd: str, iters: int = 50) -> None:
+    """Times torch.matmul (hipBLASLt) on LIBRARY_SHAPES with device events; writes a table."""
+    import torch
+    torch.manual_seed(0)
+    dev = torch.device("cuda")
+    lines = ["# The vendor GEMM library on the grouped GEMMs' shapes (bf16, one MI355X)", "",
+             "Command (repository root):", "", "```", cmd, "```", "",
+             f"torch.matmul on bf16 operands (hipBLASLt), fp32 accumulation, {iters} back-to-back calls timed with "
+             "device events after 5 warm-up calls; contiguous operands.  % of peak against the dense bf16 peak "
+             f"{PEAK_TFLOPS['BF16']} TFLOP/s.", "",
+             "| shape | us per call | TFLOP/s | % of bf16 peak |", "|---|---:|---:|---:|"]
+    for label, b, m, n, k in LIBRARY_SHAPES:
+        a = torch.randn(b, m, k, device=dev, dtype=torch.bfloat16)
+        w = torch.randn(b, k, n, device=dev, dtype=torch.bfloat16).contiguous()
+        for _ in range(5):
+            torch.matmul(a, w)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            torch.matmul(a, w)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        tf = 2.0 * b * m * n * k / ms / 1e9
+        lines.append(f"| {label} | {ms * 1e3:.1f} | {tf:.0f} | {100 * tf / PEAK_TFLOPS['BF16']:.1f}% |")
+        print(lines[-1], flush=True)
+        del a, w
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+# Wave-state and LDS counters (two rocprofv3 passes of eight SQ counters each; a third pass with
+# the L2 hit and miss counts).  SQ_WAVE_CYCLES and the SQ_WAIT_* / SQ_ACTIVE_* counters count in
+# the same unit, so their ratios compare like with like.
+WAVE_PASSES = (
+    ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+     "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_VALU"),
+    ("SQ_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+     "SQ_INST_CYCLES_VMEM_RD", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_MISC", "GRBM_GUI_ACTIVE"),
+    ("TCC_HIT_sum", "TCC_MISS_sum"),
+)
+
+
+def waves_md(dirs: list, kernels: list, out: str, cmds: list, title: str) -> None:
+    """Per-dispatch means of the WAVE_PASSES counters for the named kernels (short names)."""
+    vals = collections.defaultdict(dict)
+    for d in dirs:
+        per = _per_dispatch_multi(d)
+        acc = collections.defaultdict(lambda: collections.defaultdict(float))
+        cnt = collections.Counter()
+        for name, v in per.values():
+            if name not in kernels:
+                continue
+            cnt[name] += 1
+            for c, x in v.items():
+                acc[name][c] += x
+        for name in acc:
+            for c, x in acc[name].items():
+                vals[name][c] = x / cnt[name]
+    lines = [f"# {title}", "", "Commands (repository root, one MI355X; one counter pass each):", "", "```", *cmds, "```",
+             "", "Values per dispatch (mean over the kernel's dispatches; counters summed over the device as "
+             "`run_counter_collection.csv` reports them).  Percentages of the first rows are shares of SQ_WAVE_CYCLES.",
+             "", "| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |", "|---|" + "---:|" * len(kernels)]
+
+    def row(label, f):
+        cells = []
+        for k in kernels:
+            try:
+                cells.append(f(vals[k]))
+            except (KeyError, ZeroDivisionError):
+                cells.append("n/a")
+        lines.append(f"| {label} | " + " | ".join(cells) + " |")
+
+    row("SQ_WAVE_CYCLES", lambda v: f"{v['SQ_WAVE_CYCLES']:,.0f}")
+    for c, label in (("SQ_WAIT_ANY", "SQ_WAIT_ANY (waiting on s_waitcnt / barriers)"),
+                     ("SQ_WAIT_INST_ANY", "SQ_WAIT_INST_ANY (waiting for an issue slot)"),
+                     ("SQ_WAIT_INST_LDS", "SQ_WAIT_INST_LDS"),
+                     ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_ANY"),
+                     ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VALU (MFMA included)"),
+                     ("SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_LDS"),
+                     ("SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_VMEM")):
+        row(label, lambda v, c=c: f"{v[c]:,.0f} ({100 * v[c] / v['SQ_WAVE_CYCLES']:.1f}%)")
+    row("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (active cycles per XCD x 1024 SIMDs)",
+        lambda v: f"{100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (v['GRBM_GUI_ACTIVE'] * SIMD_NUM):.1f}%")
+    row("SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+        lambda v: f"{100 * v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.1f}%")
+    row("SQ_LDS_IDX_ACTIVE / SQ_BUSY_CYCLES", lambda v: f"{v['SQ_LDS_IDX_ACTIVE'] / v['SQ_BUSY_CYCLES']:.2f}")
+    row("SQ_LDS_DATA_FIFO_FULL", lambda v: f"{v['SQ_LDS_DATA_FIFO_FULL']:,.0f}")
+    row("SQ_LDS_CMD_FIFO_FULL", lambda v: f"{v['SQ_LDS_CMD_FIFO_FULL']:,.0f}")
+    row("L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)",
+        lambda v: f"{100 * v['TCC_HIT_sum'] / (v['TCC_HIT_sum'] + v['TCC_MISS_sum']):.1f}%")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="action", required=True)
@@ -331,8 +447,21 @@ def main(argv=None) -> int:
     m.add_argument("--cmd-pmc", default="")
     m.add_argument("--cmd-stats", default="")
     m.add_argument("--title", required=True)
+    w = sub.add_parser("waves")
+    w.add_argument("--dirs", nargs="+", required=True)
+    w.add_argument("--kernels", nargs="+", required=True)
+    w.add_argument("--cmds", nargs="+", required=True)
+    w.add_argument("--out", required=True)
+    w.add_argument("--title", required=True)
+    lib = sub.add_parser("library")
+    lib.add_argument("out")
+    lib.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
-    if a.action == "mfma":
+    if a.action == "waves":
+        waves_md(a.dirs, a.kernels, a.out, a.cmds, a.title)
+    elif a.action == "library":
+        library_md(a.out, a.cmd)
+    elif a.action == "mfma":
         mfma_md(a.pmc, a.stats, a.out, a.cmd_pmc, a.cmd_stats, a.title)
     elif a.action == "stats":
         stats_md(a.src, a.out, a.cmd, a.title, a.note, a.split_at)

@@ -65,6 +65,7 @@ __device__ __forceinline__ int swz(int r) {
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2nt __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -552,6 +553,34 @@ __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, i
           *reinterpret_cast<uint4*>(dst) = v;
       }
     }
+  }
+}
+
+// Writes this wave's bf16 output straight from the accumulators (no LDS staging): for each
+// fragment row-block, lane l stores its row (l % 32) and, per item group, the four consecutive
+// columns of its lane half (8 bytes; the two halves fill 16 contiguous bytes).  val and col_of as
+// for stage_store_bf16; NT marks the stores non-temporal.
+template <class C, int NQ, bool NT = false, class Val, class Col>
+__device__ __forceinline__ void direct_store_bf16(uint16_t* out, int ld, int row0, int row_end, int col0, int ncols,
+                                                  int lane, Val val, Col col_of) {
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int r = row0 + fm * 32 + (lane & 31);
+    if (r >= row_end) continue;
+    uint16_t* orow = out + (size_t)r * ld + col0 + (lane >> 5) * 4;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int c = col_of(fn, q);
+        if (col0 + c + (lane >> 5) * 4 >= ncols) continue;
+        const uint32_t x = pack_bf16x2(val(fm, fn, q, 0), val(fm, fn, q, 1));
+        const uint32_t y = pack_bf16x2(val(fm, fn, q, 2), val(fm, fn, q, 3));
+        if constexpr (NT)
+          __builtin_nontemporal_store(u32x2nt{x, y}, reinterpret_cast<u32x2nt*>(orow + c));
+        else
+          *reinterpret_cast<uint2*>(orow + c) = make_uint2(x, y);
+      }
   }
 }
 
