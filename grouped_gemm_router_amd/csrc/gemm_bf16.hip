@@ -647,12 +647,24 @@ __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, cons
       o.w = pack_bf16x2(acc[6], acc[7]);
       *reinterpret_cast<uint4*>(dX + (size_t)t * p.H + c * 8) = o;
     }
-    // d_topk_w: lane j of the token's first slice sums slot j's partials (k <= 32 lanes)
+    // d_topk_w: lane j of the token's first slice sums slot j's partials (k <= 32 lanes), eight
+    // loads in flight (eight running sums added in a fixed order at the end)
     if (sl == 0 && lane < p.k) {
       const int r = sr[lane];
-      float s = 0.f;
-      for (int q = 0; r >= 0 && q < p.nparts; ++q) s += p.dwt_part[(size_t)r * p.nparts + q];
-      dtw[t * p.k + lane] = s;
+      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (r >= 0) {
+        const float* part = p.dwt_part + (size_t)r * p.nparts;
+        int q = 0;
+        for (; q + 8 <= p.nparts; q += 8) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = part[q + i];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s8[i] += v[i];
+        }
+        for (; q < p.nparts; ++q) s8[0] += part[q];
+      }
+      dtw[t * p.k + lane] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
     }
   }
 }
