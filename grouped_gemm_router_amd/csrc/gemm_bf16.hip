@@ -20,6 +20,8 @@ using CfgRows = RowCfg<256, 256, 2, MOE_ROWS_WAVES_N, MOE_ROWS_BK, (MOE_ROWS_BK 
 // padding in its MFMAs.
 //   192 x 256: two 56 KB stages;  128 x 256: three 48 KB stages;
 //   64 x 256:  8 waves side by side, three 40 KB stages.
+// the same full tiles on the deep-B schedule (its epilogue stages 4 KB per wave in one A stage)
+using CfgRowsDB = RowCfg<256, 256, 2, 4, 64, 2, 4096>;
 using CfgRem192 = RowCfg<192, 256, 2, 4, 64, 2>;
 using CfgRem128 = RowCfg<128, 256, 2, 4, 64, 3>;
 using CfgRem64 = RowCfg<64, 256, 1, 8, 64, 3>;
@@ -520,10 +522,17 @@ using BwdRecomputeOpsAny = BwdRecomputeOps<C, ROWS_ALL, ACT_ANY>;
 // activation switch does not fit the registers of 256-row tiles)
 using CfgRecAny = RowCfg<128, 256, 2, 4, 64, 3>;
 
-MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup, FwdGateUpOps)
-MOE_ROWS_SPLIT_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny)
-MOE_ROWS_SPLIT_KERNEL(k_fwd_down, FwdDownOps)
-MOE_ROWS_SPLIT_KERNEL(k_bwd_p, BwdPOps)
+// the four passes, the full one on the deep-B schedule
+#define MOE_ROWS_SPLIT_DB_KERNEL(NAME, OPS)                                                         \
+  __global__ void __launch_bounds__(CfgRowsDB::NT) NAME(const GemmArgs p) {                          \
+    rows_gemm_split_body_db<CfgRowsDB, CfgRem192, CfgRem128, CfgRem64, OPS<CfgRowsDB, ROWS_FULL>,    \
+                            OPS<CfgRem192, ROWS_REM_Q3>, OPS<CfgRem128, ROWS_REM_Q2>,                \
+                            OPS<CfgRem64, ROWS_REM_Q1>, GemmArgs>(p);                                \
+  }
+MOE_ROWS_SPLIT_DB_KERNEL(k_fwd_gateup, FwdGateUpOps)
+MOE_ROWS_SPLIT_DB_KERNEL(k_fwd_gateup_act, FwdGateUpOpsAny)
+MOE_ROWS_SPLIT_DB_KERNEL(k_fwd_down, FwdDownOps)
+MOE_ROWS_SPLIT_DB_KERNEL(k_bwd_p, BwdPOps)
 // the recompute over the four row passes: the remainders of at most 64 rows take 64 x 256 tiles
 // of 8 waves of 32 x 64 (every pass keeps 4 waves across the 256 columns, as the router-weight
 // partial sums are laid out)
@@ -536,7 +545,7 @@ __global__ void __launch_bounds__(CfgRows::NT) k_bwd_recompute(const GemmArgs p)
 __global__ void __launch_bounds__(CfgRecAny::NT) k_bwd_recompute_act(const GemmArgs p) {
   rows_gemm_body<CfgRecAny, BwdRecomputeOpsAny<CfgRecAny>, GemmArgs>(p);
 }
-MOE_ROWS_SPLIT_KERNEL(k_bwd_dx_rows, BwdDXOps)
+MOE_ROWS_SPLIT_DB_KERNEL(k_bwd_dx_rows, BwdDXOps)
 // the ungated (ReLU^2) expert
 MOE_ROWS_SPLIT_KERNEL(k_fwd_up, FwdUpOps)
 __global__ void __launch_bounds__(CfgRecUp::NT) k_bwd_recompute_up(const GemmArgs p) {
@@ -553,21 +562,27 @@ static int row_grid(const GemmArgs& a, int N) {
   long g = tiles < cap ? tiles : cap;
   return (int)((g + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
 }
+// grid of a kernel on lane tables: every pass's tiles fit 64 per workgroup
+static int lane_row_grid(const GemmArgs& a, int N) {
+  const long A = (long)a.T * a.k;
+  const long bound = (A / 256 + (a.E < A ? a.E : A) + 1) * ((N + 255) / 256);
+  return lanes_grid(bound, (long)num_cus());
+}
 hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s) {
   if (a.act == ACT_RELU2) {
     hipLaunchKernelGGL(k_fwd_up, dim3(row_grid<CfgRows>(a, a.I)), dim3(CfgRows::NT), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_fwd_gateup : k_fwd_gateup_act, dim3(row_grid<CfgRows>(a, 2 * a.I)),
-                     dim3(CfgRows::NT), 0, s, a);
+  hipLaunchKernelGGL(a.act == ACT_SWIGLU ? k_fwd_gateup : k_fwd_gateup_act, dim3(lane_row_grid(a, 2 * a.I)),
+                     dim3(CfgRowsDB::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_fwd_down, dim3(row_grid<CfgRows>(a, a.H)), dim3(CfgRows::NT), 0, s, a);
+  hipLaunchKernelGGL(k_fwd_down, dim3(lane_row_grid(a, a.H)), dim3(CfgRowsDB::NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_p, dim3(row_grid<CfgRows>(a, a.I)), dim3(CfgRows::NT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_p, dim3(lane_row_grid(a, a.I)), dim3(CfgRowsDB::NT), 0, s, a);
   return hipGetLastError();
 }
 int bwd_nparts(int I, int act) {
@@ -586,8 +601,10 @@ hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(a.act == ACT_RELU2 ? k_bwd_dx_rows_up : k_bwd_dx_rows, dim3(row_grid<CfgRows>(a, a.H)),
-                     dim3(CfgRows::NT), 0, s, a);
+  if (a.act == ACT_RELU2)
+    hipLaunchKernelGGL(k_bwd_dx_rows_up, dim3(row_grid<CfgRows>(a, a.H)), dim3(CfgRows::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_bwd_dx_rows, dim3(lane_row_grid(a, a.H)), dim3(CfgRowsDB::NT), 0, s, a);
   return hipGetLastError();
 }
 // dX[t] = bf16(sum_j dXr[slot_row[t*k+j]]), d_topk_w[t,j] = sum of the row's partials (slots

@@ -34,7 +34,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NST_>
+// EPI_: bytes of LDS scratch per wave for the epilogue's staging (default: a stage's share).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NST_, int EPI_ = 0>
 struct RowCfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M_ * WAVES_N_;
@@ -44,6 +45,7 @@ struct RowCfg {
   static constexpr int BK = BK_, CPR = BK_ / 8, NST = NST_;
   static constexpr int A_SLOTS = BM * CPR, B_SLOTS = BN * CPR;      // 16-byte slots per stage
   static constexpr int STAGE = A_SLOTS + B_SLOTS;
+  static constexpr int EPI = EPI_ ? EPI_ : STAGE * 16 / NW;
   static_assert(CPR == 4 || CPR == 8, "k-tile of 32 or 64 bf16");
   static_assert(A_SLOTS % (64 * NW) == 0 && B_SLOTS % (64 * NW) == 0, "whole load instructions per wave");
 };
@@ -230,8 +232,10 @@ struct FragAddr {
 // NLOAD global->LDS load instructions of a later k-tile (issue(j), j < NLOAD)
 // are spread over the sub-steps, one between two MFMAs, so that no wave stalls
 // on a burst of vector-memory issues before its MFMAs.
+// The A operand is read at sa + fa.a and B at sb + fa.b; fa.b counts from the start of a
+// two-operand stage (A first), so for separate stages sb is the B stage less the A part's bytes.
 template <class C, bool LOADS, int NLOAD, bool BKM, class Issue>
-__device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragAddr<C, BKM>& fa,
+__device__ __forceinline__ void mma_ktile_rows(const uint8_t* sa, const uint8_t* sb, const FragAddr<C, BKM>& fa,
                                                f32x16 (&acc)[C::FM][C::FN], Issue issue) {
   constexpr int KK = C::BK / 16;
   constexpr int NR = C::FM + (BKM ? 2 : 1) * C::FN, NM = C::FM * C::FN;
@@ -241,13 +245,13 @@ __device__ __forceinline__ void mma_ktile_rows(const uint8_t* stage, const FragA
   auto load = [&](int kk, int buf) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
-      a[buf][fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.a[fm] ^ (32u * kk))));
+      a[buf][fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + (fa.a[fm] ^ (32u * kk))));
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       if constexpr (BKM)
-        b[buf][fn] = tr_frag((const lds_u8*)stage, fa.b[fn] + 16u * kk * (C::BN * 2), C::BN * 2);
+        b[buf][fn] = tr_frag((const lds_u8*)sb, fa.b[fn] + 16u * kk * (C::BN * 2), C::BN * 2);
       else
-        b[buf][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + (fa.b[fn] ^ (32u * kk))));
+        b[buf][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + (fa.b[fn] ^ (32u * kk))));
     }
   };
   load(0, 0);
@@ -300,7 +304,7 @@ __device__ __forceinline__ void wait_ktiles(int pending) {
 // not use) for staging the output tile into whole-row stores.
 template <class C>
 struct RowEpiLds {
-  static constexpr int BYTES = C::STAGE * 16 / C::NW;
+  static constexpr int BYTES = C::EPI;
 };
 
 // LDS of the schedule: prefix of per-expert tile counts (up to 1024 experts) and the
@@ -325,7 +329,10 @@ struct EarlyNext<T, std::void_t<decltype(T::EARLY_NEXT)>> : std::bool_constant<T
 // Every tile of Ops' schedule, with the stages at smem (C::NST * C::STAGE uint4) and the
 // schedule's scratch at sched_lds.  `carry` is XcdWalk's deal position, updated for a
 // schedule that follows on the same grid.
-template <class C, class Ops, class P>
+// With LT the schedule's scratch is the stage area (sched_lds is not used) and the workgroup's
+// tiles come from a lane table built when the pass starts (the launch gives no workgroup more
+// than LANE_TILES tiles of a pass).
+template <class C, class Ops, class P, bool LT = false>
 __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sched_lds, int& carry) {
   static_assert(C::NT / 64 <= 16, "schedule scratch");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -336,11 +343,26 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
   constexpr int PERK = AL::PER + BL::PER;                 // real load instructions per k-tile per wave
 
   typename Ops::Sched sched;
-  Ops::init_sched(sched, p, sched_lds, sched_lds + 1025);
+  int* pre = LT ? reinterpret_cast<int*>(smem) : sched_lds;
+  Ops::init_sched(sched, p, pre, pre + 1025);
   XcdWalk walk;
   carry = walk.init(sched.total, carry);
-  if (!walk.valid()) return;
-  Tile tl = sched.tile(walk.t);
+  LaneTiles<typename Ops::Sched> lt;
+  int ntile;
+  if constexpr (LT) {
+    lt.init(sched, walk.t, walk.step, walk.end);
+    ntile = lt.n;
+    __syncthreads();                                      // the prefix is read before loads land on it
+  } else {
+    ntile = walk.t < walk.end ? (walk.end - walk.t + walk.step - 1) / walk.step : 0;
+  }
+  if (ntile == 0) return;
+  auto tile_at = [&](int i) {
+    if constexpr (LT) return lt.get(sched, i);
+    else return sched.tile(walk.t + i * walk.step);
+  };
+  int ti = 0;                                             // the current tile's index
+  Tile tl = tile_at(0);
   FragAddr<C, BKM> fa;
   fa.init(wm, wn, lane);
   AL al;
@@ -382,18 +404,18 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
           if (j < AL::PER) al.issue_one(p, cur_tile, k0, st, j);
           else bl.issue_one(p, cur_tile, k0, st + C::A_SLOTS, j - AL::PER);
         };
-        mma_ktile_rows<C, true, PERK, BKM>(reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE), fa, acc, issue);
+        const uint8_t* cst = reinterpret_cast<const uint8_t*>(smem + cs * C::STAGE);
+        mma_ktile_rows<C, true, PERK, BKM>(cst, cst, fa, acc, issue);
       }
       // last k step: its loads are the next tile's first k-tile
       if (nk > 1 || !prewaited) wait_vmcnt<0>();
       __syncthreads();
       const int scratch = (base + nk - 1) & 1;            // the stage this step reads
-      walk.next();
-      const bool more = walk.valid();
+      const bool more = ++ti < ntile;
       {
         // without a next tile the same loads fetch this tile's first k-tile again (in bounds,
         // never read), so that the MFMA sequence has no branch around it
-        tl = more ? sched.tile(walk.t) : cur_tile;
+        tl = more ? tile_at(ti) : cur_tile;
         al.init(p, tl);
         bl.init(p, tl);
         uint4* st = smem + (scratch ^ 1) * C::STAGE;
@@ -401,7 +423,8 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
           if (j < AL::PER) al.issue_one(p, tl, 0, st, j);
           else bl.issue_one(p, tl, 0, st + C::A_SLOTS, j - AL::PER);
         };
-        mma_ktile_rows<C, true, PERK, BKM>(reinterpret_cast<const uint8_t*>(smem + scratch * C::STAGE), fa, acc, issue);
+        const uint8_t* sst = reinterpret_cast<const uint8_t*>(smem + scratch * C::STAGE);
+        mma_ktile_rows<C, true, PERK, BKM>(sst, sst, fa, acc, issue);
       }
       // every wave is past its last LDS read before the stage it read becomes scratch
       __syncthreads();
@@ -439,7 +462,7 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
           else bl.issue_one(p, tl, nxt * C::BK, st + C::A_SLOTS, j - AL::PER);
         };
         const uint8_t* cur = reinterpret_cast<const uint8_t*>(smem + (kt % C::NST) * C::STAGE);
-        mma_ktile_rows<C, decltype(loads)::value, PERK, BKM>(cur, fa, acc, issue);
+        mma_ktile_rows<C, decltype(loads)::value, PERK, BKM>(cur, cur, fa, acc, issue);
       };
       // the last NST - 1 k steps issue nothing: peeled, not branched, so that the
       // two instantiations never meet inside one loop body
@@ -449,11 +472,10 @@ __device__ __forceinline__ void rows_gemm_tiles(const P& p, uint4* smem, int* sc
       // every wave is past its last LDS read before any stage is refilled
       __syncthreads();
       const Tile done = tl;
-      walk.next();
-      const bool more = walk.valid();
+      const bool more = ++ti < ntile;
       if (more) {
         // start the next tile's loads, then run this tile's epilogue under them
-        tl = sched.tile(walk.t);
+        tl = tile_at(ti);
         al.init(p, tl);
         bl.init(p, tl);
         nk = (tl.k_hi - tl.k_lo) / C::BK;
@@ -481,6 +503,117 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
   rows_gemm_tiles<C, Ops, P>(p, smem, sched_lds, carry);
 }
 
+// The full-tile pass with the weight operand requested two k steps ahead: two A stages and three
+// B stages, [A0 | A1 | B0 | B1 | B2] (2 x 32 KB + 3 x 32 KB = 160 KB for 256 x 256 x 64 tiles),
+// and the row operand one k step ahead.  k-tiles are numbered g over the workgroup's tiles (nk per
+// tile; A k-tile g in A stage g mod 2, B k-tile g in B stage g mod 3).  Step g waits for A and B
+// k-tile g, then issues A k-tile g + 1 and B k-tile g + 2 (the A loads first, so that waiting for
+// all but the last PB loads leaves only B k-tile g + 2 in flight); loads past the workgroup's last
+// tile fetch its last k-tile 0 again (in bounds, never read).  At a tile's end the epilogue waits
+// for the next step's k-tiles, stages its output in the A stage just read and lets its stores
+// drain under the next step, as in the two-stage schedule.  The schedule's prefix and the tile
+// lookups use the stage area before the first load (lane table).  A gathered row operand's loader
+// loads its token ids when it moves to the next tile (at a tile's last step); the compiler waits
+// for those loads with vmcnt(0), which also drains the k-tiles in flight, once per tile.
+template <class C, class Ops, class P>
+__device__ __forceinline__ void rows_gemm_tiles_db(const P& p, uint4* smem, int& carry) {
+  static_assert(C::NST == 2 && C::BM == C::BN && EarlyNext<Ops>::value, "two stages, square tiles");
+  static_assert(C::EPI * C::NW <= C::A_SLOTS * 16, "epilogue staging inside one A stage");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  constexpr bool BKM = BKMajor<Ops>::value;
+  using AL = DirectRows<C, C::BM, typename Ops::SrcA, P>;
+  using BL = std::conditional_t<BKM, KMajorRowsB<C, typename Ops::SrcB, P>, DirectRows<C, C::BN, typename Ops::SrcB, P>>;
+  constexpr int PA = AL::PER, PB = BL::PER, PERK = PA + PB;
+  uint4* const As = smem;                                 // A stage s: As + s * A_SLOTS
+  uint4* const Bs = smem + 2 * C::A_SLOTS;                // B stage s: Bs + s * B_SLOTS
+
+  typename Ops::Sched sched;
+  int* pre = reinterpret_cast<int*>(smem);
+  Ops::init_sched(sched, p, pre, pre + 1025);
+  XcdWalk walk;
+  carry = walk.init(sched.total, carry);
+  LaneTiles<typename Ops::Sched> lt;
+  lt.init(sched, walk.t, walk.step, walk.end);
+  const int ntile = lt.n;
+  __syncthreads();                                        // the prefix is read before loads land on it
+  if (ntile == 0) return;
+  FragAddr<C, BKM> fa;
+  fa.init(wm, wn, lane);
+
+  // load cursors: the tile and k-tile each operand's next load fetches
+  Tile ta = lt.get(sched, 0), tb = ta;
+  const int nk = (ta.k_hi - ta.k_lo) / C::BK;             // the same for every tile of the pass
+  int ia = 0, ka = 0, ib = 0, kb = 0;
+  AL al;
+  BL bl;
+  al.init(p, ta);
+  bl.init(p, tb);
+  auto next_a = [&]() {
+    if (++ka == nk) {
+      ka = 0;
+      if (ia + 1 < ntile) {
+        ta = lt.get(sched, ++ia);
+        al.init(p, ta);
+      }
+    }
+  };
+  auto next_b = [&]() {
+    if (++kb == nk) {
+      kb = 0;
+      if (ib + 1 < ntile) {
+        tb = lt.get(sched, ++ib);
+        bl.init(p, tb);
+      }
+    }
+  };
+  // prologue: A k-tile 0, B k-tiles 0 and 1
+  al.issue(p, ta, 0, As);
+  next_a();
+  bl.issue(p, tb, 0, Bs);
+  next_b();
+  bl.issue(p, tb, kb * C::BK, Bs + C::B_SLOTS);
+  next_b();
+  int g = 0;                                              // the k-tile the next step computes
+  bool prewaited = false;
+  for (int ti = 0; ti < ntile; ++ti) {
+    const Tile cur = lt.get(sched, ti);
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+    for (int k = 0; k < nk; ++k, ++g) {
+      if (!prewaited) wait_vmcnt<PB>();
+      prewaited = false;
+      __syncthreads();
+      uint4* sta = As + ((g + 1) & 1) * C::A_SLOTS;
+      uint4* stb = Bs + ((g + 2) % 3) * C::B_SLOTS;
+      const int k0a = ka * C::BK, k0b = kb * C::BK;
+      auto issue = [&](int j) {
+        if (j < PA) al.issue_one(p, ta, k0a, sta, j);
+        else bl.issue_one(p, tb, k0b, stb, j - PA);
+      };
+      const uint8_t* sa = reinterpret_cast<const uint8_t*>(As + (g & 1) * C::A_SLOTS);
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(Bs + (g % 3) * C::B_SLOTS) - C::A_SLOTS * 16;
+      mma_ktile_rows<C, true, PERK, BKM>(sa, sb, fa, acc, issue);
+      next_a();
+      next_b();
+    }
+    // every wave is past its reads of the A stage just read (the staging area) and its B stage
+    __syncthreads();
+    wait_vmcnt<PB>();                                     // the next step's A and B k-tiles
+    prewaited = true;
+    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(As + ((g - 1) & 1) * C::A_SLOTS) + wave * C::EPI;
+    Ops::epilogue(p, cur, acc, wm, wn, lane, wave_lds);
+    // the staging area receives the next step's A load
+    __syncthreads();
+  }
+  wait_vmcnt<0>();                                        // no LDS write in flight when the pass ends
+}
+
 // Four passes over the experts' rows in one kernel, sharing one LDS allocation:
 // the full 256-row tiles (and remainders above 192 rows) with configuration CF,
 // then each remainder of at most 192, 128 and 64 rows in one C3, C2 or C1 tile.
@@ -503,6 +636,24 @@ __device__ __forceinline__ void rows_gemm_split_body(const P& p) {
   rows_gemm_tiles<C2, Ops2, P>(p, smem, sched_lds, carry);
   __syncthreads();
   rows_gemm_tiles<C1, Ops1, P>(p, smem, sched_lds, carry);
+}
+
+// The four passes with the full-tile pass on the deep-B schedule (rows_gemm_tiles_db) and the
+// remainder passes on lane tables, all in one LDS allocation with no schedule scratch beside it.
+template <class CF, class C3, class C2, class C1, class OpsF, class Ops3, class Ops2, class Ops1, class P>
+__device__ __forceinline__ void rows_gemm_split_body_db(const P& p) {
+  static_assert(C3::NT == CF::NT && C2::NT == CF::NT && C1::NT == CF::NT, "one block shape");
+  constexpr int SDB = 2 * CF::A_SLOTS + 3 * CF::B_SLOTS;
+  constexpr int SMAX = cmax<cmax<SDB, C3::NST * C3::STAGE>(), cmax<C2::NST * C2::STAGE, C1::NST * C1::STAGE>()>();
+  __shared__ uint4 smem[SMAX];
+  int carry = 0;
+  rows_gemm_tiles_db<CF, OpsF, P>(p, smem, carry);
+  __syncthreads();
+  rows_gemm_tiles<C3, Ops3, P, true>(p, smem, nullptr, carry);
+  __syncthreads();
+  rows_gemm_tiles<C2, Ops2, P, true>(p, smem, nullptr, carry);
+  __syncthreads();
+  rows_gemm_tiles<C1, Ops1, P, true>(p, smem, nullptr, carry);
 }
 
 // Stages this wave's bf16 output, one 32-row fragment row-block at a time,

@@ -41,6 +41,7 @@ struct WgCfg {
   static constexpr int A_SLOTS = BM * BK / 8, B_SLOTS = BN * BK / 8;   // 16-byte slots per stage and part
   static constexpr int B_OFF = NA * A_SLOTS;                           // first B slot of a stage
   static constexpr int STAGE = NA * A_SLOTS + NB * B_SLOTS;
+  static constexpr int EPI = STAGE * 16 / NW;                          // epilogue staging bytes per wave
   static constexpr int IDS = 2048;
   static_assert(BK % 16 == 0 && NST * STAGE * 16 + IDS * 4 <= 156 * 1024, "k-tile and LDS budget");
   static_assert(IDS % BK == 0 && IDS >= NST * BK, "whole k-tiles per id window");

@@ -133,7 +133,9 @@ struct RowGroups {
   // share GROUP_M row blocks and a few weight column blocks, and the next n-tiles of the group
   // find the row blocks still in L2; this pays where the K extent is short (row blocks of a few
   // hundred KB) and N is wide.
-  __device__ Tile tile(int t) const {
+  // Tile t's fields (expert, first row, end of the expert's rows, first column) in v[0..3]; each
+  // lane may look up a different tile.
+  __device__ void tile_lane(int t, int (&v)[4]) const {
     const int mt_lin = t / ntiles_n;
     // largest e with prefix[e] <= mt_lin (experts with no tiles have prefix[e] == prefix[e+1])
     int lo = 0, hi = E - 1;
@@ -153,18 +155,68 @@ struct RowGroups {
       mt = g * GROUP_M + r % gm;
       nt = r / gm;
     }
-    // every lane computes the same tile: keep its fields in scalar registers
+    const int o0 = offsets[lo], o1 = offsets[lo + 1];
+    v[0] = lo;
+    v[1] = o0 + first_row(o1 - o0) + mt * BM;
+    v[2] = o1;
+    v[3] = nt * BN;
+  }
+  // the tile of wave-uniform fields v, in scalar registers
+  __device__ Tile tile_of(const int (&v)[4]) const {
     Tile tl;
-    tl.e = __builtin_amdgcn_readfirstlane(lo);
-    tl.m0 = __builtin_amdgcn_readfirstlane(offsets[lo] + first_row(offsets[lo + 1] - offsets[lo]) + mt * BM);
-    tl.m_end = __builtin_amdgcn_readfirstlane(offsets[lo + 1]);
-    tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
-    tl.nt = __builtin_amdgcn_readfirstlane(nt);
+    tl.e = __builtin_amdgcn_readfirstlane(v[0]);
+    tl.m0 = __builtin_amdgcn_readfirstlane(v[1]);
+    tl.m_end = __builtin_amdgcn_readfirstlane(v[2]);
+    tl.n0 = __builtin_amdgcn_readfirstlane(v[3]);
+    tl.nt = tl.n0 / BN;
     tl.k_lo = 0;
     tl.k_hi = K;
     return tl;
   }
+  // every lane computes the same tile
+  __device__ Tile tile(int t) const {
+    int v[4];
+    tile_lane(t, v);
+    return tile_of(v);
+  }
 };
+
+// This workgroup's tiles of an XcdWalk, one per lane: lane j looks up the fields of the
+// workgroup's tile j once, when a pass starts (the schedule's LDS may be reused afterwards), and
+// get(i) reads them back with v_readlane.  Launches size their grids so that no workgroup gets
+// more than 64 tiles of one pass (lanes_grid).
+constexpr int LANE_TILES = 64;
+template <class S>
+struct LaneTiles {
+  int n;                   // this workgroup's tiles, at most LANE_TILES
+  int v[4];                // lane j: the fields of tile j
+  __device__ void init(const S& s, int t0, int step, int end) {
+    n = t0 < end ? (end - t0 + step - 1) / step : 0;
+    if (n > 0) {
+      const int t = t0 + (int)(threadIdx.x & 63) * step;
+      s.tile_lane(t < end ? t : t0, v);                 // lanes past the last tile repeat the first
+    }
+  }
+  __device__ Tile get(const S& s, int i) const {
+    int u[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) u[f] = __builtin_amdgcn_readlane(v[f], i);
+    return s.tile_of(u);
+  }
+};
+
+// Grid of a persistent launch over at most `tiles_bound` tiles per pass: one workgroup per CU
+// (`cap`), or more, a multiple of the XCD count, so that XcdWalk deals no workgroup more than
+// LANE_TILES tiles of a pass.
+inline int lanes_grid(long tiles_bound, long cap) {
+  long per_xcd = (tiles_bound + NUM_XCD - 1) / NUM_XCD;          // tiles of the busiest XCD
+  long bpx = (per_xcd + LANE_TILES - 1) / LANE_TILES;             // workgroups per XCD it needs
+  long g = bpx * NUM_XCD;
+  long c = (cap + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  if (tiles_bound < c) c = (tiles_bound + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  const long r = g > c ? g : c;
+  return (int)(r > NUM_XCD ? r : NUM_XCD);
+}
 
 template <int BM, int BN, int NT>
 struct WeightGrad {
