@@ -117,7 +117,7 @@ def stats_md(src: str, out: str, cmd: str, title: str, note: str = "", split_at:
     if note:
         lines += [note, ""]
     if split_at:
-        first = next((i for i, r in enumerate(trace) if split_at in _short(r["Kernel_Name"])), len(trace))
+        first = next((i for i, r in enumerate(trace) if split_at in r["Kernel_Name"]), len(trace))
         lines += [f"Dispatches before the first `{split_at}`:", ""] + _trace_table(trace[:first])
         if first < len(trace):
             lines += ["", f"From the first `{split_at}` on:", ""] + _trace_table(trace[first:])
