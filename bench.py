@@ -23,8 +23,9 @@ of the flush), and times each step on its own (reported under cold_cache).
 
 Prints one JSON line.  Default workload: prefill (T=4096 tokens, hidden 2048,
 intermediate 512, 256 experts, top-8, bf16); its line also carries a
-``configs`` block with the decode, large MXFP8 and training workloads measured
-the same way (each with its own roofline).  Other workloads (--workload decode
+``configs`` block with the prefill shape under rank-Zipf routing (every expert
+active, non-trivial combine weights), the decode, large MXFP8 and training
+workloads, measured the same way (each with its own roofline).  Other workloads (--workload decode
 | train | large_mxfp8 | tiny | prefill_rankzipf | model-contract shapes) are for
 diagnostics.
 """
@@ -43,7 +44,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 FLUSH_BYTES = 512 << 20        # read before each cold-cache step: more than L2 (8 x 4 MB) + Infinity Cache (256 MB)
-EXTRA_CONFIGS = ("decode", "large_mxfp8", "train")
+EXTRA_CONFIGS = ("prefill_rankzipf", "decode", "large_mxfp8", "train")
 
 
 def parse(argv=None):

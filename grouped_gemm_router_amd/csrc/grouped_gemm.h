@@ -206,16 +206,17 @@ struct LaneTiles {
 };
 
 // Grid of a persistent launch over at most `tiles_bound` tiles per pass: one workgroup per CU
-// (`cap`), or more, a multiple of the XCD count, so that XcdWalk deals no workgroup more than
-// LANE_TILES tiles of a pass.
+// (`cap`, rounded to the XCD count), or, when XcdWalk would then deal a workgroup more than
+// LANE_TILES tiles of a pass, the next multiple of that grid that deals at most LANE_TILES (the
+// extra workgroups run in whole rounds after the first, each with an equal share).
 inline int lanes_grid(long tiles_bound, long cap) {
-  long per_xcd = (tiles_bound + NUM_XCD - 1) / NUM_XCD;          // tiles of the busiest XCD
-  long bpx = (per_xcd + LANE_TILES - 1) / LANE_TILES;             // workgroups per XCD it needs
-  long g = bpx * NUM_XCD;
   long c = (cap + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
   if (tiles_bound < c) c = (tiles_bound + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
-  const long r = g > c ? g : c;
-  return (int)(r > NUM_XCD ? r : NUM_XCD);
+  if (c < NUM_XCD) c = NUM_XCD;
+  const long per_xcd = (tiles_bound + NUM_XCD - 1) / NUM_XCD;    // tiles of the busiest XCD
+  const long bpx = (per_xcd + LANE_TILES - 1) / LANE_TILES;       // workgroups per XCD it needs
+  const long g = bpx * NUM_XCD;
+  return (int)(g > c ? (g + c - 1) / c * c : c);
 }
 
 template <int BM, int BN, int NT>

@@ -50,6 +50,29 @@ def test_grouped_gemm_vs_oracle(dtype, N, K):
     assert torch.isnan(C[rows:].float()).all(), "rows past the last expert were written"
 
 
+@pytest.mark.parametrize("K", [64, 128])
+def test_grouped_gemm_many_tiles_per_workgroup(K):
+    """More full tiles than 64 per workgroup at one workgroup per CU (8 experts x 70,000 rows x 8
+    column tiles: the launch then grows the grid so that no workgroup's lane table of tiles
+    overflows), with K = 64 (one k-tile per tile, so the loads run two tiles ahead) and K = 128.
+    Every expert's first and last row and random rows against the oracle."""
+    from grouped_gemm_router_amd import binding as B
+    E, N, n = 8, 2048, 70_000
+    m_indptr = np.concatenate([[0], np.cumsum([n] * E)]).astype(np.int32)
+    M = int(m_indptr[-1])
+    _say("grouped gemm many tiles", M, N, K)
+    A, Bt = _operands(84 + K, M, N, K, E)
+    C = B.grouped_gemm(to_dev(A), to_dev(Bt), torch.from_numpy(m_indptr).cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(85)
+    rows = set(rng.integers(0, M, 160).tolist()) | set(m_indptr[:-1].tolist()) | set((m_indptr[1:] - 1).tolist())
+    rows = np.array(sorted(rows))
+    e_of = np.searchsorted(m_indptr, rows, side="right") - 1
+    sub_indptr = np.searchsorted(e_of, np.arange(E + 1), side="left").astype(np.int32)
+    ref = orc.grouped_gemm(A[rows], Bt, sub_indptr)
+    check_close(to_f64(C[torch.from_numpy(rows).cuda()]), ref, f"many tiles K={K}")
+
+
 def test_expert_mlp_down_is_the_grouped_gemm():
     """The layer's O rows equal the standalone grouped GEMM of its h rows with the packed
     W_down, bit for bit (the same kernel and tiles)."""
