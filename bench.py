@@ -44,7 +44,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 FLUSH_BYTES = 512 << 20        # read before each cold-cache step: more than L2 (8 x 4 MB) + Infinity Cache (256 MB)
-EXTRA_CONFIGS = ("prefill_rankzipf", "decode", "large_mxfp8", "train")
+EXTRA_CONFIGS = ("prefill_rankzipf", "decode", "large_mxfp8", "train", "train_saved")
 
 
 def parse(argv=None):
@@ -135,7 +135,7 @@ def cpu_baseline(cfg, logits, X, dY, min_s=10.0, max_reps=20):
     from grouped_gemm_router_amd import workloads as wl
     cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     ntok = {"prefill": cfg.T, "decode": cfg.T, "tiny": cfg.T, "prefill_rankzipf": 1024,
-            "large_mxfp8": 128, "train": 16}.get(cfg.name, 64)
+            "large_mxfp8": 128, "train": 16, "train_saved": 16}.get(cfg.name, 64)
     if cfg.H * cfg.I >= 4096 * 2048:
         ntok = 2          # the large expert shapes: each sampled expert's weights take seconds to draw
     ntok = min(ntok, cfg.T)
@@ -205,7 +205,8 @@ def measure(cfg, args, device_draw=False):
     X = torch.from_numpy(X_np.view(np.int16)).cuda().view(torch.bfloat16)
     dY = torch.from_numpy(dY_np.view(np.int16)).cuda().view(torch.bfloat16) if cfg.backward else None
     layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation,
-                     act_limit=cfg.act_limit).load_weights(W.get("gate"), W["up"], W["down"])
+                     act_limit=cfg.act_limit, save_activations=cfg.save_activations).load_weights(
+        W.get("gate"), W["up"], W["down"])
     del W
     torch.cuda.synchronize()
 
@@ -305,6 +306,7 @@ def measure(cfg, args, device_draw=False):
     rec = {
         "workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
         "top_k": cfg.k, "active_experts": n_active, "backward": cfg.backward,
+        "saved_activations": cfg.save_activations,
         "activation": cfg.activation if not cfg.act_limit else f"{cfg.activation}({cfg.act_limit:g})",
         "dtype": "mxfp8" if cfg.dtype == "mxfp8" else "bf16",
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -333,8 +335,10 @@ def measure(cfg, args, device_draw=False):
         # algorithmic bytes of one backward call: dY and X rows, the weights, h (recomputed) and the
         # weight gradients of the active experts, dX
         bwd_bytes = 2 * weight_bytes + cfg.T * cfg.H * 2 * 3
-        rec["backward_roofline"] = _roofline("moe_backward (P, recompute, dX rows, token reduce, weight "
-                                             "gradients)", f_bwd, bwd_bytes, bwd_ms, peak)
+        name = ("moe_backward_saved (P, elementwise pass over the saved G and U, dX rows, token reduce, "
+                "weight gradients)" if cfg.save_activations else
+                "moe_backward (P, recompute, dX rows, token reduce, weight gradients)")
+        rec["backward_roofline"] = _roofline(name, f_bwd, bwd_bytes, bwd_ms, peak)
     return rec
 
 

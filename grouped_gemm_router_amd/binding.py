@@ -26,7 +26,8 @@ CALL_DISPATCH, CALL_EXPERT_MLP, CALL_BACKWARD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_validate_problem", "moe_workspace_size", "moe_check_device",
            "moe_route", "moe_dispatch", "moe_pack_weights", "moe_mx_quantize", "moe_expert_mlp",
-           "moe_combine", "moe_backward", "moe_route_backward", "moe_grouped_gemm", "moe_expert_mlp_static")
+           "moe_combine", "moe_backward", "moe_route_backward", "moe_grouped_gemm", "moe_expert_mlp_static",
+           "moe_expert_mlp_save", "moe_backward_saved")
 
 
 class MoEError(RuntimeError):
@@ -62,6 +63,8 @@ def _load() -> ctypes.CDLL:
         "moe_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_gemm": (ctypes.c_int, [I32, P, I32, I64, I32, I32, P, P, P, P, P, P]),
         "moe_expert_mlp_static": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "moe_expert_mlp_save": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P]),
+        "moe_backward_saved": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -230,6 +233,34 @@ def expert_mlp(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, scales=None, H_rows=N
     return H_rows, O_rows
 
 
+def expert_mlp_save(X, row_token, offsets, Wg_t, Wu_t, Wd_t, k, H_rows=None, O_rows=None, GU_rows=None,
+                    activation="swiglu", act_limit=0.0):
+    """The training forward that keeps its projections (moe_expert_mlp_save, bf16): returns
+    (H_rows, O_rows, GU_rows) with GU_rows [T*k, 2I] fp32, G in columns [0, I) and U in [I, 2I)."""
+    T, H = X.shape
+    E, I, _ = Wu_t.shape
+    gated = activation not in UNGATED
+    _expect(X, "X", torch.bfloat16, (T, H))
+    if gated:
+        _expect(Wg_t, "Wg_t", torch.bfloat16, (E, I, H))
+    _expect(Wu_t, "Wu_t", torch.bfloat16, (E, I, H))
+    _expect(Wd_t, "Wd_t", torch.bfloat16, (E, H, I))
+    _expect(offsets, "expert_offsets", torch.int32, (E + 1,))
+    _expect(row_token, "row_token", torch.int32, (T * k,))
+    dev = X.device
+    H_rows = torch.empty(T * k, I, dtype=torch.bfloat16, device=dev) if H_rows is None else H_rows
+    O_rows = torch.empty(T * k, H, dtype=torch.bfloat16, device=dev) if O_rows is None else O_rows
+    GU_rows = torch.empty(T * k, 2 * I, dtype=torch.float32, device=dev) if GU_rows is None else GU_rows
+    _expect(H_rows, "H_rows", torch.bfloat16, (T * k, I))
+    _expect(O_rows, "O_rows", torch.bfloat16, (T * k, H))
+    _expect(GU_rows, "GU_rows", torch.float32, (T * k, 2 * I))
+    p = problem(T, H, I, E, k, "bf16", activation, act_limit)
+    _check("moe_expert_mlp_save", lib.moe_expert_mlp_save(ctypes.byref(p), _ptr(X), _ptr(row_token), _ptr(offsets),
+                                                          _ptr(Wg_t), _ptr(Wu_t), _ptr(Wd_t), _ptr(H_rows),
+                                                          _ptr(O_rows), _ptr(GU_rows), _stream()))
+    return H_rows, O_rows, GU_rows
+
+
 def grouped_gemm(A, B_t, m_indptr, scales=None, C=None):
     """Standalone grouped GEMM over expert-major rows: C[r] = bf16(A[r] B_t[e]^T) for the rows
     m_indptr[e] <= r < m_indptr[e+1].  bf16: A [M, K], B_t [E, N, K] (pack_weights); MXFP8:
@@ -266,9 +297,11 @@ def combine(O_rows, slot_row, topk_w, Y=None):
 
 
 def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, Wg_t, Wu_t, Wd_t,
-             out=None, ws=None, activation="swiglu", act_limit=0.0):
+             out=None, ws=None, activation="swiglu", act_limit=0.0, GU_rows=None):
     """Returns (dX, dW_gate, dW_up, dW_down, d_topk_w) from the packed weights Wg_t, Wu_t
-    [E, I, H] and Wd_t [E, H, I] (pack_weights); for ReLU^2 Wg_t is None and so is dW_gate."""
+    [E, I, H] and Wd_t [E, H, I] (pack_weights); for ReLU^2 Wg_t is None and so is dW_gate.
+    With ``GU_rows`` (from expert_mlp_save) it calls moe_backward_saved: G and U are read, not
+    recomputed."""
     T, H = X.shape
     E, I, _ = Wu_t.shape
     k = topk_w.shape[1]
@@ -294,6 +327,14 @@ def backward(X, dY, topk_w, row_token, row_slot, slot_row, offsets, Wg_t, Wu_t, 
         ws, n = _workspace(p, CALL_BACKWARD, dev)
     else:
         n = ws.numel()
+    if GU_rows is not None:
+        _expect(GU_rows, "GU_rows", torch.float32, (T * k, 2 * I))
+        _check("moe_backward_saved",
+               lib.moe_backward_saved(ctypes.byref(p), _ptr(X), _ptr(dY), _ptr(topk_w), _ptr(row_token),
+                                      _ptr(row_slot), _ptr(slot_row), _ptr(offsets), _ptr(Wg_t), _ptr(Wu_t),
+                                      _ptr(Wd_t), _ptr(GU_rows), _ptr(dX), _ptr(dWg), _ptr(dWu), _ptr(dWd),
+                                      _ptr(dtw), _ptr(ws), n, _stream()))
+        return dX, dWg, dWu, dWd, dtw
     _check("moe_backward", lib.moe_backward(ctypes.byref(p), _ptr(X), _ptr(dY), _ptr(topk_w), _ptr(row_token),
                                             _ptr(row_slot), _ptr(slot_row), _ptr(offsets), _ptr(Wg_t),
                                             _ptr(Wu_t), _ptr(Wd_t), _ptr(dX), _ptr(dWg), _ptr(dWu), _ptr(dWd),

@@ -207,21 +207,24 @@ namespace {
 
 // moe_expert_mlp, with the workspace given by the caller or (use_static) the library's static
 // array of MOE_STATIC_SCRATCH_BYTES on the current device.
+// With GU (bf16 only) the forward also writes the fp32 projections of every routed row, on the
+// row-grouped GEMMs for every T.
 moe_status expert_mlp(const moe_problem* p, const void* X, const int32_t* row_token, const int32_t* expert_offsets,
                       const void* Wg_t, const void* Wu_t, const void* Wd_t, const uint8_t* Sg, const uint8_t* Su,
                       const uint8_t* Sd, void* H_rows, void* O_rows, void* ws, size_t ws_bytes, bool use_static,
-                      void* stream) {
+                      void* stream, float* GU = nullptr, bool save_gu = false) {
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
   const bool gated = p->activation != MOE_ACT_RELU2;     // ReLU^2 experts have no gate weight
   const bool rows = p->T > 0;                            // token-sized arrays may be NULL for T = 0
+  if (save_gu && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (!expert_offsets || (gated && !Wg_t) || !Wu_t || !Wd_t) return MOE_ERR_INVALID_ARG;
-  if (rows && (!X || !row_token || !H_rows || !O_rows)) return MOE_ERR_INVALID_ARG;
+  if (rows && (!X || !row_token || !H_rows || !O_rows || (save_gu && !GU))) return MOE_ERR_INVALID_ARG;
   const bool mx = p->dtype == MOE_DTYPE_MXFP8;
   if (mx != ((Sg || !gated) && Su && Sd)) return MOE_ERR_INVALID_ARG;
   if (!mx && (Sg || Su || Sd)) return MOE_ERR_INVALID_ARG;
   if (!rows) return MOE_OK;                              // empty batch: nothing to compute
-  const size_t need = mlp_ws(p);
+  const size_t need = save_gu ? 0 : mlp_ws(p);
   if (use_static) {
     if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
     ws_bytes = MOE_STATIC_SCRATCH_BYTES;
@@ -244,7 +247,8 @@ moe_status expert_mlp(const moe_problem* p, const void* X, const int32_t* row_to
     a.Hrows = (uint16_t*)H_rows;
     a.Orows = (uint16_t*)O_rows;
     a.wlist = (int32_t*)ws;
-    if (p->T <= moe::DECODE_MAX_T) return from_hip(moe::launch_decode_mlp(a, st));
+    a.GU = save_gu ? GU : nullptr;
+    if (!save_gu && p->T <= moe::DECODE_MAX_T) return from_hip(moe::launch_decode_mlp(a, st));
     hipError_t e = moe::launch_fwd_gateup(a, st);
     if (e == hipSuccess) e = moe::launch_fwd_down(a, st);
     return from_hip(e);
@@ -293,6 +297,13 @@ MOE_API moe_status moe_expert_mlp_static(const moe_problem* p, const void* X, co
                                          void* H_rows, void* O_rows, void* stream) {
   return expert_mlp(p, X, row_token, expert_offsets, Wg_t, Wu_t, Wd_t, Sg, Su, Sd, H_rows, O_rows, nullptr, 0,
                     true, stream);
+}
+
+MOE_API moe_status moe_expert_mlp_save(const moe_problem* p, const void* X, const int32_t* row_token,
+                                       const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                       const void* Wd_t, void* H_rows, void* O_rows, float* GU_rows, void* stream) {
+  return expert_mlp(p, X, row_token, expert_offsets, Wg_t, Wu_t, Wd_t, nullptr, nullptr, nullptr, H_rows, O_rows,
+                    nullptr, 0, false, stream, GU_rows, true);
 }
 
 MOE_API moe_status moe_grouped_gemm(int32_t dtype, const int32_t* m_indptr, int32_t E, int64_t M, int32_t N,
@@ -347,11 +358,17 @@ MOE_API moe_status moe_combine(const void* O_rows, const int32_t* slot_row, cons
                                       (hipStream_t)stream));
 }
 
-MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY, const float* topk_w,
-                                const int32_t* row_token, const int32_t* row_slot, const int32_t* slot_row,
-                                const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
-                                const void* Wd_t, void* dX, void* dW_gate, void* dW_up, void* dW_down,
-                                float* d_topk_w, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_backward; with save_gu, G and U come from GU (moe_expert_mlp_save) and an elementwise pass
+// over P, G and U replaces the recompute GEMM.
+moe_status backward(const moe_problem* p, const void* X, const void* dY, const float* topk_w,
+                    const int32_t* row_token, const int32_t* row_slot, const int32_t* slot_row,
+                    const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t, const void* Wd_t,
+                    const float* GU, bool save_gu, void* dX, void* dW_gate, void* dW_up, void* dW_down,
+                    float* d_topk_w, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_problem(p);
   if (s != MOE_OK) return s;
   if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -361,6 +378,7 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
     return MOE_ERR_INVALID_ARG;
   if (rows && (!X || !dY || !topk_w || !row_token || !row_slot || !slot_row || !dX || !d_topk_w))
     return MOE_ERR_INVALID_ARG;
+  if (rows && save_gu && !GU) return MOE_ERR_INVALID_ARG;
   const size_t need = bwd_ws(p);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if ((s = device_ok()) != MOE_OK) return s;
@@ -378,7 +396,8 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   a.Wg_t = (const uint16_t*)Wg_t;
   a.Wu_t = (const uint16_t*)Wu_t;
   a.Wd_t = (const uint16_t*)Wd_t;
-  a.nparts = moe::bwd_nparts(p->I, p->activation);
+  a.nparts = save_gu ? 1 : moe::bwd_nparts(p->I, p->activation);
+  a.GU = const_cast<float*>(GU);
   a.P = (float*)w8;
   w8 += align_up(A * I * 4);
   a.dGU = (uint16_t*)w8;
@@ -399,13 +418,36 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
   hipError_t e = hipSuccess;
   if (p->T > 0) {
     e = moe::launch_bwd_p(a, st);
-    if (e == hipSuccess) e = moe::launch_bwd_recompute(a, st);
+    if (e == hipSuccess) e = save_gu ? moe::launch_bwd_act_rows(a, st) : moe::launch_bwd_recompute(a, st);
     if (e == hipSuccess) e = moe::launch_bwd_dx_rows(a, st);
     if (e == hipSuccess) e = moe::launch_bwd_token_reduce(a, slot_row, (uint16_t*)dX, d_topk_w, st);
   }
   if (e == hipSuccess) e = moe::launch_bwd_dw_down(a, st);
   if (e == hipSuccess) e = moe::launch_bwd_dw_gateup(a, st);
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void* dY, const float* topk_w,
+                                const int32_t* row_token, const int32_t* row_slot, const int32_t* slot_row,
+                                const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                const void* Wd_t, void* dX, void* dW_gate, void* dW_up, void* dW_down,
+                                float* d_topk_w, void* ws, size_t ws_bytes, void* stream) {
+  return backward(p, X, dY, topk_w, row_token, row_slot, slot_row, expert_offsets, Wg_t, Wu_t, Wd_t, nullptr, false,
+                  dX, dW_gate, dW_up, dW_down, d_topk_w, ws, ws_bytes, stream);
+}
+
+MOE_API moe_status moe_backward_saved(const moe_problem* p, const void* X, const void* dY, const float* topk_w,
+                                      const int32_t* row_token, const int32_t* row_slot, const int32_t* slot_row,
+                                      const int32_t* expert_offsets, const void* Wg_t, const void* Wu_t,
+                                      const void* Wd_t, const float* GU_rows, void* dX, void* dW_gate,
+                                      void* dW_up, void* dW_down, float* d_topk_w, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return backward(p, X, dY, topk_w, row_token, row_slot, slot_row, expert_offsets, Wg_t, Wu_t, Wd_t, GU_rows, true,
+                  dX, dW_gate, dW_up, dW_down, d_topk_w, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -138,6 +138,41 @@ struct RowOpsBase {
   using Sched = RowGroups<C::BM, C::BN, C::NT, PART, (PART == ROWS_ALL ? C::BM : 256)>;
 };
 
+// Saved-activation forward: the fp32 projections of the tile's valid rows into GU [A, 2I] (G in
+// columns [0, I), U in [I, 2I)), straight from the accumulators: 16 bytes per lane, 32
+// contiguous bytes per row from the two lane halves (plain stores: as non-temporal stores these
+// partial-line writes made the training forward's gate/up GEMM 1,239 -> 1,464 us).  Item group q
+// of fragment fn holds columns col_of(fn, q) + 4 (lane / 32) + [0, 4) (relative to c0); gate(q) /
+// up(q) name its accumulator items (-1: none).
+template <class C, int NQ, class Col, class Gate, class Up>
+__device__ __forceinline__ void store_gu_f32(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN], int wm,
+                                             int c0, int lane, Col col_of, Gate gate, Up up) {
+  const int hc = (lane >> 5) * 4;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int r = t.m0 + Frag<C>::row(wm, fm, lane);
+    if (r >= t.m_end) continue;
+    float* row = p.GU + (size_t)r * (2 * p.I);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int c = c0 + col_of(fn, q) + hc;
+        if (c >= p.I) continue;
+        if (gate(q) >= 0) {
+          const int v = gate(q);
+          *reinterpret_cast<float4*>(row + c) =
+              make_float4(acc[fm][fn][v], acc[fm][fn][v + 1], acc[fm][fn][v + 2], acc[fm][fn][v + 3]);
+        }
+        if (up(q) >= 0) {
+          const int v = up(q);
+          *reinterpret_cast<float4*>(row + p.I + c) =
+              make_float4(acc[fm][fn][v], acc[fm][fn][v + 1], acc[fm][fn][v + 2], acc[fm][fn][v + 3]);
+        }
+      }
+  }
+}
+
 // h = bf16(f(X Wg, X Wu)), f the problem's gated activation (SwiGLU by default)
 template <class C, int PART = ROWS_ALL, int ACTK = ACT_SWIGLU>
 struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
@@ -155,6 +190,10 @@ struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
           return gated_act(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit);
         },
         [](int fn, int q) { return fn * 16 + q * 8; });
+    if (p.GU)
+      store_gu_f32<C, 2>(
+          p, t, acc, wm, t.nt * (C::BN / 2) + wn * C::FN * 16, lane, [](int fn, int q) { return fn * 16 + q * 8; },
+          [](int q) { return 4 * q; }, [](int q) { return 4 * q + 8; });
   }
 };
 
@@ -171,6 +210,10 @@ struct FwdUpOps : RowOpsBase<C, RSrcX, RSrcUpW, PART> {
         wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.I, lane,
         [&](int fm, int fn, int q, int j) { return relu2(acc[fm][fn][4 * q + j]); },
         [](int fn, int q) { return fn * 32 + q * 8; });
+    if (p.GU)
+      store_gu_f32<C, 4>(
+          p, t, acc, wm, t.n0 + wn * C::WTN, lane, [](int fn, int q) { return fn * 32 + q * 8; },
+          [](int) { return -1; }, [](int q) { return 4 * q; });
   }
 };
 
@@ -684,6 +727,78 @@ __global__ void __launch_bounds__(256) k_bwd_token_reduce(const GemmArgs p, cons
       dtw[t * p.k + lane] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
     }
   }
+}
+
+// Saved-activation backward, in place of the recompute: per expert-major row r (weight
+// w = topk_w[row_slot[r]]), from P and the saved fp32 G, U the same quantities the recompute's
+// epilogue forms from its accumulators, with the same expressions: h = bf16(f(G, U)),
+// <h, P> (one partial sum per row, dwt_part[r]), and w h, dg = w P df/dG, du = w P df/dU,
+// each as a bf16 value and a bf16 remainder.  One wave per row, four columns per lane and
+// step (16-byte loads, 8-byte stores); the row's partial sum adds the lanes' sums in a fixed
+// butterfly.  Rows at or past expert_offsets[E] (slots dispatch skipped) have none of these.
+__global__ void __launch_bounds__(256) k_bwd_act_rows(const GemmArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long rows = p.offsets[p.E];
+  const int I = p.I;
+  const bool gated = act_gated(p.act);
+  const int ld = gated ? 2 * I : I;                 // dGU: [dg | du] rows, or du rows (ungated)
+  const int dcol = gated ? I : 0;                   // du's first column in a dGU row
+  for (long r = (long)blockIdx.x * 4 + wave; r < rows; r += (long)gridDim.x * 4) {
+    const float w = p.topk_w[p.row_slot[r]];
+    const float* Pr = p.P + (size_t)r * I;
+    const float* Gr = p.GU + (size_t)r * (2 * I);
+    const float* Ur = Gr + I;
+    float dot = 0.f;
+    for (int c = lane * 4; c < I; c += 256) {
+      const float4 p4 = *reinterpret_cast<const float4*>(Pr + c);
+      const float4 u4 = *reinterpret_cast<const float4*>(Ur + c);
+      const float4 g4 = gated ? *reinterpret_cast<const float4*>(Gr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float Pv[4] = {p4.x, p4.y, p4.z, p4.w}, Uv[4] = {u4.x, u4.y, u4.z, u4.w};
+      const float Gv[4] = {g4.x, g4.y, g4.z, g4.w};
+      float hw[4], dg[4], du[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float hf, fg, fu;
+        if (gated) {
+          gated_act_grad(Gv[j], Uv[j], p.act, p.act_limit, hf, fg, fu);
+        } else {
+          hf = relu2(Uv[j]);
+          fg = 0.f;
+          fu = relu2_grad(Uv[j]);
+        }
+        const float hv = bf16_to_f32(f32_to_bf16(hf));
+        dot += hv * Pv[j];
+        hw[j] = w * hv;
+        dg[j] = w * Pv[j] * fg;
+        du[j] = w * Pv[j] * fu;
+      }
+      uint2 hi, lo;
+      split4(hw, hi, lo);
+      *reinterpret_cast<uint2*>(p.hw + (size_t)r * I + c) = hi;
+      *reinterpret_cast<uint2*>(p.hw_lo + (size_t)r * I + c) = lo;
+      if (gated) {
+        split4(dg, hi, lo);
+        *reinterpret_cast<uint2*>(p.dGU + (size_t)r * ld + c) = hi;
+        *reinterpret_cast<uint2*>(p.dGU_lo + (size_t)r * ld + c) = lo;
+      }
+      split4(du, hi, lo);
+      *reinterpret_cast<uint2*>(p.dGU + (size_t)r * ld + dcol + c) = hi;
+      *reinterpret_cast<uint2*>(p.dGU_lo + (size_t)r * ld + dcol + c) = lo;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+    if (lane == 0) p.dwt_part[r] = dot;
+  }
+}
+
+hipError_t launch_bwd_act_rows(const GemmArgs& a, hipStream_t s) {
+  const long A = (long)a.T * a.k;
+  long blocks = (A + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_bwd_act_rows, dim3((int)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_token_reduce(const GemmArgs& a, const int32_t* slot_row, uint16_t* dX,

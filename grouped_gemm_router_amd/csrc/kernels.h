@@ -31,6 +31,8 @@ struct GemmArgs {
   float* dXr;             // [A, H]
   float* dwt_part;        // [A, nparts]
   int nparts;
+  float* GU;              // [A, 2I] fp32: G in columns [0, I), U in [I, 2I) (saved-activation path:
+                          // written by the forward gate/up GEMM when set, read by the backward)
   uint16_t* dWg;
   uint16_t* dWu;
   uint16_t* dWd;
@@ -60,6 +62,9 @@ hipError_t launch_fwd_gateup(const GemmArgs& a, hipStream_t s);
 hipError_t launch_fwd_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_p(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_recompute(const GemmArgs& a, hipStream_t s);
+// the saved-activation backward's elementwise pass over P, G and U (in place of the recompute);
+// its router-weight partial sums are one per row
+hipError_t launch_bwd_act_rows(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dx_rows(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dw_gateup(const GemmArgs& a, hipStream_t s);

@@ -16,12 +16,17 @@ from . import binding as B
 
 class MoELayer:
     def __init__(self, H: int, I: int, E: int, k: int, dtype: str = "bf16", device="cuda",
-                 activation: str = "swiglu", act_limit: float = 0.0):
+                 activation: str = "swiglu", act_limit: float = 0.0, save_activations: bool = False):
         """``activation``: swiglu (default), swiglu_clamp, swiglu_oai, geglu, reglu or relu2
         (include/moe.h, moe_activation; relu2 experts have no gate weight); ``act_limit``: the
-        clamp of the two clamped ones."""
+        clamp of the two clamped ones.  ``save_activations`` (bf16): a forward with a backward
+        plan keeps the fp32 projections G, U of every routed row (moe_expert_mlp_save) and the
+        backward reads them instead of recomputing them (moe_backward_saved)."""
+        if save_activations and dtype != "bf16":
+            raise ValueError("saved activations are a bf16 training path")
         self.H, self.I, self.E, self.k, self.dtype = H, I, E, k, dtype
         self.activation, self.act_limit = activation, act_limit
+        self.save_activations = save_activations
         self.device = torch.device(device)
         self._plans = {}
 
@@ -67,6 +72,8 @@ class MoELayer:
         }
         if backward:
             pl["ws_bwd"] = torch.empty(B.workspace_size(p, B.CALL_BACKWARD), dtype=torch.uint8, device=dev)
+            if self.save_activations:
+                pl["GU"] = torch.empty(A, 2 * I, dtype=torch.float32, device=dev)
             pl["grads"] = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
                            torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
                            if self.activation not in B.UNGATED else None,
@@ -89,13 +96,21 @@ class MoELayer:
                    ws=pl["ws_dispatch"])
         if mlp_events is not None:
             mlp_events[0].record()
-        B.expert_mlp(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
-                     scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"],
-                     activation=self.activation, act_limit=self.act_limit)
+        self._expert_mlp(X, pl)
         if mlp_events is not None:
             mlp_events[1].record()
         B.combine(pl["O_rows"], pl["slot_row"], pl["topk_w"], pl["Y"])
         return pl["Y"]
+
+    def _expert_mlp(self, X: torch.Tensor, pl):
+        if "GU" in pl:
+            B.expert_mlp_save(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
+                              H_rows=pl["H_rows"], O_rows=pl["O_rows"], GU_rows=pl["GU"],
+                              activation=self.activation, act_limit=self.act_limit)
+        else:
+            B.expert_mlp(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
+                         scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"],
+                         activation=self.activation, act_limit=self.act_limit)
 
     def forward_routed(self, topk_idx: torch.Tensor, topk_w: torch.Tensor, X: torch.Tensor,
                        backward_plan: bool = False):
@@ -113,9 +128,7 @@ class MoELayer:
         pl["topk_w"].copy_(topk_w)
         B.dispatch(pl["topk_idx"], self.E, (pl["offsets"], pl["row_token"], pl["row_slot"], pl["slot_row"]),
                    ws=pl["ws_dispatch"])
-        B.expert_mlp(X, pl["row_token"], pl["offsets"], self.Wg_t, self.Wu_t, self.Wd_t, self.k,
-                     scales=self.scales, H_rows=pl["H_rows"], O_rows=pl["O_rows"], ws=pl["ws_mlp"],
-                     activation=self.activation, act_limit=self.act_limit)
+        self._expert_mlp(X, pl)
         B.combine(pl["O_rows"], pl["slot_row"], pl["topk_w"], pl["Y"])
         return pl["Y"]
 
@@ -140,7 +153,8 @@ class MoELayer:
         pl = self.plan(T, True)
         return B.backward(X, dY, pl["topk_w"], pl["row_token"], pl["row_slot"], pl["slot_row"], pl["offsets"],
                           self.Wg_t, self.Wu_t, self.Wd_t, out=pl["grads"],
-                          ws=pl["ws_bwd"], activation=self.activation, act_limit=self.act_limit)
+                          ws=pl["ws_bwd"], activation=self.activation, act_limit=self.act_limit,
+                          GU_rows=pl.get("GU"))
 
     def route_backward(self, T: int):
         """Gradient with respect to the router logits [T, E] fp32, from the d(top-k weights) of the

@@ -51,6 +51,7 @@ class MoEConfig:
     backward: bool = False
     activation: str = "swiglu"   # gated activation (swiglu, swiglu_clamp, swiglu_oai, geglu, reglu)
     act_limit: float = 0.0       # clamp of swiglu_clamp / swiglu_oai
+    save_activations: bool = False   # training: the forward keeps G, U for the backward
 
     @property
     def A(self) -> int:
@@ -74,6 +75,9 @@ CONFIGS = {
     "decode": MoEConfig("decode", 32, 2048, 512, 256, 8, "bf16", "normal", 2),
     "large_mxfp8": MoEConfig("large_mxfp8", 8192, 4096, 1024, 512, 10, "mxfp8", "zipf", 3),
     "train": MoEConfig("train", 8192, 4096, 1024, 128, 8, "bf16", "normal", 4, backward=True),
+    # the same training step with the projections kept from the forward instead of recomputed
+    "train_saved": MoEConfig("train_saved", 8192, 4096, 1024, 128, 8, "bf16", "normal", 4, backward=True,
+                             save_activations=True),
     # Diagnostic: prefill shapes with a milder per-rank bias, every expert active.
     "prefill_rankzipf": MoEConfig("prefill_rankzipf", 4096, 2048, 512, 256, 8, "bf16", "rankzipf", 1),
     # Diagnostic: the larger expert shapes of the LightMoE compatibility table (hidden / intermediate,

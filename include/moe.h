@@ -12,6 +12,7 @@
  *   moe_expert_mlp  grouped GEMM gate/up + activation, grouped GEMM down
  *   moe_combine     weighted sum of each token's k expert rows
  *   moe_backward    dX, dW_gate, dW_up, dW_down, d(top-k weights)
+ *   moe_expert_mlp_save, moe_backward_saved  the training pair that keeps G, U
  *   moe_route_backward  d(router logits) from d(top-k weights)
  *   moe_grouped_gemm    standalone grouped GEMM over expert-major rows
  *
@@ -288,6 +289,44 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* X, const void*
                                 const void* Wu_t, const void* Wd_t, void* dX, void* dW_gate,
                                 void* dW_up, void* dW_down, float* d_topk_w, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/*
+ * Training forward that keeps its projections for the backward.  The pages'
+ * backward recomputes G and U (LigerCute "Backward pass": activation
+ * recomputation) to save memory; a GPU with 288 GB of HBM holds a step's fp32
+ * G and U (T*k*2I*4 bytes: 512 MiB for 8,192 tokens, top-8, I = 1024) at no
+ * cost worth the recompute GEMM, so this pair of calls trades that memory for
+ * the 4*T*k*H*I FLOP of the recompute.
+ * moe_expert_mlp_save: moe_expert_mlp (bf16 only, the row-grouped GEMMs for
+ * every T, no workspace) that also writes
+ *   GU_rows  [T*k, 2I] fp32 out: G = X[row_token[r]] W_gate[e] in columns [0, I)
+ *            and U = X[row_token[r]] W_up[e] in columns [I, 2I) of every routed
+ *            row r, the fp32 accumulations from which h is formed (MOE_ACT_RELU2:
+ *            U only; columns [0, I) are not written)
+ * Other arguments, results and errors as moe_expert_mlp (bf16, Sg = Su = Sd = NULL);
+ * MXFP8 problems give MOE_ERR_UNSUPPORTED_SHAPE.
+ */
+MOE_API moe_status moe_expert_mlp_save(const moe_problem* p, const void* X, const int32_t* row_token,
+                                       const int32_t* expert_offsets, const void* Wg_t,
+                                       const void* Wu_t, const void* Wd_t, void* H_rows,
+                                       void* O_rows, float* GU_rows, void* stream);
+
+/*
+ * moe_backward with G and U read from GU_rows (as moe_expert_mlp_save wrote it
+ * for the same problem, dispatch and weights) instead of recomputed.  The
+ * results are those of moe_backward: dX and the weight gradients from the same
+ * operands, d_topk_w[s] = <h, P> summed per row in a fixed order of its own.
+ *   GU_rows  [T*k, 2I] fp32 in
+ * Other arguments, workspace (moe_workspace_size(MOE_CALL_BACKWARD)) and errors
+ * as moe_backward.
+ */
+MOE_API moe_status moe_backward_saved(const moe_problem* p, const void* X, const void* dY,
+                                      const float* topk_w, const int32_t* row_token,
+                                      const int32_t* row_slot, const int32_t* slot_row,
+                                      const int32_t* expert_offsets, const void* Wg_t,
+                                      const void* Wu_t, const void* Wd_t, const float* GU_rows,
+                                      void* dX, void* dW_gate, void* dW_up, void* dW_down,
+                                      float* d_topk_w, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Standalone grouped GEMM (LightMoE "Grouped GEMM": contiguous expert-major

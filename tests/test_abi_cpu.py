@@ -146,6 +146,23 @@ def test_calls_reject_bad_arguments_before_touching_the_device():
     assert lib.moe_route_backward(v, v, v, 4, 2048, 2, v, None) == 2
 
 
+def test_saved_pair_argument_checks():
+    """moe_expert_mlp_save / moe_backward_saved: bf16 only (MXFP8 gives 2) and the saved
+    projections are required (1), both reported before the device check."""
+    import ctypes
+    from grouped_gemm_router_amd import binding as B
+    lib = B.lib
+    v = ctypes.c_void_p(16)
+    pm = B.problem(64, 256, 128, 8, 2, "mxfp8")
+    assert lib.moe_expert_mlp_save(ctypes.byref(pm), *([v] * 9), None) == 2
+    assert lib.moe_backward_saved(ctypes.byref(pm), *([v] * 16), v, 1 << 30, None) == 2
+    p = B.problem(300, 256, 128, 8, 2)
+    assert lib.moe_expert_mlp_save(ctypes.byref(p), *([v] * 8), None, None) == 1
+    ptrs = [v] * 16
+    ptrs[10] = None                                 # GU_rows
+    assert lib.moe_backward_saved(ctypes.byref(p), *ptrs, v, 1 << 30, None) == 1
+
+
 def test_empty_batch_accepts_null_token_arrays():
     """T = 0 is a valid problem: token-sized pointers may be NULL.  Calls that compute nothing
     return MOE_OK without touching the device; the others get past the argument checks and

@@ -19,15 +19,16 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _setup(name, backward=False, T=None):
+def _setup(name, backward=False, T=None, saved=False):
     from grouped_gemm_router_amd.layer import MoELayer
     cfg = wl.config(name) if T is None else wl.config(name, T=T)
     logits, X = wl.make_logits(cfg), wl.make_x(cfg)
     idx, w = orc.route(logits, cfg.k)
     active = np.unique(idx)
-    _say(name, "active experts", len(active))
+    _say(name, "active experts", len(active), "saved activations" if saved else "")
     W = {n: device_weights(cfg, n, experts=active) for n in ("gate", "up", "down")}
-    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype).load_weights(W["gate"], W["up"], W["down"])
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, save_activations=saved).load_weights(
+        W["gate"], W["up"], W["down"])
     layer.forward(torch.from_numpy(logits).cuda(), to_dev(X), backward_plan=backward)
     torch.cuda.synchronize()
     return cfg, layer, logits, X, idx, w
@@ -83,8 +84,12 @@ def test_forward_full_size_sampled(name, T):
         check_close(Og[sel], O, f"{name} O[rows of expert {e}]", ambiguity=amb)
 
 
-def test_backward_full_size_sampled():
-    cfg, layer, logits, X, idx, w = _setup("train", backward=True)
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_backward_full_size_sampled(saved):
+    """The training workload's backward on the recompute path (moe_backward) and on the saved
+    projections (moe_expert_mlp_save + moe_backward_saved, whose saved G and U rows of the sampled
+    tokens are checked too)."""
+    cfg, layer, logits, X, idx, w = _setup("train", backward=True, saved=saved)
     dY = wl.make_dy(cfg)
     dX, dWg, dWu, dWd, dtw = layer.backward(to_dev(X), to_dev(dY))
     torch.cuda.synchronize()
@@ -92,6 +97,19 @@ def test_backward_full_size_sampled():
     fn = lambda n: host_weight_fn(cfg, n)
     rng = np.random.default_rng(7)
     tokens = np.sort(rng.choice(cfg.T, 24, replace=False))
+    if saved:
+        pl = layer.plan(cfg.T, True)
+        slot_row = pl["slot_row"].cpu().numpy()
+        GU = pl["GU"]
+        Xv = orc.bf16_decode(X)
+        for t in tokens[:6]:
+            for j in range(cfg.k):
+                r, e = int(slot_row[t * cfg.k + j]), int(idx[t, j])
+                G, U, _, _ = orc.expert_forward_rows(Xv[t:t + 1], orc.bf16_decode(fn("gate")(e)),
+                                                     orc.bf16_decode(fn("up")(e)), orc.bf16_decode(fn("down")(e)))
+                gu = GU[r].cpu().numpy().astype(np.float64)
+                check_close(gu[:cfg.I], G[0], f"saved G (token {t}, slot {j})")
+                check_close(gu[cfg.I:], U[0], f"saved U (token {t}, slot {j})")
     rdX, rdwt = orc.backward_tokens(X, dY, idx, w, fn("gate"), fn("up"), fn("down"), tokens)
     check_close(to_f64(dX[torch.from_numpy(tokens).cuda()]), rdX, "dX[sampled tokens]")
     check_close(dtw.cpu().numpy()[tokens], rdwt, "d_topk_w[sampled tokens]")
