@@ -2,8 +2,9 @@
 replayed several times, with eager work on other inputs through the same plan
 buffers between the replays, gives the eager result bit for bit every time, and
 that result matches the oracle (routing bit for bit, outputs and gradients within
-the layer tolerance).  No call of the library allocates or clears memory with a
-memset, so the whole step can be captured."""
+the layer tolerance), on the recompute and the saved-projection training paths.
+No call of the library allocates or clears memory with a memset, so the whole
+step can be captured."""
 import dataclasses
 
 import numpy as np
@@ -23,6 +24,11 @@ CASES = [
     wl.config("tiny", name="graph_decode", T=24, H=256, I=128, E=64, k=4, seed=42),
     wl.config("tiny", name="graph_mx", T=96, H=256, I=128, E=6, k=2, dtype="mxfp8", seed=43),
     wl.config("tiny", name="graph_relu2", T=300, H=320, I=192, E=5, k=3, seed=44, backward=True, activation="relu2"),
+    # the training pair that keeps G and U (moe_expert_mlp_save + moe_backward_saved)
+    wl.config("tiny", name="graph_saved", T=300, H=320, I=192, E=5, k=3, seed=45, backward=True,
+              save_activations=True),
+    wl.config("tiny", name="graph_saved_relu2", T=300, H=320, I=192, E=5, k=3, seed=46, backward=True,
+              activation="relu2", save_activations=True),
 ]
 
 
@@ -35,8 +41,8 @@ def test_graph_replays_match_eager(cfg):
     from grouped_gemm_router_amd.layer import MoELayer
     _say("graph", cfg)
     W = {n: device_weights(cfg, n) for n in cfg.mats}
-    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation).load_weights(
-        W.get("gate"), W["up"], W["down"])
+    layer = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.dtype, activation=cfg.activation,
+                     save_activations=cfg.save_activations).load_weights(W.get("gate"), W["up"], W["down"])
     logits = torch.from_numpy(wl.make_logits(cfg)).cuda()
     X = to_dev(wl.make_x(cfg))
     dY = to_dev(wl.make_dy(cfg)) if cfg.backward else None
