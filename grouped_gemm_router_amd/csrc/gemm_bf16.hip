@@ -180,11 +180,14 @@ struct FwdGateUpOps : RowOpsBase<C, RSrcX, RSrcGateUpW<C>, PART> {
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, 2 * p.I, p.H, pre, red);
   }
+  // the h stores are counted; the saved-activation forward's G, U stores are not
+  static constexpr int OUT_STORES = stage_store_count<C, C::FN * 16>();
+  __device__ static bool stores_counted(const GemmArgs& p) { return p.GU == nullptr; }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t* wlds) {
     // fragment fn holds intermediate columns (wn * FN + fn) * 16 + [0, 16): items 4q + j (q = 0, 1)
     // are gate and 4q + 8 + j the up values of column 8q + 4 * (lane / 32) + j
-    stage_store_bf16<C, C::FN * 16, 2>(
+    stage_store_bf16<C, C::FN * 16, 2, false, true>(
         wlds, p.Hrows, p.I, t.m0 + wm * C::WTM, t.m_end, t.nt * (C::BN / 2) + wn * C::FN * 16, p.I, lane,
         [&](int fm, int fn, int q, int j) {
           return gated_act(acc[fm][fn][4 * q + j], acc[fm][fn][4 * q + 8 + j], act_code(ACTK, p.act), p.act_limit);
@@ -218,26 +221,31 @@ struct FwdUpOps : RowOpsBase<C, RSrcX, RSrcUpW, PART> {
 };
 
 // fp32 rows straight from the accumulators: each lane writes its 16-byte item
-// groups (32 contiguous bytes per row from the two lane halves).
+// groups (32 contiguous bytes per row from the two lane halves).  Every wave issues exactly
+// FM * FN * 4 buffer stores (rows at or past the segment's end and columns at or past ncols
+// dropped by the resource's range), the count the deep-B schedule waits on.
 template <class C>
 __device__ __forceinline__ void store_rows_f32(float* base, int ld, int ncols, const Tile& t,
                                                f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
+  const int row0 = t.m0 + wm * C::WTM;                   // the wave's first row
+  const int valid = min(max(t.m_end - row0, 0), C::WTM);
+  const __amdgpu_buffer_rsrc_t rs = out_rsrc(base + (size_t)row0 * ld, (uint32_t)valid * (uint32_t)ld * 4u);
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
-    const int r = t.m0 + Frag<C>::row(wm, fm, lane);
-    if (r >= t.m_end) continue;
-    float* out = base + (size_t)r * ld;
+    const uint32_t rrel = (uint32_t)(fm * 32 + (lane & 31));
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = t.n0 + Frag<C>::col(wn, fn, q, lane);
-        if (n >= ncols) continue;
-        *reinterpret_cast<float4*>(out + n) =
-            make_float4(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]);
+        const uint32_t off = n < ncols ? (rrel * (uint32_t)ld + (uint32_t)n) * 4u : BUF_DROP;
+        buf_store16(rs, off, __float_as_uint(acc[fm][fn][4 * q]), __float_as_uint(acc[fm][fn][4 * q + 1]),
+                    __float_as_uint(acc[fm][fn][4 * q + 2]), __float_as_uint(acc[fm][fn][4 * q + 3]));
       }
   }
 }
+template <class C>
+constexpr int store_rows_f32_count() { return C::FM * C::FN * 4; }
 
 // O = bf16(h Wd)
 template <class C, int PART = ROWS_ALL>
@@ -246,9 +254,11 @@ struct FwdDownOps : RowOpsBase<C, RSrcH, RSrcDownW, PART> {
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, p.I, pre, red);
   }
+  static constexpr int OUT_STORES = stage_store_count<C, C::WTN>();
+  __device__ static bool stores_counted(const GemmArgs&) { return true; }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t* wlds) {
-    stage_store_bf16<C, C::WTN, 4>(
+    stage_store_bf16<C, C::WTN, 4, false, true>(
         wlds, p.Orows, p.H, t.m0 + wm * C::WTM, t.m_end, t.n0 + wn * C::WTN, p.H, lane,
         [&](int fm, int fn, int q, int j) { return acc[fm][fn][4 * q + j]; },
         [](int fn, int q) { return fn * 32 + q * 8; });
@@ -263,6 +273,8 @@ struct BwdPOps : RowOpsBase<C, RSrcDY, KSrcDownWt, PART> {
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.I, p.H, pre, red);
   }
+  static constexpr int OUT_STORES = store_rows_f32_count<C>();
+  __device__ static bool stores_counted(const GemmArgs&) { return true; }
   __device__ static void epilogue(const GemmArgs& p, const Tile& t, f32x16 (&acc)[C::FM][C::FN],
                                   int wm, int wn, int lane, uint8_t*) {
     store_rows_f32<C>(p.P, p.I, p.I, t, acc, wm, wn, lane);
@@ -536,6 +548,8 @@ struct BwdDXUpOps : RowOpsBase<C, RSrcDU2, KSrcUpWt2, PART> {
 template <class C, int PART = ROWS_ALL>
 struct BwdDXOps : RowOpsBase<C, RSrcDGU, KSrcGateUpWt, PART> {
   static constexpr bool B_KMAJOR = true;
+  static constexpr int OUT_STORES = store_rows_f32_count<C>();
+  __device__ static bool stores_counted(const GemmArgs&) { return true; }
   __device__ static void init_sched(typename RowOpsBase<C, RSrcDGU, KSrcGateUpWt, PART>::Sched& s,
                                     const GemmArgs& p, int* pre, int* red) {
     s.init(p.offsets, p.E, p.H, 2 * p.I, pre, red);

@@ -326,6 +326,14 @@ struct EarlyNext : std::true_type {};
 template <class T>
 struct EarlyNext<T, std::void_t<decltype(T::EARLY_NEXT)>> : std::bool_constant<T::EARLY_NEXT> {};
 
+// Output stores per wave and tile that Ops' epilogue issues whatever the tile's rows
+// (Ops::OUT_STORES, -1 when absent: not counted), and whether it did so for these arguments
+// (Ops::stores_counted(p)).
+template <class T, class = void>
+struct OutStores : std::integral_constant<int, -1> {};
+template <class T>
+struct OutStores<T, std::void_t<decltype(T::OUT_STORES)>> : std::integral_constant<int, T::OUT_STORES> {};
+
 // Every tile of Ops' schedule, with the stages at smem (C::NST * C::STAGE uint4) and the
 // schedule's scratch at sched_lds.  `carry` is XcdWalk's deal position, updated for a
 // schedule that follows on the same grid.
@@ -509,16 +517,22 @@ __device__ __forceinline__ void rows_gemm_body(const P& p) {
 // tile; A k-tile g in A stage g mod 2, B k-tile g in B stage g mod 3).  Step g waits for A and B
 // k-tile g, then issues A k-tile g + 1 and B k-tile g + 2 (the A loads first, so that waiting for
 // all but the last PB loads leaves only B k-tile g + 2 in flight); loads past the workgroup's last
-// tile fetch its last k-tile 0 again (in bounds, never read).  At a tile's end the epilogue waits
-// for the next step's k-tiles, stages its output in the A stage just read and lets its stores
-// drain under the next step, as in the two-stage schedule.  The schedule's prefix and the tile
-// lookups use the stage area before the first load (lane table).  A gathered row operand's loader
-// loads its token ids when it moves to the next tile (at a tile's last step); the compiler waits
-// for those loads with vmcnt(0), which also drains the k-tiles in flight, once per tile.
+// tile fetch its last k-tile 0 again (in bounds, never read).
+// At a tile's end (g = the next tile's first k-tile) the A stage and the B stage just read are
+// free: A k-tile g + 1 is issued at once into the A one, the epilogue waits for A and B k-tile g,
+// stages its output in the B one and issues its stores, and the next tile's first step issues
+// only B k-tile g + 2 (into the staging area, after a barrier).  With an epilogue whose stores
+// are counted (OutStores), the second step waits for A and B k-tile g + 1 but lets the SO stores
+// issued after them stay in flight, so they drain under two k steps; otherwise it waits for
+// them.  The schedule's prefix and the tile lookups use the stage area before the first load
+// (lane table).  A gathered row operand's loader loads its token ids when it moves to the next
+// tile; the compiler waits for those loads with vmcnt(0), which also drains the k-tiles in
+// flight, once per tile.
 template <class C, class Ops, class P>
 __device__ __forceinline__ void rows_gemm_tiles_db(const P& p, uint4* smem, int& carry) {
   static_assert(C::NST == 2 && C::BM == C::BN && EarlyNext<Ops>::value, "two stages, square tiles");
-  static_assert(C::EPI * C::NW <= C::A_SLOTS * 16, "epilogue staging inside one A stage");
+  static_assert(C::EPI * C::NW <= C::B_SLOTS * 16, "epilogue staging inside one B stage");
+  constexpr int SO = OutStores<Ops>::value;               // counted output stores per wave (-1: none)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   constexpr bool BKM = BKMajor<Ops>::value;
@@ -575,7 +589,8 @@ __device__ __forceinline__ void rows_gemm_tiles_db(const P& p, uint4* smem, int&
   bl.issue(p, tb, kb * C::BK, Bs + C::B_SLOTS);
   next_b();
   int g = 0;                                              // the k-tile the next step computes
-  bool prewaited = false;
+  bool after_epi = false;                                 // an epilogue ran before this tile
+  bool counted = false;                                   // ... and its SO stores are in flight
   for (int ti = 0; ti < ntile; ++ti) {
     const Tile cur = lt.get(sched, ti);
     f32x16 acc[C::FM][C::FN];
@@ -586,29 +601,51 @@ __device__ __forceinline__ void rows_gemm_tiles_db(const P& p, uint4* smem, int&
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
     for (int k = 0; k < nk; ++k, ++g) {
-      if (!prewaited) wait_vmcnt<PB>();
-      prewaited = false;
+      // (after an epilogue: step 0's k-tiles were waited for at the tile's end; step 1's were
+      // issued before the epilogue's stores)
+      if (!after_epi || k > 1) wait_vmcnt<PB>();
+      else if (k == 1) {
+        if constexpr (SO >= 0) {
+          if (counted) wait_vmcnt<PB + SO>();
+          else wait_vmcnt<PB>();
+        } else {
+          wait_vmcnt<PB>();
+        }
+      }
       __syncthreads();
       uint4* sta = As + ((g + 1) & 1) * C::A_SLOTS;
       uint4* stb = Bs + ((g + 2) % 3) * C::B_SLOTS;
       const int k0a = ka * C::BK, k0b = kb * C::BK;
-      auto issue = [&](int j) {
-        if (j < PA) al.issue_one(p, ta, k0a, sta, j);
-        else bl.issue_one(p, tb, k0b, stb, j - PA);
-      };
       const uint8_t* sa = reinterpret_cast<const uint8_t*>(As + (g & 1) * C::A_SLOTS);
       const uint8_t* sb = reinterpret_cast<const uint8_t*>(Bs + (g % 3) * C::B_SLOTS) - C::A_SLOTS * 16;
-      mma_ktile_rows<C, true, PERK, BKM>(sa, sb, fa, acc, issue);
-      next_a();
+      if (after_epi && k == 0) {
+        // A k-tile g + 1 is already in flight: B only
+        auto issue = [&](int j) { bl.issue_one(p, tb, k0b, stb, j); };
+        mma_ktile_rows<C, true, PB, BKM>(sa, sb, fa, acc, issue);
+      } else {
+        auto issue = [&](int j) {
+          if (j < PA) al.issue_one(p, ta, k0a, sta, j);
+          else bl.issue_one(p, tb, k0b, stb, j - PA);
+        };
+        mma_ktile_rows<C, true, PERK, BKM>(sa, sb, fa, acc, issue);
+        next_a();
+      }
       next_b();
     }
-    // every wave is past its reads of the A stage just read (the staging area) and its B stage
+    // every wave is past its reads of the A and B stages of the last step
     __syncthreads();
-    wait_vmcnt<PB>();                                     // the next step's A and B k-tiles
-    prewaited = true;
-    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(As + ((g - 1) & 1) * C::A_SLOTS) + wave * C::EPI;
+    // A k-tile g + 1 into the A stage just read, then wait for A and B k-tile g (B k-tile g + 1
+    // and A k-tile g + 1 stay in flight)
+    al.issue(p, ta, ka * C::BK, As + ((g + 1) & 1) * C::A_SLOTS);
+    next_a();
+    wait_vmcnt<PB + PA>();
+    after_epi = true;
+    if constexpr (SO >= 0) counted = Ops::stores_counted(p);
+    // the output stores follow those loads in issue order
+    asm volatile("" ::: "memory");
+    uint8_t* wave_lds = reinterpret_cast<uint8_t*>(Bs + ((g + 2) % 3) * C::B_SLOTS) + wave * C::EPI;
     Ops::epilogue(p, cur, acc, wm, wn, lane, wave_lds);
-    // the staging area receives the next step's A load
+    // the staging area receives the next step's B load
     __syncthreads();
   }
   wait_vmcnt<0>();                                        // no LDS write in flight when the pass ends
@@ -656,6 +693,25 @@ __device__ __forceinline__ void rows_gemm_split_body_db(const P& p) {
   rows_gemm_tiles<C1, Ops1, P, true>(p, smem, nullptr, carry);
 }
 
+// Output stores through a buffer resource (raw buffer: stride 0; the hardware drops a store
+// whose offset is at or past the resource's size).  Every wave issues every such store,
+// whether or not any of its lanes is in range, so the number of vector-memory operations an
+// epilogue leaves in flight is a compile-time constant, which the deep-B schedule counts in the
+// waits of the next tile's second k step.
+constexpr uint32_t BUF_DROP = 0x80000000u;              // an offset past every output resource
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void* base, uint32_t bytes) {
+  const uint8_t* b = uniform_ptr(reinterpret_cast<const uint8_t*>(base));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes < 0x7fffffffu ? bytes : 0x7fffffffu);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(b), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t x, uint32_t y,
+                                            uint32_t z, uint32_t w) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4nt{x, y, z, w}, r, off, 0, 0);
+}
+// Store instructions per wave of stage_store_bf16<C, CW, ...> with COUNTED.
+template <class C, int CW>
+constexpr int stage_store_count() { return C::FM * (32 * (CW * 2 / 16) / 64); }
+
 // Stages this wave's bf16 output, one 32-row fragment row-block at a time,
 // through its LDS scratch and writes whole row segments (16 bytes per lane,
 // CW * 2 contiguous bytes per row).  val(fm, fn, q, j) gives the value of
@@ -663,9 +719,13 @@ __device__ __forceinline__ void rows_gemm_split_body_db(const P& p) {
 // wave's CW-wide slab) of that item group for lane half 0 (lane half 1 adds 4).
 // NQ item groups per fragment are stored.  NT marks the global stores non-temporal (streamed
 // through L2 without displacing the operand tiles other workgroups are still reading).
-template <class C, int CW, int NQ, bool NT = false, class Val, class Col>
+// COUNTED issues exactly stage_store_count<C, CW>() buffer stores per wave (rows at or past
+// row_end and columns at or past ncols dropped by the resource's range); row0 and col0 are then
+// the wave's first row and column.
+template <class C, int CW, int NQ, bool NT = false, bool COUNTED = false, class Val, class Col>
 __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, int ld, int row0, int row_end,
                                                  int col0, int ncols, int lane_, Val val, Col col_of) {
+  static_assert(!(NT && COUNTED), "counted stores are plain");
   const int lane = opaque_lane(lane_);
   constexpr int CPRW = CW * 2 / 16;                      // 16-byte chunks per row
   // Rows padded by 16 bytes where the scratch allows it, else unpadded 128-byte
@@ -675,6 +735,11 @@ __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, i
   static_assert(32 * PITCH <= RowEpiLds<C>::BYTES, "staging area too small");
   static_assert(!SWZ || CPRW == 8, "swizzled staging needs 128-byte rows");
   auto pos = [](int r, int ch) { return SWZ ? (ch ^ ((r >> 1) & 7)) : ch; };
+  __amdgpu_buffer_rsrc_t rs;
+  if constexpr (COUNTED) {
+    const int valid = min(max(row_end - row0, 0), C::FM * 32);
+    rs = out_rsrc(out + (size_t)row0 * ld + col0, (uint32_t)valid * (uint32_t)ld * 2u);
+  }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int r = lane & 31;
@@ -696,7 +761,10 @@ __device__ __forceinline__ void stage_store_bf16(uint8_t* wlds, uint16_t* out, i
       const uint4 v = *reinterpret_cast<const uint4*>(wlds + rr * PITCH + pos(rr, ch) * 16);
       const int grow = row0 + fm * 32 + rr;
       const int gcol = col0 + ch * 8;
-      if (grow < row_end && gcol < ncols) {
+      if constexpr (COUNTED) {
+        const uint32_t off = gcol < ncols ? ((uint32_t)(fm * 32 + rr) * (uint32_t)ld + ch * 8) * 2u : BUF_DROP;
+        buf_store16(rs, off, v.x, v.y, v.z, v.w);
+      } else if (grow < row_end && gcol < ncols) {
         uint16_t* dst = out + (size_t)grow * ld + gcol;
         if constexpr (NT)
           __builtin_nontemporal_store(u32x4nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4nt*>(dst));
