@@ -66,6 +66,40 @@ def check_close(gpu, ref, what: str, atol=ATOL, rtol=RTOL, ambiguity=None, max_r
     return msg
 
 
+def mx_block_sum_ambiguity(x_rows, wg, wu, wd, act="swiglu", limit=None):
+    """Ambiguity of the O rows of x_rows on the MXFP8 path with the hardware's FP8 summation
+    taken into account (``orc.mx_block_dot_deviation``): G and U of the gate/up GEMM may lie that
+    far from the exact ones, which widens the valid requantisations of h, and the down GEMM's own
+    sums move O by its deviation (float64 values in, per element of O out)."""
+    gated = orc.is_gated(act)
+    G, U, h, _ = orc.expert_forward_rows(x_rows, wg, wu, wd, mxfp8=True, act=act, limit=limit)
+    dG = orc.mx_block_dot_deviation(x_rows, wg) if gated else None
+    dU = orc.mx_block_dot_deviation(x_rows, wu)
+    amb = orc.mx_down_ambiguity(G, U, wd, act, limit, dG=dG, dU=dU)
+    return amb + np.abs(orc.mx_block_dot_deviation(h, wd))
+
+
+def check_close_mx(gpu, ref, what, ambiguity, refine_rows, max_rows=0.001):
+    """check_close with the MXFP8 requantisation ambiguity, where rows holding an element outside
+    it get the ambiguity ``refine_rows(rows)`` returns (``mx_block_sum_ambiguity``: that of an
+    implementation on the hardware's FP8 block summation); at most a fraction ``max_rows`` of the
+    rows (and at least 2) may need it.  Returns the ambiguity used."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    amb = np.array(ambiguity, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    lim = ATOL + RTOL * np.abs(ref) + np.where(amb > 0, amb + (np.abs(ref) + amb) * 2.0 ** -7, 0.0)
+    rows = np.unique(np.nonzero(err > lim)[0])
+    note = ""
+    if rows.size:
+        assert rows.size <= max(2, int(max_rows * gpu.shape[0])), \
+            f"{what}: {rows.size} rows outside the requantisation ambiguity"
+        amb[rows] = np.maximum(amb[rows], refine_rows(rows))
+        note = f" ({rows.size} rows with the FP8 block-sum ambiguity)"
+    check_close(gpu, ref, what + note, ambiguity=amb)
+    return amb
+
+
 def device_weights(cfg, name, experts=None, fill=float("nan")):
     """[E, K, N] bf16 device tensor with the seeded weights of ``experts`` (all
     when None); the others hold ``fill`` (NaN: an unread expert stays unread)."""
