@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes on every element: h and O of every routed row
-(expert by expert) and Y of every token, against the oracle, for the four forward workloads
-(the prefill shapes with both routings, decode and large MXFP8), in the launch configuration
+(expert by expert) and Y of every token, against the oracle, for the five forward workloads
+(the prefill shapes with both routings, decode, large MXFP8 and the training forward, whose
+experts of 447-572 rows run every remainder-tile class), in the launch configuration
 the benchmark times.  For large MXFP8, rows with an element outside the requantisation
 ambiguity get the one of an implementation on the hardware's FP8 block summation
 (``check_close_mx``).  The training workload's backward is checked the same way, every
@@ -21,7 +22,7 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-@pytest.mark.parametrize("name", ["prefill", "prefill_rankzipf", "decode", "large_mxfp8"])
+@pytest.mark.parametrize("name", ["prefill", "prefill_rankzipf", "decode", "large_mxfp8", "train"])
 def test_forward_every_element(name):
     cfg, layer, logits, X, idx, w = _setup(name)
     pl = layer.plan(cfg.T)
