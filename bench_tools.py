@@ -64,7 +64,7 @@ MLP_KERNELS = {                         # kernels of one moe_expert_mlp call, pe
 _COMMON_SOURCES = ("api.cpp", "common.h", "kernels.h", "grouped_gemm.h")
 MLP_SOURCES = {
     "bf16": _COMMON_SOURCES + ("gemm_rows.h", "gemm_bf16.hip"),
-    "decode": _COMMON_SOURCES + ("decode.hip",),
+    "decode": _COMMON_SOURCES + ("gemm_rows.h", "decode.hip"),
     "mxfp8": _COMMON_SOURCES + ("gemm_rows.h", "mx_gemm.hip", "elementwise.hip"),
 }
 
