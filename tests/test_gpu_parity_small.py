@@ -204,6 +204,11 @@ SMALL = [
     wl.config("tiny", name="I64", T=600, H=128, I=64, E=4, k=2, seed=15),
     wl.config("tiny", name="mx_small", T=96, H=256, I=128, E=6, k=2, dtype="mxfp8", seed=16),
     wl.config("tiny", name="mx_ragged", T=333, H=384, I=256, E=5, k=3, dtype="mxfp8", seed=17),
+    # small-token streams: 5 k steps of gate/up split 1, 1, 1, 2 over the waves, 3 down steps (an
+    # odd count for the two-stage ring), experts of more than 16 rows (several row groups)
+    wl.config("tiny", name="decode_ragged", T=64, H=320, I=192, E=16, k=8, seed=18),
+    # one gate/up k step: three waves of every workgroup stream nothing
+    wl.config("tiny", name="decode_h64", T=33, H=64, I=64, E=8, k=2, seed=19),
 ]
 
 
