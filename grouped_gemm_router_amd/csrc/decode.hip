@@ -4,9 +4,11 @@
 // wave into v_mfma_f32_16x16x32_bf16 ("swap-AB": 16 weight rows are the A operand,
 // up to 16 token rows the B operand), with no barrier inside the stream.
 //
-// Work units are (used expert, slab of output features); a persistent grid
-// walks them after building the list of experts that have rows, so experts
-// without rows cost nothing.
+// Work units are (used expert, group of up to 16 rows, slab of output features),
+// one workgroup each.  A one-workgroup kernel first lists the (expert, row group)
+// entries of the experts that have rows, so experts without rows cost nothing;
+// the launch covers the most units a call can have, and the workgroups past the
+// real count exit at once.
 //
 // A k step is 64 contraction elements: 128 bytes, one cache line, of each of 16
 // rows.  Its rows reach LDS through direct global->LDS loads of whole lines (8

@@ -209,6 +209,8 @@ SMALL = [
     wl.config("tiny", name="decode_ragged", T=64, H=320, I=192, E=16, k=8, seed=18),
     # one gate/up k step: three waves of every workgroup stream nothing
     wl.config("tiny", name="decode_h64", T=33, H=64, I=64, E=8, k=2, seed=19),
+    # the most experts the small-token work list holds
+    wl.config("tiny", name="decode_e1024", T=16, H=128, I=64, E=1024, k=8, seed=20),
 ]
 
 
