@@ -109,8 +109,11 @@ def test_route_ties_and_signed_zeros():
     assert np.all(w.cpu().numpy()[0] == np.float32(1.0 / k))
 
 
+# (the one-workgroup dispatch holds 1, 2 or 4 groups of 64 slots per wave: T k = 1024 | 1032 and
+# 2048 | 2056 sit on both sides of its two boundaries)
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (1, 8, 8), (5, 3, 3), (3000, 7, 2), (9000, 1024, 32),
-                                   (4097, 64, 1), (0, 16, 4)])
+                                   (4097, 64, 1), (0, 16, 4), (128, 64, 8), (129, 64, 8), (256, 32, 8),
+                                   (257, 32, 8)])
 def test_dispatch_edge_cases(T, E, k):
     B = _B()
     _say("dispatch", T, E, k)
